@@ -1,0 +1,287 @@
+"""Pins for the CPU oracle: it is checked against facts that do not come from it.
+
+* the sliding-window worked example printed on the ultralytics glossary page
+  (58 vs 136 scored pairs, last-token reach 4 -> 7 -> 10 -> 13);
+* closed-form pair counts (sums of min() terms worked out by hand);
+* brute-force membership from index offsets (oracle/dense.py);
+* library routines: torch scaled_dot_product_attention (fp64, CPU) for the
+  dense-causal, dense-bidirectional, alpha -> 1 and alpha -> 0 special cases,
+  and torch.logsumexp for the two-set mixture identity that the pages'
+  "local sweep / periodic gather / fusion" decomposition implies;
+* invariants (row 0, constant values, convex hull, varlen = separate runs,
+  decode = last prefill row).
+
+None of these needs a GPU.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+from oracle import dense
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed, std=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * std
+
+
+def _single(q, k, v, g, kw, pi, M, bidir, scale, want_lse=False):
+    """Run the C oracle on one (sequence, head) given [n, d] arrays."""
+    n, d = q.shape
+    res = oracle.fwd(q[:, None, :], k[:, None, :], v[:, None, :], g[:, None],
+                     np.array([0, n]), kw, pi, M, bidir, scale, want_lse=want_lse)
+    if want_lse:
+        return res[0], res[1]
+    return res
+
+
+def _sdpa(q, k, v, mask=None, causal=False, scale=None):
+    t = lambda x: torch.from_numpy(np.ascontiguousarray(x))[None, None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None]
+    o = F.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m, is_causal=causal,
+                                       scale=scale)
+    return o[0, 0].numpy()
+
+
+# ---------------------------------------------------------------- index sets
+
+def test_swa_worked_example_counts_and_reach(oracle_lib):
+    gold = json.load(open(os.path.join(GOLDEN, "swa_worked_example.json")))
+    n, w = gold["seq_len"], gold["window"]
+    idx, kind, cnt = oracle.neighbor_table(n, w - 1, 1, 0, False)
+    assert int(cnt.sum()) == gold["scores_with_window"]
+    _, _, cnt_full = oracle.neighbor_table(n, n - 1, 1, 0, False)
+    assert int(cnt_full.sum()) == gold["scores_full_causal"]
+    # neighbour matrix and its repeated boolean products
+    mask = np.zeros((n, n), bool)
+    for i in range(n):
+        mask[i, idx[i, :cnt[i]]] = True
+    reach = mask.copy()
+    got = []
+    for _layer in range(len(gold["last_token_reach_by_layer"])):
+        got.append(int(reach[-1].sum()))
+        reach = (mask.astype(np.int64) @ reach.astype(np.int64)) > 0
+    assert got == gold["last_token_reach_by_layer"]
+
+
+@pytest.mark.parametrize("bidir", [False, True])
+def test_membership_matches_offset_masks(oracle_lib, bidir):
+    """Exhaustive tiny sweep: oracle neighbour lists == offset-mask formulation."""
+    for n in (1, 2, 5, 13, 24):
+        for kw in range(0, n + 1):
+            for pi in range(1, n + 2):
+                for M in range(0, n // pi + 2):
+                    local, skip = dense.masks(n, kw, pi, M, bidir)
+                    idx, kind, cnt = oracle.neighbor_table(n, kw, pi, M, bidir)
+                    for i in range(n):
+                        ii = idx[i, :cnt[i]]
+                        kk = kind[i, :cnt[i]]
+                        assert np.all(np.diff(ii) > 0)
+                        assert set(ii[kk == 1]) == set(np.nonzero(local[i])[0])
+                        assert set(ii[kk == 2]) == set(np.nonzero(skip[i])[0])
+
+
+def _counts(n, kw, pi, M, bidir):
+    tot_l = tot_s = 0
+    for i in range(n):
+        _, kind = oracle.neighbors(n, kw, pi, M, bidir, i)
+        tot_l += int((kind == 1).sum())
+        tot_s += int((kind == 2).sum())
+    return tot_l, tot_s
+
+
+@pytest.mark.parametrize("n,kw,pi,M", [
+    (256, 8, 16, 4),          # tiny fp32 workload
+    (8192, 64, 128, 16),      # 8K prefill workload
+    (1000, 3, 7, 9),
+    (4096, 100, 101, 40),
+])
+def test_closed_form_causal_counts(oracle_lib, n, kw, pi, M):
+    assert pi > kw and n >= M * pi and n > kw
+    loc, sk = _counts(n, kw, pi, M, False)
+    assert loc == n * (kw + 1) - kw * (kw + 1) // 2
+    assert sk == pi * M * (M - 1) // 2 + M * (n - M * pi)
+
+
+@pytest.mark.parametrize("n,kw,pi,M", [
+    (4096, 32, 64, 32),       # shortest bidirectional varlen sequence
+    (5000, 32, 64, 32),
+    (777, 5, 9, 20),
+])
+def test_closed_form_bidir_counts(oracle_lib, n, kw, pi, M):
+    assert pi > kw and n >= M * pi and n > 2 * kw
+    loc, sk = _counts(n, kw, pi, M, True)
+    assert loc == n * (2 * kw + 1) - kw * (kw + 1)
+    assert sk == 2 * M * n - pi * M * (M + 1)
+
+
+def test_long_prefill_counts_sampled(oracle_lib):
+    """128K prefill: per-row counts equal min() closed forms on sampled rows."""
+    n, kw, pi, M = 131072, 128, 256, 64
+    rng = np.random.default_rng(5)
+    rows = np.concatenate([np.arange(0, 600), rng.integers(0, n, 2000), np.arange(n - 50, n)])
+    for i in rows:
+        _, kind = oracle.neighbors(n, kw, pi, M, False, int(i))
+        assert (kind == 1).sum() == min(i, kw) + 1
+        assert (kind == 2).sum() == min(M, i // pi)
+
+
+def test_decode_row_counts(oracle_lib):
+    # decode workload: query at position 32767 of a 32768-token cache
+    idx, kind = oracle.neighbors(32768, 256, 512, 63, False, 32767)
+    assert (kind == 1).sum() == 257 and (kind == 2).sum() == 63
+    assert idx[0] == 32767 - 63 * 512 and idx[-1] == 32767
+
+
+# ------------------------------------------------------------------- values
+
+@pytest.mark.parametrize("bidir", [False, True])
+def test_dense_special_case_is_sdpa(oracle_lib, bidir):
+    """k >= n-1 and M = 0: plain softmax attention (the gate is a constant shift)."""
+    n, d = 37, 16
+    q, k, v = (_rand((n, d), s) for s in (1, 2, 3))
+    g = _rand(n, 4) * 3
+    got = _single(q, k, v, g, n - 1, 5, 0, bidir, 1 / math.sqrt(d))
+    ref = _sdpa(q, k, v, causal=not bidir)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_alpha_one_is_ring_local(oracle_lib):
+    """g = +inf: skip weights vanish; result = SDPA with the causal window mask."""
+    n, d, kw, pi, M = 64, 8, 3, 8, 5
+    q, k, v = (_rand((n, d), s) for s in (11, 12, 13))
+    pos = np.arange(n)
+    off = pos[:, None] - pos[None, :]
+    mask = (off >= 0) & (off < kw + 1)
+    ref = _sdpa(q, k, v, mask=mask)
+    got = _single(q, k, v, np.full(n, np.inf), kw, pi, M, False, 1 / math.sqrt(d))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+    near = _single(q, k, v, np.full(n, 40.0), kw, pi, M, False, 1 / math.sqrt(d))
+    np.testing.assert_allclose(near, ref, rtol=0, atol=1e-12)
+
+
+def test_alpha_zero_is_skip_only(oracle_lib):
+    """g = -inf: rows with skips attend over the skip set alone."""
+    n, d, kw, pi, M = 64, 8, 3, 8, 5
+    q, k, v = (_rand((n, d), s) for s in (21, 22, 23))
+    local, skip = dense.masks(n, kw, pi, M, False)
+    has = skip.any(1)
+    mask = np.where(has[:, None], skip, local)
+    ref = _sdpa(q, k, v, mask=mask)
+    got = _single(q, k, v, np.full(n, -np.inf), kw, pi, M, False, 1 / math.sqrt(d))
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("bidir", [False, True])
+def test_mixture_identity(oracle_lib, bidir):
+    """One softmax with a log-prior equals the alpha-weighted mix of the two
+    per-set softmaxes, weighted by their normalisers:
+        o = (a Z_L O_L + (1-a) Z_S O_S) / (a Z_L + (1-a) Z_S).
+    O_L, O_S from torch SDPA; Z_L, Z_S from torch.logsumexp."""
+    n, d, kw, pi, M = 70, 12, 4, 9, 6
+    scale = 0.3
+    q, k, v = (_rand((n, d), s) for s in (31, 32, 33))
+    g = _rand(n, 34) * 2
+    local, skip = dense.masks(n, kw, pi, M, bidir)
+    has = skip.any(1)
+    got, lse = _single(q, k, v, g, kw, pi, M, bidir, scale, want_lse=True)
+    o_l = _sdpa(q, k, v, mask=local, scale=scale)
+    skip_safe = np.where(has[:, None], skip, local)
+    o_s = _sdpa(q, k, v, mask=skip_safe, scale=scale)
+    s = torch.from_numpy(scale * (q @ k.T))
+    lz_l = torch.logsumexp(s.masked_fill(~torch.from_numpy(local), -math.inf), 1).numpy()
+    lz_s = torch.logsumexp(s.masked_fill(~torch.from_numpy(skip_safe), -math.inf), 1).numpy()
+    a = 1 / (1 + np.exp(-g))
+    wl = a * np.exp(lz_l)
+    ws = (1 - a) * np.exp(lz_s)
+    ref = np.where(has[:, None], (wl[:, None] * o_l + ws[:, None] * o_s) / (wl + ws)[:, None], o_l)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-11)
+    ref_lse = np.where(has, np.log(wl + ws), lz_l)
+    np.testing.assert_allclose(lse, ref_lse, rtol=0, atol=1e-11)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_c_oracle_matches_dense(oracle_lib, seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 60))
+    d = int(rng.choice([4, 8, 16]))
+    kw = int(rng.integers(0, 12))
+    pi = int(rng.integers(1, 20))
+    M = int(rng.integers(0, 8))
+    bidir = bool(seed % 2)
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    g = rng.standard_normal(n) * 3
+    got, lse = _single(q, k, v, g, kw, pi, M, bidir, 0.25, want_lse=True)
+    ref, rlse = dense.attention(q, k, v, g, kw, pi, M, bidir, 0.25, want_lse=True)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-12)
+
+
+def test_invariants(oracle_lib):
+    n, d, kw, pi, M = 50, 8, 2, 7, 4
+    q, k, v = (_rand((n, d), s) for s in (41, 42, 43))
+    g = _rand(n, 44)
+    got = _single(q, k, v, g, kw, pi, M, False, 0.5)
+    np.testing.assert_array_equal(got[0], v[0])           # row 0 sees only itself
+    const = np.tile(_rand(d, 45), (n, 1))
+    np.testing.assert_allclose(_single(q, k, const, g, kw, pi, M, False, 0.5), const,
+                               rtol=0, atol=1e-13)
+    for i in range(n):                                      # convex hull of its keys
+        ii, _ = oracle.neighbors(n, kw, pi, M, False, i)
+        assert np.all(got[i] <= v[ii].max(0) + 1e-12)
+        assert np.all(got[i] >= v[ii].min(0) - 1e-12)
+
+
+def test_varlen_equals_separate(oracle_lib):
+    lens = [5, 17, 1, 30]
+    H, d, kw, pi, M = 3, 8, 3, 4, 3
+    T = sum(lens)
+    rng = np.random.default_rng(7)
+    q, k, v = (rng.standard_normal((T, H, d)) for _ in range(3))
+    g = rng.standard_normal((T, H))
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    for bidir in (False, True):
+        packed = oracle.fwd(q, k, v, g, cu, kw, pi, M, bidir, 0.4).reshape(T, H, d)
+        for s in range(len(lens)):
+            a, b = cu[s], cu[s + 1]
+            alone = oracle.fwd(q[a:b], k[a:b], v[a:b], g[a:b], [0, b - a], kw, pi, M, bidir,
+                               0.4).reshape(b - a, H, d)
+            np.testing.assert_array_equal(packed[a:b], alone)
+
+
+def test_decode_equals_last_prefill_row(oracle_lib):
+    S, H, L, d, kw, pi, M = 3, 2, 90, 16, 6, 10, 7
+    rng = np.random.default_rng(8)
+    kc, vc = rng.standard_normal((S, H, L, d)), rng.standard_normal((S, H, L, d))
+    lens = np.array([90, 41, 1], np.int32)
+    g = rng.standard_normal((S, H))
+    q = rng.standard_normal((S, H, d))
+    out = oracle.decode(q, kc, vc, lens, g, kw, pi, M, 0.25)
+    for s in range(S):
+        n = int(lens[s])
+        for h in range(H):
+            qq = kc[s, h, :n].copy()
+            qq[n - 1] = q[s, h]
+            gg = np.zeros(n)
+            gg[n - 1] = g[s, h]
+            ref = _single(qq, kc[s, h, :n], vc[s, h, :n], gg, kw, pi, M, False, 0.25)
+            np.testing.assert_array_equal(out[s, h], ref[n - 1])
+
+
+def test_bf16_inputs_read_exactly(oracle_lib):
+    n, H, d = 20, 2, 8
+    t = torch.randn(n, H, d, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    bits = t.view(torch.int16).numpy().view(np.uint16)
+    as64 = t.double().numpy()
+    g = np.zeros((n, H))
+    a = oracle.fwd(bits, bits, bits, g, [0, n], 2, 3, 2, False, 0.3)
+    b = oracle.fwd(as64, as64, as64, g, [0, n], 2, 3, 2, False, 0.3)
+    np.testing.assert_array_equal(a, b)
