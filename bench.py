@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Benchmark of the pi-Attention forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload prefill_8k]
+
+A step is one piattn_fwd call over the whole workload (every query row of
+every (sequence, head)): window and skip enumeration, QK^T, gate prior,
+single online softmax, PV and the bf16 store all run inside it.  Inputs are
+seeded synthetic tensors already resident in HBM; several input sets are
+rotated so that successive steps do not hit the 256 MB Infinity Cache.
+
+Prints ONE JSON line on stdout.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "π-attn fwd queries/s + achieved HBM GB/s & MFMA %, n=8192 d=64 bf16, 1 GPU"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16
+MALL_BYTES = 256 << 20
+KERNEL_SOURCES = ["pattern.hpp", "common.hpp", "gather.hpp", "fwd_gather.hip", "fwd_tiled.hip",
+                  "decode.hip", "api.cpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_digest() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_long_context_piattn_amd", "csrc")
+    for name in KERNEL_SOURCES:
+        p = os.path.join(csrc, name)
+        if os.path.exists(p):
+            h.update(name.encode())
+            h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def pair_counts(w, lengths=None):
+    """(local, skip) scored pairs of the workload from the pattern's closed
+    range arithmetic (vectorised over rows)."""
+    import numpy as np
+
+    def one(n):
+        i = np.arange(n, dtype=np.int64)
+        lo = np.maximum(0, i - w.k)
+        hi = np.minimum(n - 1, i + w.k) if w.bidir else i
+        mlo = w.k // w.pi + 1
+        mb = np.minimum(w.M, i // w.pi)
+        nb = np.maximum(0, mb - mlo + 1)
+        nf = 0
+        if w.bidir:
+            mf = np.minimum(w.M, (n - 1 - i) // w.pi)
+            nf = np.maximum(0, mf - mlo + 1)
+        return int((hi - lo + 1).sum()), int((nb + nf).sum())
+
+    if w.nseq:
+        tot = [one(n) for n in lengths]
+        loc, sk = sum(t[0] for t in tot), sum(t[1] for t in tot)
+    else:
+        loc, sk = one(w.n)
+        loc, sk = loc * w.B, sk * w.B
+    return loc * w.H, sk * w.H
+
+
+def algorithmic(w, lengths=None):
+    """Per-launch algorithmic bytes (q, k, v, out once each plus the fp32
+    gate) and flops (4*d per scored pair), and the number of query rows."""
+    esz = 4 if w.dtype == "f32" else 2
+    T = sum(lengths) if w.nseq else w.B * w.n
+    rows = T * w.H
+    loc, sk = pair_counts(w, lengths)
+    bytes_ = rows * (4 * w.d * esz + 4)
+    flops = 4 * w.d * (loc + sk)
+    return bytes_, flops, rows, loc, sk
+
+
+def traffic_record(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if
+    it was taken on the current kernel sources."""
+    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("kernel_digest") != kernel_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, budget_s: float):
+    """Time the fp64 CPU oracle on a bounded sample of the same workload."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    threads = oracle.max_threads()
+    B, H, n, d = x["q"].shape
+
+    def host(t):
+        t = t.detach().permute(0, 2, 1, 3).reshape(B * n, H, d).contiguous().cpu()
+        return t.view(torch.int16).numpy().view(np.uint16)
+
+    q, k, v = host(x["q"]), host(x["k"]), host(x["v"])
+    g = x["g"].detach().permute(0, 2, 1).reshape(B * n, H).double().cpu().numpy()
+    cu = np.arange(B + 1, dtype=np.int64) * n
+    rng = np.random.default_rng(0)
+    total_rows = B * n * H
+    count = 4096
+    elapsed = 0.0
+    while True:
+        rows = np.sort(rng.integers(0, total_rows, count))
+        t0 = time.perf_counter()
+        oracle.fwd(q, k, v, g, cu, w.k, w.pi, w.M, w.bidir, w.scale, rows=rows)
+        elapsed = time.perf_counter() - t0
+        if elapsed >= budget_s * 0.5 or count >= total_rows:
+            break
+        count = min(total_rows, int(count * max(2.0, budget_s / max(elapsed, 1e-3))))
+    return {"value": count / elapsed, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": "%d uniformly sampled query rows of the %s workload (of %d), fp64, "
+                      "OpenMP over rows, %.1f s" % (count, w.name, total_rows, elapsed)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        log("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+            "(a (sequence, head) shard per GPU would need no exchange; see the design notes).")
+        sys.exit(2)
+
+    import torch
+
+    import sparse_long_context_piattn_amd as pa
+    from sparse_long_context_piattn_amd import workloads as wl
+
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = wl.WORKLOADS[args.workload]
+    if w.kind != "fwd":
+        log("bench.py times prefill workloads; %s is %s" % (w.name, w.kind))
+        sys.exit(2)
+    lengths = wl.varlen_lengths(w) if w.nseq else None
+    alg_bytes, alg_flops, rows, loc, sk = algorithmic(w, lengths)
+    set_bytes = alg_bytes
+    nsets = args.sets or max(1, math.ceil(3 * MALL_BYTES / set_bytes))
+    nsets = min(nsets, 6)
+    log("workload %s: %d rows, %d local + %d skip pairs, %.1f MB/launch, %d input sets"
+        % (w.name, rows, loc, sk, alg_bytes / 1e6, nsets))
+    sets = [wl.make_fwd_inputs(w, device=dev, seed=w.seed + s, lengths=lengths)
+            for s in range(nsets)]
+    outs = [torch.empty_like(x["q"]) for x in sets]
+
+    def step(j):
+        x = sets[j % nsets]
+        pa.fwd(x["q"], x["k"], x["v"], x["g"], window_k=w.k, period_pi=w.pi, num_skips=w.M,
+               bidirectional=w.bidir, cu_seqlens=x.get("cu_seqlens"),
+               max_seqlen=max(lengths) if lengths else None, out=outs[j % nsets])
+
+    for j in range(args.warmup):
+        step(j)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for j in range(args.steps):
+        step(j)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1)
+    ms_per_step = ms / args.steps
+    sec = ms_per_step / 1e3
+    qps = rows / sec
+    achieved_gbps = alg_bytes / sec / 1e9
+    tflops = alg_flops / sec / 1e12
+    log("%.4f ms/step  %.3e queries/s  %.0f GB/s (%.1f%% of HBM peak)  %.2f TFLOP/s (%.2f%% MFMA)"
+        % (ms_per_step, qps, achieved_gbps, 100 * achieved_gbps / HBM_PEAK_GBPS, tflops,
+           100 * tflops / BF16_MFMA_PEAK_TFLOPS))
+
+    traffic = traffic_record(w.name)
+    roof = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s", "frac": round(achieved_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": traffic}
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracle on a sample ...")
+        cpu = cpu_baseline(w, sets[0], args.cpu_budget)
+        log("oracle: %.3e queries/s on %d threads" % (cpu["value"], cpu["cores"]))
+
+    cfg = {"workload": w.name, "B": w.B if not w.nseq else len(lengths), "H": w.H,
+           "n": w.n if not w.nseq else max(lengths), "d": w.d, "k": w.k, "pi": w.pi, "M": w.M,
+           "bidirectional": w.bidir, "global_batch": w.B, "seq_len": w.n,
+           "parallelism": "single GPU", "input_sets": nsets}
+    res = {"metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1,
+           "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16"
+           if w.dtype == "bf16" else "f32", "data": "synthetic (seeded N(0,1) q/k/v, N(0,1) "
+           "gate logits)", "config": cfg,
+           "hbm_gbps_algorithmic": round(achieved_gbps, 1),
+           "tflops_algorithmic": round(tflops, 3),
+           "mfma_pct_algorithmic": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 3),
+           "kernel_digest": kernel_digest(),
+           "roofline": roof, "cpu_baseline": cpu}
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

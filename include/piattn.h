@@ -1,0 +1,177 @@
+/*
+ * piattn.h -- C ABI of libpiattn, a pi-Attention forward library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * pi-Attention (Liu and Yu, arXiv 2511.10696; described on gist.science
+ * "pi-Attention: Periodic Sparse Transformers for Efficient Long-Context
+ * Modeling", section 2 "Methodology": "Ring-Local Attention", "pi-Skip
+ * Attention" and "Dynamic Adaptive Fusion") lets query i of a sequence of
+ * length n attend to the union of
+ *
+ *   a ring-local window   L(i) = { j : |i - j| <= k, 0 <= j < n }, with j <= i
+ *                         for the causal (autoregressive) form, and
+ *   periodic skip keys    S(i) = { i - m*pi : 1 <= m <= M } (plus i + m*pi in
+ *                         the bidirectional form), keeping only keys inside
+ *                         [0, n) and outside L(i).
+ *
+ * A per-query gate alpha_i = sigmoid(g_i) enters as a log-prior: log(alpha_i)
+ * is added to the scaled logits of local keys and log(1 - alpha_i) to those
+ * of skip keys, and one softmax runs over the union.  A row whose skip set is
+ * empty gets no prior (it would be a constant shift).  Keys are never
+ * wrapped around the sequence end.
+ *
+ * Conventions shared by every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The
+ *     piattn_pattern struct is host memory, read during the call only.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and the call returns without synchronising.  The library allocates no
+ *     memory and keeps no state besides a thread-local error string.
+ *   - Every argument is validated before anything is launched.  A non-zero
+ *     status is returned on error and piattn_last_error() describes it.
+ *     Nothing aborts and nothing throws across the ABI.
+ *   - Element strides are given per tensor as {sequence, head, token}, in
+ *     elements; the head dimension d is always contiguous.
+ */
+#ifndef PIATTN_H
+#define PIATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of q, k, v and the output.  Gate logits are always fp32. */
+typedef enum { PIATTN_F32 = 0, PIATTN_BF16 = 1 } piattn_dtype;
+
+/* Status codes. */
+enum {
+    PIATTN_OK = 0,
+    PIATTN_EINVAL = 1,       /* bad pointer, size, stride, alignment or pattern */
+    PIATTN_EUNSUPPORTED = 2, /* valid request this build does not implement */
+    PIATTN_EWORKSPACE = 3,   /* decode workspace missing or too small */
+    PIATTN_EHIP = 4          /* the HIP runtime reported a launch error */
+};
+
+/*
+ * The sparsity pattern (the pages' n, k, pi; M and the gate form as stated
+ * above).
+ *   window_k      k >= 0: keys i-k..i (causal) or i-k..i+k (bidirectional)
+ *   period_pi     pi >= 1: skip stride
+ *   num_skips_M   M >= 0: skips per direction
+ *   bidirectional 0 = causal, 1 = two-sided window and skips
+ *   scale         logit scale; <= 0 selects 1/sqrt(d)
+ */
+typedef struct {
+    int32_t window_k;
+    int32_t period_pi;
+    int32_t num_skips_M;
+    int32_t bidirectional;
+    float scale;
+} piattn_pattern;
+
+/*
+ * piattn_fwd -- prefill: every query row of every (sequence, head).
+ *
+ * Dense mode (cu_seqlens == NULL): B sequences of n tokens each.  Element
+ * (b, h, t, c) of q, k, v, out lives at
+ *     base + b*s[0] + h*s[1] + t*s[2] + c
+ * with s = strides[0] (q), strides[1] (k), strides[2] (v), strides[3] (out).
+ * Gate logit (b, h, t) lives at gate_logits + b*s[0] + h*s[1] + t*s[2] with
+ * s = strides[4]; lse_out (optional, may be NULL) uses the same addressing
+ * and receives the natural-log normaliser log(sum_j exp(logit_j)) of each
+ * row, logits including the prior.
+ *
+ * Varlen mode (cu_seqlens != NULL): B packed sequences; sequence b occupies
+ * tokens [cu_seqlens[b], cu_seqlens[b+1]) of one packed token axis (device
+ * int32 array of B+1 non-decreasing offsets starting at 0).  The sequence
+ * stride s[0] is ignored and t is the packed token index.  n must be >= the
+ * longest sequence (the grid covers n rows per sequence; the library reads
+ * cu_seqlens on the device and does not check them).  No attention crosses a
+ * sequence boundary.
+ *
+ * Requirements: B, H, n >= 1; d in {32, 64, 128}; for PIATTN_BF16 the q, k,
+ * v, out pointers are 16-byte aligned and their strides multiples of 8
+ * elements; for PIATTN_F32, 16-byte aligned and multiples of 4 elements.
+ * The output must not alias an input.  Indices must fit in int64.
+ * Returns PIATTN_OK, PIATTN_EINVAL, PIATTN_EUNSUPPORTED or PIATTN_EHIP.
+ */
+int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d,
+               const void *q, const void *k, const void *v,
+               const float *gate_logits, void *out, float *lse_out,
+               const int64_t strides[5][3], const int32_t *cu_seqlens,
+               const piattn_pattern *pattern, void *stream);
+
+/*
+ * piattn_decode -- one new query per sequence against its KV cache (the
+ * pages' inference mode, gist.science section 2 "Execution & Scheduling",
+ * item "Inference").  The query of sequence s sits at position
+ * cache_lens[s] - 1: its own key and value are already in the cache, and it
+ * attends causally over the window and skips of that position.
+ *
+ *   q [S, H, d]               element (s, h, c) at q + s*s0 + h*s1 + c,
+ *                             {s0, s1, -} = strides[0]
+ *   k_cache, v_cache          element (s, h, t, c) at base + s*s0 + h*s1 + t*s2 + c,
+ *                             strides[1], strides[2]; t < cache_capacity
+ *   cache_lens [S]            device int32; a row whose length is outside
+ *                             [1, cache_capacity] is written as NaN
+ *   gate_logits [S, H]        fp32, strides[4] (token stride ignored)
+ *   out [S, H, d]             strides[3] (token stride ignored)
+ *   pattern                   must be causal (bidirectional == 0)
+ *   num_splits                key-range splits per (sequence, head); 0 = auto
+ *   workspace                 device scratch of at least
+ *                             piattn_decode_workspace_bytes(S, H, d, num_splits,
+ *                             pattern)
+ *                             bytes, 256-byte aligned (unused, may be NULL, when
+ *                             that size is 0)
+ * Alignment rules as for piattn_fwd.  Calls that share a workspace must be
+ * ordered on one stream.
+ */
+int piattn_decode(piattn_dtype dtype, int32_t S, int32_t H, int32_t d,
+                  const void *q, const void *k_cache, const void *v_cache,
+                  const int32_t *cache_lens, int32_t cache_capacity,
+                  const float *gate_logits, void *out,
+                  const int64_t strides[5][3], const piattn_pattern *pattern,
+                  int32_t num_splits, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/* Workspace bytes piattn_decode needs for this shape and split count
+ * (num_splits 0 = the automatic choice for `pattern`).  0 means no workspace
+ * is needed; 0 is also returned for invalid arguments. */
+size_t piattn_decode_workspace_bytes(int32_t S, int32_t H, int32_t d,
+                                     int32_t num_splits,
+                                     const piattn_pattern *pattern);
+
+/* Number of splits piattn_decode uses for num_splits = 0 on this shape. */
+int32_t piattn_decode_auto_splits(int32_t S, int32_t H, int32_t d,
+                                  const piattn_pattern *pattern);
+
+/*
+ * piattn_neighbors -- debug dump of the neighbour lists that the compute
+ * kernels enumerate, for queries q_begin .. q_begin+q_count-1 of a sequence
+ * of length n.  Row r of idx [q_count, cap] (device int32) receives the keys
+ * in ascending order, padded with -1; kind [q_count, cap] (device int8)
+ * receives 1 for a local key, 2 for a skip key, 0 for padding; count
+ * [q_count] (device int32) the list length.  cap must be at least
+ * piattn_neighbors_cap(pattern).
+ */
+int piattn_neighbors(int32_t n, const piattn_pattern *pattern, int32_t q_begin,
+                     int32_t q_count, int32_t cap, int32_t *idx, int8_t *kind,
+                     int32_t *count, void *stream);
+
+/* Longest possible list: (k+1)+M causal, (2k+1)+2M bidirectional; -1 if the
+ * pattern is invalid. */
+int32_t piattn_neighbors_cap(const piattn_pattern *pattern);
+
+/* Description of the last error on this thread ("" if none). */
+const char *piattn_last_error(void);
+
+/* Library version string. */
+const char *piattn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PIATTN_H */

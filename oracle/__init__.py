@@ -58,6 +58,8 @@ def _load():
         lib.oracle_decode.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp, vp, i32, i32,
                                       i32, dbl, vp, vp, i32]
         lib.oracle_decode.restype = None
+        lib.oracle_neighbor_table.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
+        lib.oracle_neighbor_table.restype = i32
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         _lib = lib
@@ -100,15 +102,13 @@ def neighbor_table(n: int, k: int, pi: int, M: int, bidir: bool, q_begin: int = 
         q_count = n - q_begin
     if cap is None:
         cap = (2 * k + 1 + 2 * M) if bidir else (k + 1 + M)
-    idx = np.full((q_count, cap), -1, np.int32)
-    kind = np.zeros((q_count, cap), np.int8)
-    cnt = np.zeros(q_count, np.int32)
-    for r in range(q_count):
-        ii, kk = neighbors(n, k, pi, M, bidir, q_begin + r)
-        assert len(ii) <= cap
-        idx[r, :len(ii)] = ii
-        kind[r, :len(kk)] = kk
-        cnt[r] = len(ii)
+    idx = np.empty((q_count, cap), np.int32)
+    kind = np.empty((q_count, cap), np.int8)
+    cnt = np.empty(q_count, np.int32)
+    rc = _load().oracle_neighbor_table(n, k, pi, M, int(bool(bidir)), q_begin, q_count, cap,
+                                       _ptr(idx), _ptr(kind), _ptr(cnt))
+    if rc != 0:
+        raise ValueError("a neighbour list does not fit in cap=%d" % cap)
     return idx, kind, cnt
 
 

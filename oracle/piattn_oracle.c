@@ -282,3 +282,40 @@ int oracle_max_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Neighbour lists of queries q_begin .. q_begin+q_count-1 as a padded table:
+ * idx [q_count, cap] (-1 padding), kind [q_count, cap] (0 padding),
+ * count [q_count].  Returns 0, or -1 if some list does not fit in cap.
+ */
+int oracle_neighbor_table(int n, int k, int pi, int M, int bidir, int q_begin,
+                          int q_count, int cap, int32_t *idx, int8_t *kind,
+                          int32_t *count)
+{
+    int bad = 0;
+    int full = list_cap(k, M);
+#pragma omp parallel
+    {
+        int32_t *ti = (int32_t *)malloc(sizeof(int32_t) * full);
+        int8_t *tk = (int8_t *)malloc((size_t)full);
+        int r;
+#pragma omp for schedule(static)
+        for (r = 0; r < q_count; ++r) {
+            int c = oracle_neighbors(n, k, pi, M, bidir, q_begin + r, ti, tk);
+            int a;
+            if (c > cap) {
+#pragma omp atomic write
+                bad = 1;
+                c = cap;
+            }
+            for (a = 0; a < cap; ++a) {
+                idx[(int64_t)r * cap + a] = a < c ? ti[a] : -1;
+                kind[(int64_t)r * cap + a] = a < c ? tk[a] : 0;
+            }
+            count[r] = c;
+        }
+        free(ti);
+        free(tk);
+    }
+    return bad ? -1 : 0;
+}

@@ -1,0 +1,11 @@
+"""sparse_long_context_piattn_amd -- pi-Attention forward on AMD MI355X.
+
+The compute lives in libpiattn.so (HIP kernels for gfx950, C ABI in
+include/piattn.h); this package is its thin Python binding plus the seeded
+synthetic workloads used by the tests and the benchmark.
+"""
+from .binding import (Pattern, PiattnError, decode, decode_workspace_bytes, fwd, lib,
+                      make_pattern, neighbors, neighbors_cap, version)
+
+__all__ = ["Pattern", "PiattnError", "decode", "decode_workspace_bytes", "fwd", "lib",
+           "make_pattern", "neighbors", "neighbors_cap", "version"]

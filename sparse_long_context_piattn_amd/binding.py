@@ -1,0 +1,246 @@
+"""Thin ctypes binding over libpiattn (include/piattn.h).
+
+Argument marshalling only: shapes and dtypes are checked, strides and data
+pointers are read from torch tensors, and the call is enqueued on torch's
+current HIP stream.  Every step of the computation runs in the HIP kernels of
+libpiattn.so; if that library is missing the calls raise -- there is no
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpiattn.so")
+
+PIATTN_F32, PIATTN_BF16 = 0, 1
+STATUS = {0: "PIATTN_OK", 1: "PIATTN_EINVAL", 2: "PIATTN_EUNSUPPORTED", 3: "PIATTN_EWORKSPACE",
+          4: "PIATTN_EHIP"}
+
+EXPORTS = ["piattn_fwd", "piattn_decode", "piattn_decode_workspace_bytes",
+           "piattn_decode_auto_splits", "piattn_neighbors", "piattn_neighbors_cap",
+           "piattn_last_error", "piattn_version"]
+
+
+class PiattnError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__("%s: %s" % (STATUS.get(code, str(code)), msg))
+        self.code = code
+
+
+class Pattern(ctypes.Structure):
+    """piattn_pattern: window half-width k, period pi, skips M, direction, scale."""
+    _fields_ = [("window_k", ctypes.c_int32), ("period_pi", ctypes.c_int32),
+                ("num_skips_M", ctypes.c_int32), ("bidirectional", ctypes.c_int32),
+                ("scale", ctypes.c_float)]
+
+
+Strides = ctypes.c_int64 * 15
+_lib = None
+
+
+def lib():
+    """Load libpiattn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libpiattn.so is not built; run "
+                               "`python -m sparse_long_context_piattn_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        pat = ctypes.POINTER(Pattern)
+        L.piattn_fwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                 ctypes.POINTER(Strides), vp, pat, vp]
+        L.piattn_fwd.restype = ctypes.c_int
+        L.piattn_decode.argtypes = [ctypes.c_int, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp,
+                                    ctypes.POINTER(Strides), pat, i32, vp, sz, vp]
+        L.piattn_decode.restype = ctypes.c_int
+        L.piattn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32, pat]
+        L.piattn_decode_workspace_bytes.restype = sz
+        L.piattn_decode_auto_splits.argtypes = [i32, i32, i32, pat]
+        L.piattn_decode_auto_splits.restype = i32
+        L.piattn_neighbors.argtypes = [i32, pat, i32, i32, i32, vp, vp, vp, vp]
+        L.piattn_neighbors.restype = ctypes.c_int
+        L.piattn_neighbors_cap.argtypes = [pat]
+        L.piattn_neighbors_cap.restype = i32
+        L.piattn_last_error.argtypes = []
+        L.piattn_last_error.restype = ctypes.c_char_p
+        L.piattn_version.argtypes = []
+        L.piattn_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise PiattnError(rc, lib().piattn_last_error().decode())
+
+
+def make_pattern(k: int, pi: int, M: int, bidir: bool = False, scale: float = 0.0) -> Pattern:
+    return Pattern(int(k), int(pi), int(M), int(bool(bidir)), float(scale))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return PIATTN_F32
+    if t.dtype == torch.bfloat16:
+        return PIATTN_BF16
+    raise TypeError("q/k/v must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+def fwd(q, k, v, g, *, window_k: int, period_pi: int, num_skips: int, bidirectional=False,
+        scale: float = 0.0, cu_seqlens=None, max_seqlen: int | None = None, out=None,
+        lse=None):
+    """pi-Attention prefill.
+
+    Dense: q, k, v [B, H, n, d] (any strides, last dim contiguous), g [B, H, n].
+    Varlen: q, k, v [T, H, d], g [T, H], cu_seqlens int32 [B + 1] on the GPU.
+    Returns out (same shape and dtype as q); lse, if given, is written with
+    the natural-log normaliser of each row (shape of g, fp32).
+    """
+    code = _dtype_code(q)
+    _need_cuda(q, k, v, g, out, lse, cu_seqlens)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    if g.dtype != torch.float32:
+        raise TypeError("gate logits must be float32")
+    if out is None:
+        out = torch.empty_like(q)
+    if q.numel() == 0 or (cu_seqlens is not None and cu_seqlens.numel() <= 1):
+        return out  # nothing to attend
+    if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("dense mode expects q [B, H, n, d]")
+        B, H, n, d = q.shape
+        if k.shape != q.shape or v.shape != q.shape or out.shape != q.shape:
+            raise ValueError("q, k, v, out shapes differ")
+        if tuple(g.shape) != (B, H, n):
+            raise ValueError("g must be [B, H, n]")
+        st4 = [tuple(t.stride()[:3]) for t in (q, k, v, out)]
+        gst = tuple(g.stride())
+        if lse is not None and (tuple(lse.shape) != (B, H, n) or lse.stride() != g.stride()):
+            raise ValueError("lse must have g's shape and strides")
+        cu_ptr = None
+    else:
+        if q.dim() != 3:
+            raise ValueError("varlen mode expects q [T, H, d]")
+        T, H, d = q.shape
+        if k.shape != q.shape or v.shape != q.shape or out.shape != q.shape:
+            raise ValueError("q, k, v, out shapes differ")
+        if tuple(g.shape) != (T, H):
+            raise ValueError("g must be [T, H]")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+        B = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            cu_h = cu_seqlens.cpu()
+            max_seqlen = int((cu_h[1:] - cu_h[:-1]).max()) if B > 0 else 0
+        n = int(max_seqlen)
+        if n == 0:
+            return out
+        st4 = [(0, t.stride(1), t.stride(0)) for t in (q, k, v, out)]
+        gst = (0, g.stride(1), g.stride(0))
+        if lse is not None and (tuple(lse.shape) != (T, H) or lse.stride() != g.stride()):
+            raise ValueError("lse must have g's shape and strides")
+        cu_ptr = _ptr(cu_seqlens)
+    for t in (q, k, v, out):
+        if t.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
+    strides = Strides(*[x for s in st4 for x in s], *gst)
+    pat = make_pattern(window_k, period_pi, num_skips, bidirectional, scale)
+    rc = lib().piattn_fwd(code, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out),
+                          _ptr(lse), ctypes.byref(strides), cu_ptr, ctypes.byref(pat),
+                          ctypes.c_void_p(_stream(q.device)))
+    _check(rc)
+    return out
+
+
+def decode_workspace_bytes(S, H, d, num_splits, pattern: Pattern) -> int:
+    return int(lib().piattn_decode_workspace_bytes(S, H, d, num_splits, ctypes.byref(pattern)))
+
+
+def decode(q, k_cache, v_cache, cache_lens, g, *, window_k: int, period_pi: int,
+           num_skips: int, scale: float = 0.0, num_splits: int = 0, workspace=None, out=None):
+    """pi-Attention decode: q [S, H, d], caches [S, H, L, d] (strided, last dim
+    contiguous), cache_lens int32 [S] (query position len-1), g [S, H].
+    workspace: optional uint8 GPU tensor; allocated here when needed and absent."""
+    code = _dtype_code(q)
+    _need_cuda(q, k_cache, v_cache, cache_lens, g, out, workspace)
+    if q.dim() != 3 or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expect q [S, H, d] and caches [S, H, L, d]")
+    S, H, d = q.shape
+    if tuple(k_cache.shape[:2]) != (S, H) or k_cache.shape[3] != d:
+        raise ValueError("cache shape does not match q")
+    if cache_lens.dtype != torch.int32 or tuple(cache_lens.shape) != (S,):
+        raise ValueError("cache_lens must be int32 [S]")
+    if g.dtype != torch.float32 or tuple(g.shape) != (S, H):
+        raise ValueError("g must be float32 [S, H]")
+    if out is None:
+        out = torch.empty_like(q)
+    pat = make_pattern(window_k, period_pi, num_skips, False, scale)
+    need = decode_workspace_bytes(S, H, d, num_splits, pat)
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    for t in (q, k_cache, v_cache, out):
+        if t.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
+    st = [(q.stride(0), q.stride(1), 0), tuple(k_cache.stride()[:3]),
+          tuple(v_cache.stride()[:3]), (out.stride(0), out.stride(1), 0),
+          (g.stride(0), g.stride(1), 0)]
+    strides = Strides(*[x for s in st for x in s])
+    rc = lib().piattn_decode(code, S, H, d, _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                             _ptr(cache_lens), k_cache.shape[2], _ptr(g), _ptr(out),
+                             ctypes.byref(strides), ctypes.byref(pat), int(num_splits),
+                             _ptr(workspace), wbytes, ctypes.c_void_p(_stream(q.device)))
+    _check(rc)
+    return out
+
+
+def neighbors_cap(window_k, period_pi, num_skips, bidirectional=False) -> int:
+    pat = make_pattern(window_k, period_pi, num_skips, bidirectional)
+    return int(lib().piattn_neighbors_cap(ctypes.byref(pat)))
+
+
+def neighbors(n: int, *, window_k: int, period_pi: int, num_skips: int, bidirectional=False,
+              q_begin: int = 0, q_count: int | None = None, cap: int | None = None,
+              device="cuda"):
+    """Debug dump: (idx int32 [q_count, cap], kind int8, count int32) on the GPU."""
+    pat = make_pattern(window_k, period_pi, num_skips, bidirectional)
+    if q_count is None:
+        q_count = n - q_begin
+    if cap is None:
+        cap = min(int(lib().piattn_neighbors_cap(ctypes.byref(pat))), n)
+    idx = torch.empty((q_count, cap), dtype=torch.int32, device=device)
+    kind = torch.empty((q_count, cap), dtype=torch.int8, device=device)
+    count = torch.empty(q_count, dtype=torch.int32, device=device)
+    rc = lib().piattn_neighbors(n, ctypes.byref(pat), q_begin, q_count, cap, _ptr(idx),
+                                _ptr(kind), _ptr(count), ctypes.c_void_p(_stream(idx.device)))
+    _check(rc)
+    return idx, kind, count
+
+
+def version() -> str:
+    return lib().piattn_version().decode()
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

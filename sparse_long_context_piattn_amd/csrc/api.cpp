@@ -1,0 +1,276 @@
+// api.cpp -- the C ABI of libpiattn: argument validation, kernel selection
+// and launches on the caller's stream.  Declarations and the contract of
+// every entry point are in include/piattn.h.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/piattn.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return PIATTN_OK;
+}
+
+constexpr int32_t kMaxExtent = 1 << 30;  // n + k and friends stay far from int32 overflow
+
+int check_pattern(const piattn_pattern* p, PiPattern* out) {
+    if (!p) return fail(PIATTN_EINVAL, "pattern is NULL");
+    if (p->window_k < 0 || p->window_k >= kMaxExtent)
+        return fail(PIATTN_EINVAL, "window_k=%d out of range [0, 2^30)", p->window_k);
+    if (p->period_pi < 1 || p->period_pi >= kMaxExtent)
+        return fail(PIATTN_EINVAL, "period_pi=%d out of range [1, 2^30)", p->period_pi);
+    if (p->num_skips_M < 0 || p->num_skips_M >= kMaxExtent)
+        return fail(PIATTN_EINVAL, "num_skips_M=%d out of range [0, 2^30)", p->num_skips_M);
+    if (p->bidirectional != 0 && p->bidirectional != 1)
+        return fail(PIATTN_EINVAL, "bidirectional=%d must be 0 or 1", p->bidirectional);
+    if (!isfinite(p->scale)) return fail(PIATTN_EINVAL, "scale is not finite");
+    out->k = p->window_k;
+    out->pi = p->period_pi;
+    out->M = p->num_skips_M;
+    out->bidir = p->bidirectional;
+    return PIATTN_OK;
+}
+
+float scale_log2(const piattn_pattern* p, int d) {
+    const float s = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)d);
+    return s * 1.4426950408889634f;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int check_tensor(const char* name, const void* p, const int64_t s[3], int64_t mult,
+                 bool use_seq) {
+    if (!p) return fail(PIATTN_EINVAL, "%s is NULL", name);
+    if (!aligned(p, 16)) return fail(PIATTN_EINVAL, "%s is not 16-byte aligned", name);
+    for (int j = 0; j < 3; ++j) {
+        if (j == 0 && !use_seq) continue;
+        if (s[j] < 0) return fail(PIATTN_EINVAL, "%s stride[%d]=%lld is negative", name, j,
+                                  (long long)s[j]);
+        if (s[j] % mult)
+            return fail(PIATTN_EINVAL, "%s stride[%d]=%lld is not a multiple of %lld elements",
+                        name, j, (long long)s[j], (long long)mult);
+    }
+    return PIATTN_OK;
+}
+
+Str3 str3(const int64_t s[3]) { return Str3{s[0], s[1], s[2]}; }
+
+int launch_status(hipError_t e) {
+    if (e != hipSuccess) return fail(PIATTN_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int decode_splits_for(int32_t S, int32_t H, const PiPattern& p) {
+    // Enough workgroups to cover the chip several times, but at least 64
+    // union positions per split so that each split still streams rows.
+    const int64_t rows = (int64_t)S * H;
+    const int64_t umax = (int64_t)p.k + 1 + p.M;
+    int64_t want = (2048 + rows - 1) / rows;
+    int64_t cap = umax / 64 > 0 ? umax / 64 : 1;
+    if (want > cap) want = cap;
+    if (want < 1) want = 1;
+    if (want > 64) want = 64;
+    return (int)want;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* piattn_last_error(void) { return g_err; }
+
+const char* piattn_version(void) { return "libpiattn 0.1 (gfx950)"; }
+
+int32_t piattn_neighbors_cap(const piattn_pattern* pattern) {
+    PiPattern p;
+    if (check_pattern(pattern, &p) != PIATTN_OK) return -1;
+    const int64_t cap = p.bidir ? 2LL * p.k + 1 + 2LL * p.M : (int64_t)p.k + 1 + p.M;
+    return cap > INT32_MAX ? -1 : (int32_t)cap;
+}
+
+int piattn_neighbors(int32_t n, const piattn_pattern* pattern, int32_t q_begin, int32_t q_count,
+                     int32_t cap, int32_t* idx, int8_t* kind, int32_t* count, void* stream) {
+    PiPattern p;
+    int rc = check_pattern(pattern, &p);
+    if (rc) return rc;
+    if (n < 1 || n >= kMaxExtent) return fail(PIATTN_EINVAL, "n=%d out of range [1, 2^30)", n);
+    if (q_begin < 0 || q_count < 0 || (int64_t)q_begin + q_count > n)
+        return fail(PIATTN_EINVAL, "query range [%d, %d+%d) not inside [0, %d)", q_begin, q_begin,
+                    q_count, n);
+    const int64_t need = p.bidir ? 2LL * p.k + 1 + 2LL * p.M : (int64_t)p.k + 1 + p.M;
+    const int64_t need_n = need < n ? need : n;  // a list never exceeds n keys
+    if (cap < need_n)
+        return fail(PIATTN_EINVAL, "cap=%d is smaller than the longest list (%lld)", cap,
+                    (long long)need_n);
+    if (q_count == 0) return ok();
+    if (!idx || !kind || !count) return fail(PIATTN_EINVAL, "idx, kind and count must be non-NULL");
+    return launch_status(launch_neighbors(n, p, q_begin, q_count, cap, idx, kind, count,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, const void* q,
+               const void* k, const void* v, const float* gate_logits, void* out, float* lse_out,
+               const int64_t strides[5][3], const int32_t* cu_seqlens,
+               const piattn_pattern* pattern, void* stream) {
+    if (dtype != PIATTN_F32 && dtype != PIATTN_BF16)
+        return fail(PIATTN_EINVAL, "dtype=%d is not PIATTN_F32 or PIATTN_BF16", (int)dtype);
+    PiPattern p;
+    int rc = check_pattern(pattern, &p);
+    if (rc) return rc;
+    if (B < 1 || B > 65535) return fail(PIATTN_EINVAL, "B=%d out of range [1, 65535]", B);
+    if (H < 1 || H > 65535) return fail(PIATTN_EINVAL, "H=%d out of range [1, 65535]", H);
+    if (n < 1 || n >= kMaxExtent - p.k)
+        return fail(PIATTN_EINVAL, "n=%d out of range (n >= 1, n + k < 2^30)", n);
+    if (d < 1) return fail(PIATTN_EINVAL, "d=%d must be positive", d);
+    if (d != 32 && d != 64 && d != 128)
+        return fail(PIATTN_EUNSUPPORTED, "d=%d unsupported (32, 64 or 128)", d);
+    if (!strides) return fail(PIATTN_EINVAL, "strides is NULL");
+    const int64_t mult = dtype == PIATTN_BF16 ? 8 : 4;
+    const bool dense = cu_seqlens == nullptr;
+    if ((rc = check_tensor("q", q, strides[0], mult, dense))) return rc;
+    if ((rc = check_tensor("k", k, strides[1], mult, dense))) return rc;
+    if ((rc = check_tensor("v", v, strides[2], mult, dense))) return rc;
+    if ((rc = check_tensor("out", out, strides[3], mult, dense))) return rc;
+    if (!gate_logits) return fail(PIATTN_EINVAL, "gate_logits is NULL");
+    if (!aligned(gate_logits, 4) || (lse_out && !aligned(lse_out, 4)))
+        return fail(PIATTN_EINVAL, "gate_logits / lse_out must be 4-byte aligned");
+    for (int j = 0; j < 3; ++j)
+        if (strides[4][j] < 0) return fail(PIATTN_EINVAL, "gate stride[%d] is negative", j);
+    if (out == q || out == k || out == v) return fail(PIATTN_EINVAL, "out aliases an input");
+    if (!dense && !aligned(cu_seqlens, 4))
+        return fail(PIATTN_EINVAL, "cu_seqlens must be 4-byte aligned");
+
+    FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = gate_logits;
+    a.o = out;
+    a.lse = lse_out;
+    a.sq = str3(strides[0]);
+    a.sk = str3(strides[1]);
+    a.sv = str3(strides[2]);
+    a.so = str3(strides[3]);
+    a.sg = str3(strides[4]);
+    a.cu = cu_seqlens;
+    a.B = B;
+    a.H = H;
+    a.n = n;
+    a.d = d;
+    a.pat = p;
+    a.scale_log2 = scale_log2(pattern, d);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return launch_status(launch_fwd_gather(dtype == PIATTN_BF16 ? 1 : 0, a, st));
+}
+
+size_t piattn_decode_workspace_bytes(int32_t S, int32_t H, int32_t d, int32_t num_splits,
+                                     const piattn_pattern* pattern) {
+    if (S < 1 || H < 1 || d < 1 || num_splits < 0 || num_splits > 64) return 0;
+    int splits = num_splits;
+    if (splits == 0) {
+        PiPattern p;
+        if (check_pattern(pattern, &p) != PIATTN_OK) return 0;
+        splits = decode_splits_for(S, H, p);
+    }
+    if (splits <= 1) return 0;
+    return (size_t)S * H * splits * (d + 2) * sizeof(float);
+}
+
+int32_t piattn_decode_auto_splits(int32_t S, int32_t H, int32_t d, const piattn_pattern* pattern) {
+    PiPattern p;
+    (void)d;
+    if (check_pattern(pattern, &p) != PIATTN_OK || S < 1 || H < 1) return -1;
+    return decode_splits_for(S, H, p);
+}
+
+int piattn_decode(piattn_dtype dtype, int32_t S, int32_t H, int32_t d, const void* q,
+                  const void* k_cache, const void* v_cache, const int32_t* cache_lens,
+                  int32_t cache_capacity, const float* gate_logits, void* out,
+                  const int64_t strides[5][3], const piattn_pattern* pattern, int32_t num_splits,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    if (dtype != PIATTN_F32 && dtype != PIATTN_BF16)
+        return fail(PIATTN_EINVAL, "dtype=%d is not PIATTN_F32 or PIATTN_BF16", (int)dtype);
+    PiPattern p;
+    int rc = check_pattern(pattern, &p);
+    if (rc) return rc;
+    if (p.bidir) return fail(PIATTN_EINVAL, "decode needs a causal pattern (bidirectional=0)");
+    if (S < 1 || H < 1 || (int64_t)S * H > INT32_MAX)
+        return fail(PIATTN_EINVAL, "S=%d H=%d out of range", S, H);
+    if (cache_capacity < 1 || cache_capacity >= kMaxExtent - p.k)
+        return fail(PIATTN_EINVAL, "cache_capacity=%d out of range", cache_capacity);
+    if (d < 1) return fail(PIATTN_EINVAL, "d=%d must be positive", d);
+    if (d != 32 && d != 64 && d != 128)
+        return fail(PIATTN_EUNSUPPORTED, "d=%d unsupported (32, 64 or 128)", d);
+    if (!strides) return fail(PIATTN_EINVAL, "strides is NULL");
+    if (num_splits < 0 || num_splits > 64)
+        return fail(PIATTN_EINVAL, "num_splits=%d out of range [0, 64]", num_splits);
+    const int64_t mult = dtype == PIATTN_BF16 ? 8 : 4;
+    int64_t sq[3] = {strides[0][0], strides[0][1], 0};
+    int64_t so[3] = {strides[3][0], strides[3][1], 0};
+    if ((rc = check_tensor("q", q, sq, mult, true))) return rc;
+    if ((rc = check_tensor("k_cache", k_cache, strides[1], mult, true))) return rc;
+    if ((rc = check_tensor("v_cache", v_cache, strides[2], mult, true))) return rc;
+    if ((rc = check_tensor("out", out, so, mult, true))) return rc;
+    if (!gate_logits || !aligned(gate_logits, 4))
+        return fail(PIATTN_EINVAL, "gate_logits is NULL or misaligned");
+    if (strides[4][0] < 0 || strides[4][1] < 0)
+        return fail(PIATTN_EINVAL, "gate strides are negative");
+    if (!cache_lens || !aligned(cache_lens, 4))
+        return fail(PIATTN_EINVAL, "cache_lens is NULL or misaligned");
+    if (out == q || out == k_cache || out == v_cache)
+        return fail(PIATTN_EINVAL, "out aliases an input");
+
+    const int splits = num_splits == 0 ? decode_splits_for(S, H, p) : num_splits;
+    const size_t need = splits > 1 ? (size_t)S * H * splits * (d + 2) * sizeof(float) : 0;
+    if (need) {
+        if (!workspace) return fail(PIATTN_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+        if (workspace_bytes < need)
+            return fail(PIATTN_EWORKSPACE, "workspace of %zu bytes is smaller than %zu", workspace_bytes,
+                        need);
+        if (!aligned(workspace, 256)) return fail(PIATTN_EINVAL, "workspace is not 256-byte aligned");
+    }
+    const int64_t umax = (int64_t)p.k + 1 + p.M;
+
+    DecodeArgs a;
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.lens = cache_lens;
+    a.g = gate_logits;
+    a.o = out;
+    a.ws = static_cast<float*>(workspace);
+    a.sq = Str3{strides[0][0], strides[0][1], 0};
+    a.sk = str3(strides[1]);
+    a.sv = str3(strides[2]);
+    a.so = Str3{strides[3][0], strides[3][1], 0};
+    a.sg = Str3{strides[4][0], strides[4][1], 0};
+    a.S = S;
+    a.H = H;
+    a.d = d;
+    a.cap = cache_capacity;
+    a.splits = splits;
+    a.chunk = (int32_t)((umax + splits - 1) / splits);
+    a.pat = p;
+    a.scale_log2 = scale_log2(pattern, d);
+    return launch_status(launch_decode(dtype == PIATTN_BF16 ? 1 : 0, a,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// common.hpp -- argument blocks and small device helpers shared by the
+// libpiattn kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pattern.hpp"
+
+#define PIATTN_LOG2E 1.4426950408889634f
+#define PIATTN_LN2 0.6931471805599453f
+
+// Strides of one tensor, in elements: sequence, head, token.
+struct Str3 {
+    int64_t s, h, t;
+};
+
+struct FwdArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    void* o;
+    float* lse;
+    Str3 sq, sk, sv, so, sg;
+    const int32_t* cu;   // varlen offsets or nullptr
+    int32_t B, H, n, d;
+    PiPattern pat;
+    float scale_log2;    // logit scale * log2(e)
+};
+
+struct DecodeArgs {
+    const void* q;
+    const void* kc;
+    const void* vc;
+    const int32_t* lens;
+    const float* g;
+    void* o;
+    float* ws;           // partials [S*H][splits][d + 2] when splits > 1
+    Str3 sq, sk, sv, so, sg;
+    int32_t S, H, d, cap;
+    int32_t splits;
+    int32_t chunk;       // union positions per split
+    PiPattern pat;
+    float scale_log2;
+};
+
+// ---------------------------------------------------------------- bf16
+
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 with round-to-nearest-even; NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+// ---------------------------------------------------------------- gate
+
+// log2(sigmoid(x)) computed without overflow: -softplus(-x) / ln 2.
+__device__ __forceinline__ float log2_sigmoid(float x) {
+    // softplus(y) = max(y, 0) + log1p(exp(-|y|))
+    const float y = -x;
+    const float sp = fmaxf(y, 0.0f) + log1pf(__expf(-fabsf(y)));
+    return -sp * PIATTN_LOG2E;
+}
+
+// Priors in log2 units for a row: local gets log2(alpha), skip log2(1-alpha);
+// both zero when the row has no skip keys.
+__device__ __forceinline__ void gate_priors(float g, bool has_skip, float* pl, float* ps) {
+    if (has_skip) {
+        *pl = log2_sigmoid(g);
+        *ps = log2_sigmoid(-g);
+    } else {
+        *pl = 0.0f;
+        *ps = 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------- wave helpers
+
+template <int MASK>
+__device__ __forceinline__ float shfl_xor_f(float x) {
+    return __shfl_xor(x, MASK, 64);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }

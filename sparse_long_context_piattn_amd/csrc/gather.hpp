@@ -1,0 +1,138 @@
+// gather.hpp -- per-row gather attention on one wavefront (gfx950, wave64).
+//
+// A wave owns one query row.  Its 64 lanes form NS = 512/D key slots of
+// LPK = D/8 lanes each; a lane holds 8 consecutive head-dimension elements
+// of the query, of the slot's key and value, and of the running output.
+// Keys are taken NS at a time from the row's union (RowSpan order); each
+// slot reduces its dot product over its LPK lanes, the chunk maximum is
+// reduced over the slots, and one online softmax (running max m in log2
+// units, shared by the wave; per-lane partial sum l and accumulator) absorbs
+// local and skip keys alike, the gate prior being added to each logit
+// according to the key's kind (pi-Attention "Dynamic Adaptive Fusion":
+// log(alpha) on local logits, log(1 - alpha) on skip logits, one softmax).
+//
+// This path serves fp32, d = 32, and patterns the tiled prefill kernel does
+// not take, and is the building block of split-K decode.
+#pragma once
+
+#include "common.hpp"
+
+template <typename T>
+struct Elem;
+
+template <>
+struct Elem<float> {
+    static __device__ __forceinline__ void load8(const float* p, float x[8]) {
+        const float4 a = *reinterpret_cast<const float4*>(p);
+        const float4 b = *reinterpret_cast<const float4*>(p + 4);
+        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    }
+    static __device__ __forceinline__ void store8(float* p, const float x[8]) {
+        *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+    }
+};
+
+// bf16 is carried as its raw 16-bit pattern.
+template <>
+struct Elem<uint16_t> {
+    static __device__ __forceinline__ void load8(const uint16_t* p, float x[8]) {
+        const uint4 w = *reinterpret_cast<const uint4*>(p);
+        x[0] = bf16lo(w.x); x[1] = bf16hi(w.x); x[2] = bf16lo(w.y); x[3] = bf16hi(w.y);
+        x[4] = bf16lo(w.z); x[5] = bf16hi(w.z); x[6] = bf16lo(w.w); x[7] = bf16hi(w.w);
+    }
+    static __device__ __forceinline__ void store8(uint16_t* p, const float x[8]) {
+        uint4 w;
+        w.x = pack_bf16x2(x[0], x[1]);
+        w.y = pack_bf16x2(x[2], x[3]);
+        w.z = pack_bf16x2(x[4], x[5]);
+        w.w = pack_bf16x2(x[6], x[7]);
+        *reinterpret_cast<uint4*>(p) = w;
+    }
+};
+
+template <int D>
+struct GatherShape {
+    static_assert(D == 32 || D == 64 || D == 128, "head dim");
+    static constexpr int LPK = D / 8;   // lanes per key
+    static constexpr int NS = 64 / LPK; // key slots per wave
+};
+
+// Online-softmax partial state of one wave over a range of union positions.
+struct RowPartial {
+    float m;       // running max (log2 units), wave-uniform
+    float l;       // sum of exp2(s - m) over this lane's slot
+    float acc[8];  // sum of exp2(s - m) * v over this lane's slot
+};
+
+// Process union positions [u0, u1) of row i.  kbase/vbase point at token 0
+// of the row's (sequence, head); k_tok_stride / v_tok_stride are the token
+// strides of the key and value tensors.
+template <typename T, int D>
+__device__ __forceinline__ void gather_row(const T* __restrict__ qrow, const T* __restrict__ kbase,
+                                           const T* __restrict__ vbase, int64_t k_tok_stride,
+                                           int64_t v_tok_stride,
+                                           const RowSpan& sp, int32_t i, int32_t pi, int32_t u0,
+                                           int32_t u1, float pl, float ps, float scale_log2,
+                                           RowPartial& st) {
+    using G = GatherShape<D>;
+    const int lane = threadIdx.x & 63;
+    const int slot = lane / G::LPK;
+    const int c = (lane % G::LPK) * 8;
+    float qv[8];
+    Elem<T>::load8(qrow + c, qv);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) qv[j] *= scale_log2;
+    st.m = -INFINITY;
+    st.l = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) st.acc[j] = 0.0f;
+
+    for (int32_t base = u0; base < u1; base += G::NS) {
+        const int32_t u = base + slot;
+        const bool valid = u < u1;
+        float kv[8], vv[8];
+        float prior = 0.0f;
+        if (valid) {
+            bool loc;
+            const int32_t key = span_key(sp, i, pi, u, &loc);
+            Elem<T>::load8(kbase + (int64_t)key * k_tok_stride + c, kv);
+            Elem<T>::load8(vbase + (int64_t)key * v_tok_stride + c, vv);
+            prior = loc ? pl : ps;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) kv[j] = vv[j] = 0.0f;
+        }
+        float dot = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) dot = fmaf(qv[j], kv[j], dot);
+#pragma unroll
+        for (int off = 1; off < G::LPK; off <<= 1) dot += __shfl_xor(dot, off, 64);
+        const float s = valid ? dot + prior : -INFINITY;
+        float cmax = s;
+#pragma unroll
+        for (int off = G::LPK; off < 64; off <<= 1) cmax = fmaxf(cmax, __shfl_xor(cmax, off, 64));
+        const float mnew = fmaxf(st.m, cmax);
+        const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
+        const float fac = exp2_fast(st.m - mu);
+        const float p = exp2_fast(s - mu);
+        st.l = fmaf(st.l, fac, p);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st.acc[j] = fmaf(st.acc[j], fac, p * vv[j]);
+        st.m = mnew;
+    }
+}
+
+// Sum l and acc over the key slots; afterwards every lane holds the wave's
+// totals for its 8 head-dimension elements.
+template <int D>
+__device__ __forceinline__ void reduce_slots(RowPartial& st) {
+    using G = GatherShape<D>;
+#pragma unroll
+    for (int off = G::LPK; off < 64; off <<= 1) {
+        st.l += __shfl_xor(st.l, off, 64);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st.acc[j] += __shfl_xor(st.acc[j], off, 64);
+    }
+}

@@ -1,0 +1,152 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/piattn.h declares, and rejects bad arguments before launching
+anything (fake, never-dereferenced device addresses are passed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_long_context_piattn_amd as pa
+from sparse_long_context_piattn_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "piattn.h")
+
+EINVAL, EUNSUPPORTED, EWORKSPACE = 1, 2, 3
+A = ctypes.c_void_p(1 << 20)      # 16-byte aligned fake device address (never touched)
+A2 = ctypes.c_void_p(2 << 20)
+A3 = ctypes.c_void_p(3 << 20)
+OUT = ctypes.c_void_p(4 << 20)
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(piattn_\w+)\s*\(", text)))
+
+
+def test_header_declares_expected_api():
+    assert header_functions() == sorted(binding.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = pa.lib()
+    for name in header_functions():
+        assert hasattr(L, name), name
+    assert pa.version().startswith("libpiattn")
+
+
+def test_neighbors_cap_and_workspace_queries():
+    L = pa.lib()
+    assert L.piattn_neighbors_cap(ctypes.byref(pa.make_pattern(8, 16, 4))) == 13
+    assert L.piattn_neighbors_cap(ctypes.byref(pa.make_pattern(32, 64, 32, True))) == 129
+    assert L.piattn_neighbors_cap(ctypes.byref(pa.make_pattern(-1, 16, 4))) == -1
+    p = pa.make_pattern(256, 512, 63)
+    assert pa.decode_workspace_bytes(128, 32, 128, 1, p) == 0
+    assert pa.decode_workspace_bytes(2, 2, 128, 4, p) == 2 * 2 * 4 * 130 * 4
+    auto = L.piattn_decode_auto_splits(2, 2, 128, ctypes.byref(p))
+    assert 1 <= auto <= 64
+    assert pa.decode_workspace_bytes(2, 2, 128, 0, p) == (0 if auto == 1 else 2 * 2 * auto * 130 * 4)
+
+
+def _strides(vals=None):
+    vals = vals or [8 * 64 * 64, 64 * 64, 64] * 4 + [64 * 8, 64, 1]
+    return binding.Strides(*vals)
+
+
+def _fwd(dtype=1, B=1, H=1, n=64, d=64, q=A, k=A2, v=A3, g=A, out=OUT, lse=None,
+         strides=None, cu=None, pat=None):
+    L = pa.lib()
+    st = strides if strides is not None else _strides()
+    p = pat if pat is not None else pa.make_pattern(4, 16, 2)
+    rc = L.piattn_fwd(dtype, B, H, n, d, q, k, v, g, out, lse, ctypes.byref(st), cu,
+                      ctypes.byref(p), None)
+    return rc, L.piattn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dtype=7), EINVAL),
+    (dict(B=0), EINVAL),
+    (dict(H=0), EINVAL),
+    (dict(n=0), EINVAL),
+    (dict(d=48), EUNSUPPORTED),
+    (dict(d=256), EUNSUPPORTED),
+    (dict(d=0), EINVAL),
+    (dict(q=None), EINVAL),
+    (dict(g=None), EINVAL),
+    (dict(q=ctypes.c_void_p((1 << 20) + 8)), EINVAL),           # misaligned
+    (dict(out=A), EINVAL),                                       # aliases q
+    (dict(pat=pa.make_pattern(-1, 16, 2)), EINVAL),
+    (dict(pat=pa.make_pattern(4, 0, 2)), EINVAL),
+    (dict(pat=pa.make_pattern(4, 16, -3)), EINVAL),
+    (dict(pat=binding.Pattern(4, 16, 2, 2, 0.0)), EINVAL),
+    (dict(pat=binding.Pattern(4, 16, 2, 0, float("nan"))), EINVAL),
+    (dict(strides=_strides([8 * 64 * 64, 64 * 64, 60] * 4 + [64, 64, 1])), EINVAL),
+    (dict(strides=_strides([-64, 64 * 64, 64] * 4 + [64, 64, 1])), EINVAL),
+])
+def test_fwd_rejects_bad_arguments(kw, expect):
+    rc, msg = _fwd(**kw)
+    assert rc == expect and msg
+
+
+def test_fwd_strides_null_rejected():
+    L = pa.lib()
+    p = pa.make_pattern(4, 16, 2)
+    rc = L.piattn_fwd(1, 1, 1, 64, 64, A, A2, A3, A, OUT, None, None, None, ctypes.byref(p), None)
+    assert rc == EINVAL
+
+
+def test_fp32_stride_multiple_of_four_is_accepted_by_validation_only():
+    # fp32 needs multiples of 4 elements; 60 fails for bf16 (8) but the check
+    # for fp32 must pass it -- use an unsupported d so nothing launches.
+    rc, msg = _fwd(dtype=0, d=48, strides=_strides([8 * 64 * 60, 64 * 60, 60] * 4 + [64, 64, 1]))
+    assert rc == EUNSUPPORTED, msg
+
+
+def _decode(dtype=1, S=2, H=2, d=128, cap=100, pat=None, splits=0, ws=None, wsb=0, lens=A,
+            out=OUT):
+    L = pa.lib()
+    st = binding.Strides(*([2 * 128, 128, 0] + [2 * 100 * 128, 100 * 128, 128] * 2 +
+                           [2 * 128, 128, 0] + [2, 1, 0]))
+    p = pat if pat is not None else pa.make_pattern(8, 16, 4)
+    rc = L.piattn_decode(dtype, S, H, d, A, A2, A3, lens, cap, A, out, ctypes.byref(st),
+                         ctypes.byref(p), splits, ws, wsb, None)
+    return rc, L.piattn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(pat=pa.make_pattern(8, 16, 4, True)), EINVAL),     # decode is causal only
+    (dict(S=0), EINVAL),
+    (dict(cap=0), EINVAL),
+    (dict(d=96), EUNSUPPORTED),
+    (dict(lens=None), EINVAL),
+    (dict(splits=65), EINVAL),
+    (dict(splits=4, ws=None), EWORKSPACE),
+    (dict(splits=4, ws=ctypes.c_void_p(1 << 24), wsb=16), EWORKSPACE),
+    (dict(splits=4, ws=ctypes.c_void_p((1 << 24) + 16), wsb=1 << 20), EINVAL),  # not 256-aligned
+    (dict(out=A), EINVAL),
+])
+def test_decode_rejects_bad_arguments(kw, expect):
+    rc, msg = _decode(**kw)
+    assert rc == expect and msg
+
+
+@pytest.mark.parametrize("args,expect", [
+    ((0, 0, 1, 13), EINVAL),        # n < 1
+    ((16, 10, 7, 13), EINVAL),      # range past n
+    ((16, -1, 2, 13), EINVAL),
+    ((16, 0, 4, 12), EINVAL),       # cap below the longest list
+])
+def test_neighbors_rejects_bad_arguments(args, expect):
+    L = pa.lib()
+    n, qb, qc, cap = args
+    p = pa.make_pattern(8, 16, 4)
+    rc = L.piattn_neighbors(n, ctypes.byref(p), qb, qc, cap, A, A2, A3, None)
+    assert rc == expect and L.piattn_last_error()
+
+
+def test_neighbors_empty_range_is_a_no_op():
+    L = pa.lib()
+    p = pa.make_pattern(8, 16, 4)
+    assert L.piattn_neighbors(16, ctypes.byref(p), 3, 0, 13, None, None, None, None) == 0
