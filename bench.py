@@ -132,6 +132,76 @@ def cpu_baseline(w, x, budget_s: float):
                       "OpenMP over rows, %.1f s" % (count, w.name, total_rows, elapsed)}
 
 
+def decode_algorithmic(w):
+    """Per-call algorithmic bytes of decode: the K and V rows each (sequence,
+    head) row touches, plus q, out and the fp32 gate; flops 4*d per pair."""
+    import numpy as np
+    i = w.n - 1
+    loc = min(i, w.k) + 1
+    mlo = w.k // w.pi + 1
+    sk = max(0, min(w.M, i // w.pi) - mlo + 1)
+    rows = w.B * w.H
+    bytes_ = rows * (2 * (loc + sk) * w.d * 2 + 2 * w.d * 2 + 4)
+    flops = rows * 4 * w.d * (loc + sk)
+    return bytes_, flops, rows, loc, sk
+
+
+def bench_decode(args, w, dev):
+    import torch
+
+    import sparse_long_context_piattn_amd as pa
+    from sparse_long_context_piattn_amd import workloads as wl
+
+    alg_bytes, alg_flops, rows, loc, sk = decode_algorithmic(w)
+    log("workload %s: %d (sequence, head) rows x (%d local + %d skip) keys, %.1f MB/call"
+        % (w.name, rows, loc, sk, alg_bytes / 1e6))
+    x = wl.make_decode_inputs(w, device=dev)
+    out = torch.empty_like(x["q"])
+    pat = pa.make_pattern(w.k, w.pi, w.M)
+    splits = args.splits
+    need = pa.decode_workspace_bytes(w.B, w.H, w.d, splits, pat)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def step(_j):
+        pa.decode(x["q"], x["k_cache"], x["v_cache"], x["lens"], x["g"], window_k=w.k,
+                  period_pi=w.pi, num_skips=w.M, num_splits=splits, workspace=ws, out=out)
+
+    ms_per_step = timed(step, args, dev)
+    sec = ms_per_step / 1e3
+    gbps = alg_bytes / sec / 1e9
+    log("%.4f ms/call  %.3e row-queries/s  %.0f GB/s (%.1f%% of HBM peak)"
+        % (ms_per_step, rows / sec, gbps, 100 * gbps / HBM_PEAK_GBPS))
+    res = {"metric": "pi-attn decode (sequence, head) queries/s, 32K cache d=128 bf16, 1 GPU",
+           "value": round(rows / sec, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) cache, query and gate logits)",
+           "config": {"workload": w.name, "sequences": w.B, "H": w.H, "cache_len": w.n,
+                      "d": w.d, "k": w.k, "pi": w.pi, "M": w.M, "num_splits": splits},
+           "hbm_gbps_algorithmic": round(gbps, 1), "kernel_digest": kernel_digest(),
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                        "traffic": traffic_record(w.name)},
+           "cpu_baseline": None}
+    print(json.dumps(res), flush=True)
+
+
+def timed(step, args, dev):
+    import torch
+    for j in range(args.warmup):
+        step(j)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    for j in range(args.steps):
+        step(j)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / args.steps
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -141,6 +211,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
+    ap.add_argument("--splits", type=int, default=0, help="decode key-range splits (0 = auto)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -158,9 +229,8 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     w = wl.WORKLOADS[args.workload]
-    if w.kind != "fwd":
-        log("bench.py times prefill workloads; %s is %s" % (w.name, w.kind))
-        sys.exit(2)
+    if w.kind == "decode":
+        return bench_decode(args, w, dev)
     lengths = wl.varlen_lengths(w) if w.nseq else None
     alg_bytes, alg_flops, rows, loc, sk = algorithmic(w, lengths)
     set_bytes = alg_bytes
@@ -178,19 +248,7 @@ def main():
                bidirectional=w.bidir, cu_seqlens=x.get("cu_seqlens"),
                max_seqlen=max(lengths) if lengths else None, out=outs[j % nsets])
 
-    for j in range(args.warmup):
-        step(j)
-    torch.cuda.synchronize()
-    stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    for j in range(args.steps):
-        step(j)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    ms = ev0.elapsed_time(ev1)
-    ms_per_step = ms / args.steps
+    ms_per_step = timed(step, args, dev)
     sec = ms_per_step / 1e3
     qps = rows / sec
     achieved_gbps = alg_bytes / sec / 1e9

@@ -8,7 +8,7 @@
 
 #include <hip/hip_runtime.h>
 
-#include "../../include/piattn.h"
+#include "piattn.h"
 #include "kernels.hpp"
 
 namespace {
@@ -177,7 +177,10 @@ int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
     a.pat = p;
     a.scale_log2 = scale_log2(pattern, d);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return launch_status(launch_fwd_gather(dtype == PIATTN_BF16 ? 1 : 0, a, st));
+    const int dt = dtype == PIATTN_BF16 ? 1 : 0;
+    if (fwd_phased_supported(dt, a)) return launch_status(launch_fwd_phased(a, st));
+    if (fwd_tiled_supported(dt, a)) return launch_status(launch_fwd_tiled(a, st));
+    return launch_status(launch_fwd_gather(dt, a, st));
 }
 
 size_t piattn_decode_workspace_bytes(int32_t S, int32_t H, int32_t d, int32_t num_splits,

@@ -62,14 +62,17 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
 }
 
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
 // ---------------------------------------------------------------- gate
 
-// log2(sigmoid(x)) computed without overflow: -softplus(-x) / ln 2.
+// log2(sigmoid(x)) computed without overflow: -softplus(-x) / ln 2, with
+// softplus(y) = max(y, 0) + log(1 + exp(-|y|)).  In log2 units:
+// -max(-x, 0) * log2(e) - log2(1 + 2^(-|x| log2 e)); the second term is
+// evaluated in fp32 (absolute error ~1e-7, below the logits' rounding).
 __device__ __forceinline__ float log2_sigmoid(float x) {
-    // softplus(y) = max(y, 0) + log1p(exp(-|y|))
-    const float y = -x;
-    const float sp = fmaxf(y, 0.0f) + log1pf(__expf(-fabsf(y)));
-    return -sp * PIATTN_LOG2E;
+    const float t = exp2_fast(-fabsf(x) * PIATTN_LOG2E);
+    return -fmaxf(-x, 0.0f) * PIATTN_LOG2E - __log2f(1.0f + t);
 }
 
 // Priors in log2 units for a row: local gets log2(alpha), skip log2(1-alpha);
@@ -91,4 +94,4 @@ __device__ __forceinline__ float shfl_xor_f(float x) {
     return __shfl_xor(x, MASK, 64);
 }
 
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+

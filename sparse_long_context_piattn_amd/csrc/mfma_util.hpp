@@ -1,0 +1,76 @@
+// mfma_util.hpp -- small gfx950 helpers shared by the tiled prefill kernels:
+// bf16 vector types, hardware bf16 packing, 4-lane reductions with
+// v_permlane16/32_swap, the transposing LDS read and the XOR swizzle of the
+// [rows][D] LDS tiles.
+#pragma once
+
+#include "common.hpp"
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
+
+
+constexpr int NW = 8;          // waves per workgroup
+constexpr int NT = NW * 64;    // threads per workgroup
+constexpr float LAZY = 8.0f;   // lazy-rescale threshold (log2 units)
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8_t, u); }
+
+__device__ __forceinline__ short bf16_short(float f) { return (short)f32_to_bf16_bits(f); }
+
+__device__ __forceinline__ float bf16_round(float f) {
+    return __uint_as_float(f32_to_bf16_bits(f) << 16);
+}
+
+// Sum / max over the four lanes {x, x+16, x+32, x+48} of a query.
+__device__ __forceinline__ float sum4(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ float max4(float v) {
+    auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float a0 = __uint_as_float(a[0]), a1 = __uint_as_float(a[1]);
+    v = a0 > a1 ? a0 : a1;
+    auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float b0 = __uint_as_float(b[0]), b1 = __uint_as_float(b[1]);
+    return b0 > b1 ? b0 : b1;
+}
+
+// bf16 dot product of 8 element pairs, accumulated in fp32.
+__device__ __forceinline__ float dot8(bf16x8_t a, bf16x8_t b, float c) {
+    const uint4 ua = __builtin_bit_cast(uint4, a), ub = __builtin_bit_cast(uint4, b);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ua.x), __builtin_bit_cast(bf16x2_t, ub.x), c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ua.y), __builtin_bit_cast(bf16x2_t, ub.y), c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ua.z), __builtin_bit_cast(bf16x2_t, ub.z), c, false);
+    c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, ua.w), __builtin_bit_cast(bf16x2_t, ub.w), c, false);
+    return c;
+}
+
+// Element xr of a 4-vector without branches (two selects).
+__device__ __forceinline__ float diag_pick(f32x4_t s4, int xr) {
+    const float a = (xr & 1) ? s4[1] : s4[0];
+    const float b = (xr & 1) ? s4[3] : s4[2];
+    return (xr & 2) ? b : a;
+}
+
+// Two fp32 values to packed bf16 (hardware round to nearest even).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, bf16x2_t));
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16) of the 8 bytes at p.
+__device__ __forceinline__ s16x4_t ld_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4_t*)p);
+}
+
+// Element offset of 16-byte chunk c of row r in a swizzled [rows][D] tile.
+template <int D>
+__device__ __forceinline__ int swz(int r, int c) {
+    return r * D + ((c ^ (r & 7)) << 3);
+}

@@ -3,6 +3,9 @@
 Layout conversion only (torch views to the oracle's packed [T, H, d] arrays);
 no attention arithmetic lives here.
 """
+import json
+import os
+
 import numpy as np
 import torch
 
@@ -11,6 +14,11 @@ from sparse_long_context_piattn_amd import workloads as wl
 
 BF16_TOL = 2e-2
 F32_TOL = 1e-5
+# Row log-normaliser: the bf16 MFMA path normalises with the bf16-rounded
+# softmax weights it multiplies V by, so its sum carries their unit roundoff
+# 2^-8 (relative), i.e. up to ~0.0039 in natural-log units.
+LSE_TOL_BF16 = 5e-3
+LSE_TOL_F32 = 1e-5
 
 
 def host_array(t: torch.Tensor):
@@ -54,9 +62,18 @@ def oracle_varlen_fwd(x, w, rows=None, want_lse=False):
                       w.k, w.pi, w.M, w.bidir, w.scale, rows=rows, want_lse=want_lse)
 
 
-def max_err(got: torch.Tensor, ref) -> float:
+def max_err(got: torch.Tensor, ref, tag: str | None = None) -> float:
     g = got.detach().float().cpu().double().numpy()
-    return float(np.abs(g - np.asarray(ref)).max()) if g.size else 0.0
+    err = float(np.abs(g - np.asarray(ref)).max()) if g.size else 0.0
+    log_path = os.environ.get("PIATTN_ERRLOG")
+    if log_path and tag:
+        with open(log_path, "a") as f:
+            f.write(json.dumps({"case": tag, "max_abs_err": err}) + "\n")
+    return err
+
+
+def lse_tol_for(w) -> float:
+    return LSE_TOL_F32 if w.dtype == "f32" else LSE_TOL_BF16
 
 
 def tol_for(w) -> float:
