@@ -235,7 +235,7 @@ def test_fwd_bidir_varlen_sampled_rows():
     rows = toks * w.H + heads
     ref = oracle_varlen_fwd(x, w, rows=rows)
     got = out.reshape(T * w.H, w.d).index_select(0, torch.from_numpy(rows).to(DEV))
-    assert max_err(got, ref) <= BF16_TOL
+    assert max_err(got, ref, "fwd bidir_varlen sampled") <= BF16_TOL
 
 
 @pytest.mark.parametrize("pi", [32, 64])
