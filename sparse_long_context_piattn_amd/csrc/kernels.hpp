@@ -13,6 +13,8 @@ hipError_t launch_fwd_gather(int dtype, const FwdArgs& a, hipStream_t stream);
 bool fwd_tiled_supported(int dtype, const FwdArgs& a);
 hipError_t launch_fwd_tiled(const FwdArgs& a, hipStream_t stream);
 // Two-phase variant of the tiled prefill for head dim 64.
+bool fwd_resid_supported(int dtype, const FwdArgs& a);
+hipError_t launch_fwd_resid(const FwdArgs& a, hipStream_t stream);
 bool fwd_phased_supported(int dtype, const FwdArgs& a);
 hipError_t launch_fwd_phased(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t stream);
