@@ -3,34 +3,42 @@
 //
 // Write a query row as i = a + t*pi (residue a = i mod pi, period t).  A
 // workgroup owns 64 residues [a0, a0+64) x T = 8 periods [t0, t0+8): 512
-// rows, 16 row groups of 16 rows (one period, 16 consecutive residues).  Each
-// of the 8 waves owns the 4 row groups of one 16-residue a-group and a period
-// parity, and keeps their online-softmax state (max m, per-lane partial sums
-// l, fp32 O^T) in registers.
+// rows, 32 row groups of 16 rows (one period, 16 consecutive residues).  Each
+// of the 8 waves owns the 4 row groups of one 16-residue a-group and one
+// period parity and keeps their online-softmax state (max m, per-lane partial
+// sums l, fp32 O^T) in registers.
 //
 // Phase 1, ring-local windows (pi-Attention "Ring-Local Attention"): step s
 // stages the windows of periods t0+2s and t0+2s+1 ([a0 + t pi - k,
-// a0 + t pi + 64 (+k)) each) and every wave runs its group's band on MFMA.
+// a0 + t pi + 64 (+k)) each) and every wave runs its row group's band:
+// S^T = K Q^T on v_mfma_f32_16x16x32_bf16, mask, log(alpha) prior, online
+// softmax, O^T += V^T P^T.
 //
 // Phase 2, periodic skips ("pi-Skip Attention").  The skip keys of row
-// (a, t) are (a, t - m) -- same residue, earlier (and, bidirectional, later)
-// periods -- so for one residue they form a band of width M over the
-// pi-strided sequence.  For each a-group (16 residues), LDS stages hold 16
-// key periods x 16 residues of K and V; an "item" is one residue with its T
-// query periods as the MFMA query columns, and S^T = K Q^T, the band mask,
-// the log(1-alpha) prior, an online softmax and O^T += V^T P^T run densely
-// on MFMA.  When an a-group's key periods are done, its items' partial states
-// (m, l, O^T) pass through a small LDS buffer into the row groups' registers,
-// merged exactly (m = max, O and l rescaled by 2^(m_part - m)).  One softmax
-// over window and skips results ("Dynamic Adaptive Fusion").
+// (a, t) are (a, t -/+ m) -- the same residue in other periods -- so for one
+// residue they form a band of width M over the pi-strided sequence.  For each
+// a-group (16 residues), an LDS stage holds 16 key periods x 16 residues of K
+// and V; an "item" is one residue with the tile's T query periods as MFMA
+// columns, and S^T = K Q^T, the band mask, the log(1-alpha) prior, an online
+// softmax and O^T += V^T P^T run densely on MFMA.  After an a-group's key
+// periods, its items' partial states (m, l, O^T) pass through a small LDS
+// buffer into the owners' registers and are merged exactly (m = max, l and O
+// rescaled by 2^(m_part - m)): one softmax over window and skips ("Dynamic
+// Adaptive Fusion").
 //
-// Staging: global_load_lds_dwordx4 into two alternating LDS stages (the
-// next stage's rows are in flight while the current one computes); rows are
+// Softmax bookkeeping is lazy: the running max of a column moves only when a
+// new score exceeds it by more than 2^8, so in steady state a block costs
+// mask + fma + exp per score and no rescale of the accumulators.
+//
+// Staging: global_load_lds_dwordx4 into two alternating LDS stages (the next
+// stage's rows are in flight while the current one computes); rows are
 // XOR-swizzled by 16-byte chunk with key (row ^ row/16) % 8 so that both
-// consecutive rows and rows 16 apart spread over the banks.  Rows outside
-// the sequence are filled from a clamped valid row and masked out.
+// consecutive rows and rows 16 apart spread over the banks.  Rows outside the
+// sequence are loaded from a clamped valid row and masked out.
 #include "kernels.hpp"
 #include "mfma_util.hpp"
+
+#include <type_traits>
 
 namespace {
 
@@ -39,12 +47,17 @@ constexpr int NA = 4, AT = 64, PW = 2, TW = 4, T = PW * TW;
 constexpr int CH = D / 8, DC = D / 32, DB = D / 16;
 constexpr int RMAX = 128;                     // staged rows of one window
 constexpr int SROWS = 256;                    // rows per stage (2 windows, or 16 periods x 16 residues)
-constexpr int STAGE = 2 * SROWS * D;          // elements per stage: K rows then V rows
+constexpr int STG = SROWS * D;                // elements of one stage array (32 KB)
 constexpr int DMA_PER_WAVE = 2 * SROWS * CH / (NW * 64);
+constexpr int UNIT = 32 * D;                  // one wave's skip unit: 16 K rows + 16 V rows
+static_assert(NW * UNIT == STG, "skip units of all waves fill one stage array");
 constexpr int IW = 2;                         // skip items (residues) per wave
-constexpr int REC = 4 + D / 2;                // merge record: m, l, 2 pad, half of O^T
+constexpr int REC = 4 + 16;                   // merge record: m, l, 2 pad, a quarter of O^T
 constexpr int RSTR = T * REC + 4;             // records of one residue (padded against bank conflicts)
+constexpr int QSLOT = T * D;                  // one item's query rows (T periods)
+constexpr int32_t EMPTY = 0x40000000;         // lower bound of an empty key range
 static_assert(2 * SROWS * CH % (NW * 64) == 0, "stage split");
+static_assert(SROWS * CH % (DMA_PER_WAVE * 64) == 0, "a wave stages only K or only V");
 static_assert(T <= 16, "query columns");
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -58,33 +71,109 @@ struct Ctx {
     int32_t skt, svt, n;
 };
 
-// One stage of LDS-direct loads.  Load i of wave w covers stage chunks
-// [64 (w*DMA_PER_WAVE + i), +64): rows r0 .. r0+7 (r0 a multiple of 8), lane l
+// One window stage of LDS-direct loads (K rows into Ks, V rows into Vs).
+// Load i of wave w covers chunks [64 ((w%4)*DMA_PER_WAVE + i), +64) of K
+// (waves 0-3) or V (waves 4-7): rows r0 .. r0+7 (r0 a multiple of 8), lane l
 // taking row r0 + l/8 and physical chunk l%8.  base(r0) is the sequence row
-// of stage row r0; rows r0..r0+7 are consecutive sequence rows.
+// of stage row r0; rows r0..r0+7 are consecutive sequence rows.  lc0 is
+// ((l%8) ^ (l/8)) * 8, loff the lane's row offset (l/8) * token stride.
 template <class Base>
-__device__ __forceinline__ void dma_stage(uint16_t* stage, const Ctx& c, Base base) {
+__device__ __forceinline__ void dma_window(uint16_t* Ks, uint16_t* Vs, const Ctx& c, int32_t lc0, uint32_t loff,
+                                           Base base) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
-    const int lhi = lane >> 3;
+    const bool isv = wave >= NW / 2;
+    const uint16_t* src0 = isv ? c.Vb : c.Kb;
+    uint16_t* dst = isv ? Vs : Ks;
+    const int32_t st = isv ? c.svt : c.skt;
 #pragma unroll
     for (int i = 0; i < DMA_PER_WAVE; ++i) {
-        const int c0 = (wave * DMA_PER_WAVE + i) * 64;
-        const bool isv = c0 >= SROWS * CH;
-        const int r0 = (isv ? c0 - SROWS * CH : c0) >> 3;
-        const int key = (lhi ^ (r0 >> 4)) & 7;          // swizzle key of row r0 + lhi
-        const int lc8 = ((lane & 7) ^ key) << 3;
-        int32_t srow = base(r0) + lhi;
-        srow = imin32(imax32(srow, 0), c.n - 1);
-        const uint16_t* src = isv ? c.Vb + (uint32_t)(srow * c.svt + lc8) : c.Kb + (uint32_t)(srow * c.skt + lc8);
-        __builtin_amdgcn_global_load_lds(src, (lds_void_t*)(stage + c0 * 8), 16, 0, 0);
+        const int c0 = ((wave % (NW / 2)) * DMA_PER_WAVE + i) * 64;
+        const int r0 = c0 >> 3;
+        const int32_t lc8 = lc0 ^ (((r0 >> 4) & 7) << 3);
+        const int32_t s0 = __builtin_amdgcn_readfirstlane(base(r0));
+        // uniform base + 32-bit lane offset (rows r0..r0+7 all inside the
+        // sequence: no per-lane clamp)
+        const bool inside = s0 >= 0 && s0 + 7 < c.n;
+        const uint16_t* ub = inside ? src0 + (int64_t)s0 * st : src0;
+        const uint32_t off = inside ? loff + (uint32_t)lc8
+                                    : (uint32_t)(imin32(imax32(s0 + (lane >> 3), 0), c.n - 1) * st + lc8);
+        const char* srcb = reinterpret_cast<const char*>(ub) + (uint32_t)(off * 2u);   // byte offset
+        __builtin_amdgcn_global_load_lds(srcb, (lds_void_t*)(dst + c0 * 8), 16, 0, 0);
     }
+}
+
+// Element offset of 16-byte chunk c of row r (0..15) of a skip unit; the key
+// (r/2) % 8 puts the 16 rows of a K-operand read on distinct banks.
+__device__ __forceinline__ int swu(int r, int c) { return r * D + ((c ^ ((r >> 1) & 7)) << 3); }
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// All LDS reads of one skip unit -- two 16-byte K-operand chunks and four
+// transposed V-operand reads -- issued together and completed inside the
+// block.  The unit's slice was filled by this wave's own LDS-direct loads,
+// which the caller has already waited for with vmcnt; keeping these reads
+// out of the compiler's view keeps it from adding its own (conservative,
+// pipeline-draining) vmcnt waits in front of them.
+__device__ __forceinline__ void unit_reads(uint32_t k0, uint32_t k1, uint32_t v0, uint32_t v1, uint32_t v2,
+                                           uint32_t v3, bf16x8_t& ka, bf16x8_t& kb, s16x4_t (&vv)[4]) {
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %7\n\t"
+        "ds_read_b64_tr_b16 %2, %8\n\t"
+        "ds_read_b64_tr_b16 %3, %9\n\t"
+        "ds_read_b64_tr_b16 %4, %10\n\t"
+        "ds_read_b64_tr_b16 %5, %11\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(ka), "=&v"(kb), "=&v"(vv[0]), "=&v"(vv[1]), "=&v"(vv[2]), "=&v"(vv[3])
+        : "v"(k0), "v"(k1), "v"(v0), "v"(v1), "v"(v2), "v"(v3)
+        : "memory");
+}
+
+// LDS reads of one item's query operand (two 16-byte chunks) and gate
+// logit, completed inside the block (same reasoning as unit_reads).
+__device__ __forceinline__ void item_reads(uint32_t q0, uint32_t q1, uint32_t ga, bf16x8_t& qa, bf16x8_t& qb,
+                                           float& gl) {
+    asm volatile(
+        "ds_read_b128 %0, %3\n\t"
+        "ds_read_b128 %1, %4\n\t"
+        "ds_read_b32 %2, %5\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(qa), "=&v"(qb), "=&v"(gl)
+        : "v"(q0), "v"(q1), "v"(ga)
+        : "memory");
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its loads in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Number of periods t >= 0 with res + t*pi < n, for a residue res in
+// [a0, a0 + pi) of a sequence in which residue a0 has P periods.
+__device__ __forceinline__ int32_t periods_of(int32_t res, int32_t P, int32_t pi, int32_t n) {
+    return P - (res + (P - 1) * pi >= n ? 1 : 0);
+}
+
+// Whether row (residue res, period t) has any skip key: a backward skip
+// needs t >= mlo, a forward one t + mlo < periods of res; none if M < mlo.
+template <bool BIDIR>
+__device__ __forceinline__ bool has_skip_rt(int32_t t, int32_t pr, int32_t mlo, int32_t M) {
+    return M >= mlo && (t >= mlo || (BIDIR && t + mlo < pr));
 }
 
 template <bool BIDIR>
 __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tiles, int32_t t_tiles,
                                                        int32_t total_tiles) {
-    __shared__ __attribute__((aligned(16))) uint16_t stA[STAGE];
-    __shared__ __attribute__((aligned(16))) uint16_t stB[STAGE];
+    // window stages: A = (st0 K, st1 V), B = (st2 K, st3 V); skip units
+    // rotate through st0..st3, each wave in its own UNIT-sized slice
+    __shared__ __attribute__((aligned(16))) uint16_t st0[STG];
+    __shared__ __attribute__((aligned(16))) uint16_t st1[STG];
+    __shared__ __attribute__((aligned(16))) uint16_t st2[STG];
+    __shared__ __attribute__((aligned(16))) uint16_t st3[STG];
+    __shared__ __attribute__((aligned(16))) uint16_t qst[NW * IW * QSLOT];   // items' query rows
+    __shared__ __attribute__((aligned(16))) float gst[NW * IW * 64];          // items' gate logits
     __shared__ __attribute__((aligned(16))) float mrec[16 * RSTR];
 
     // XCD-aware order: each XCD gets a contiguous run of logical tiles.
@@ -124,7 +213,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     const int32_t klo = imax32(0, t0 - M);
     const int32_t khi = imin32(P - 1, t0 + T - 1 + (BIDIR ? M : -mlo));
     const int32_t nkb = (M >= mlo && khi >= klo) ? (khi - klo + 16) >> 4 : 0;
-    const int32_t nss = NA * nkb;                  // skip steps: a-group major, key block minor
+    const int32_t NU = NA * nkb * IW;              // skip units per wave: a-group, key block, item
 
     const int64_t bq = a.cu ? 0 : (int64_t)b;
     const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + bq * a.sq.s + h * a.sq.h + tok0 * a.sq.t;
@@ -136,44 +225,48 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     cx.n = n;
     uint16_t* Ob = static_cast<uint16_t*>(a.o) + bq * a.so.s + h * a.so.h + tok0 * a.so.t;
     const int64_t gbase = bq * a.sg.s + h * a.sg.h + tok0 * a.sg.t;
+    const int32_t lc0 = ((lane & 7) ^ (lane >> 3)) << 3;
+    const uint32_t loff = (uint32_t)((lane >> 3) * (wave >= NW / 2 ? cx.svt : cx.skt));
+    // skip-unit loads: lane l takes row 8*half + l/8 (key period offset) and
+    // physical chunk l%8 of K (loads 0, 1) or V (loads 2, 3)
+    uint32_t uoff[2][2];
+    int32_t ulc[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        const int r = 8 * hf + (lane >> 3);
+        ulc[hf] = ((lane & 7) ^ ((r >> 1) & 7)) << 3;
+        uoff[0][hf] = (uint32_t)r * (uint32_t)pi * (uint32_t)cx.skt + (uint32_t)ulc[hf];
+        uoff[1][hf] = (uint32_t)r * (uint32_t)pi * (uint32_t)cx.svt + (uint32_t)ulc[hf];
+    }
 
     auto win_map = [=](int s) {
         return [=](int r) { return a0 + (t0 + PW * s + r / RMAX) * pi - kw + r % RMAX; };
     };
-    // skip step q: a-group q / nkb, key block q % nkb; stage row 16u + xx holds
-    // residue a0 + 16*ag + xx of key period klo + 16*kb + u
-    auto own_map = [=](int q) {
-        const int ag = q / nkb, kb = q % nkb;
-        return [=](int r) { return a0 + 16 * ag + (klo + 16 * kb + (r >> 4)) * pi + (r & 15); };
-    };
-
-    // ---- row groups of this wave: period t_j = t0 + wp + 2j
-    bf16x8_t qf[TW][DC];
-    f32x4_t acc[TW][DB];
-    float mrun[TW], lrun[TW], pl[TW];
-    int32_t ij[TW];
-    bool qv[TW];
+    // Skip unit (ag, kb, it) of this wave: residue a0 + 16*ag + 2*wave + it,
+    // key periods klo + 16*kb + [0, 16); row u of the unit's K and V is key
+    // period klo + 16*kb + u (rows past the sequence: clamped, masked).
+    // Rows past the last key period any of the tile's queries uses (or past
+    // the sequence) repeat the last needed row: the repeated lines are
+    // fetched once per load, and the rows are masked out.
+    auto dma_unit = [&](uint16_t* stj, int ag, int kb, int it) {
+        const int32_t res = a0 + 16 * ag + 2 * wave + it;
+        const int32_t row0 = res + (klo + 16 * kb) * pi;
+        const int32_t umax = imin32(khi, periods_of(res, P, pi, n) - 1) - (klo + 16 * kb);
+        const bool full = umax >= 15;
+        uint16_t* Kd = stj + wave * UNIT;
 #pragma unroll
-    for (int j = 0; j < TW; ++j) {
-        const int32_t tj = t0 + wp + PW * j;
-        ij[j] = a0 + 16 * ga + x + tj * pi;
-        qv[j] = tj < P && ij[j] < n;
-        const int32_t ic = qv[j] ? ij[j] : 0;
-#pragma unroll
-        for (int c = 0; c < DC; ++c) {
-            uint4 u = make_uint4(0, 0, 0, 0);
-            if (qv[j]) u = *reinterpret_cast<const uint4*>(Qb + (int64_t)ic * a.sq.t + 32 * c + 8 * g);
-            qf[j][c] = as_bf16x8(u);
+        for (int i = 0; i < 4; ++i) {
+            const int isv = i >> 1, hf = i & 1;
+            const uint16_t* src0 = isv ? cx.Vb : cx.Kb;
+            const int32_t stv = isv ? cx.svt : cx.skt;
+            const uint16_t* ub = full ? src0 + (int64_t)row0 * stv : src0;
+            const int32_t ue = imin32(8 * hf + (lane >> 3), imax32(umax, 0));
+            const uint32_t off =
+                full ? uoff[isv][hf] : (uint32_t)(imin32(row0 + ue * pi, n - 1) * stv + ulc[hf]);
+            const char* srcb = reinterpret_cast<const char*>(ub) + (uint32_t)(off * 2u);
+            __builtin_amdgcn_global_load_lds(srcb, (lds_void_t*)(Kd + isv * 16 * D + hf * 8 * D), 16, 0, 0);
         }
-        const RowSpan sp = row_span(ic, n, a.pat);
-        const float gl = qv[j] ? a.g[gbase + (int64_t)ic * a.sg.t] : 0.0f;
-        float psk;
-        gate_priors(gl, sp.has_skip(), &pl[j], &psk);
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) acc[j][bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        mrun[j] = -INFINITY;
-        lrun[j] = 0.0f;
-    }
+    };
 
     const float sl2 = a.scale_log2;
     const int tr_row = 4 * g + (x >> 2);
@@ -181,22 +274,52 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
     const s16x4_t ones4 = __builtin_bit_cast(s16x4_t, make_uint2(0x3f803f80u, 0x3f803f80u));
 
+    // ---- row groups of this wave: period t_j = t0 + wp + 2j
+    bf16x8_t qf[TW][DC];
+    f32x4_t acc[TW][DB];
+    float mrun[TW], lrun[TW], pl[TW];
+    int32_t ij[TW];
+    bool qv[TW];
+    {
+        const int32_t res = a0 + 16 * ga + x;
+        const int32_t pr = periods_of(res, P, pi, n);
+#pragma unroll
+        for (int j = 0; j < TW; ++j) {
+            const int32_t tj = t0 + wp + PW * j;
+            ij[j] = res + tj * pi;
+            qv[j] = tj < pr;
+            const int32_t ic = qv[j] ? ij[j] : 0;
+#pragma unroll
+            for (int c = 0; c < DC; ++c) {
+                uint4 u = make_uint4(0, 0, 0, 0);
+                if (qv[j]) u = *reinterpret_cast<const uint4*>(Qb + (int64_t)ic * a.sq.t + 32 * c + 8 * g);
+                qf[j][c] = as_bf16x8(u);
+            }
+            const float gl = qv[j] ? a.g[gbase + (int64_t)ic * a.sg.t] : 0.0f;
+            float psk;
+            gate_priors(gl, has_skip_rt<BIDIR>(tj, pr, mlo, M), &pl[j], &psk);
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb) acc[j][bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+            mrun[j] = -INFINITY;
+            lrun[j] = 0.0f;
+        }
+    }
+
     // ---------------------------------------------------------- window step
-    auto local = [&](int j, const uint16_t* st) {
+    auto local = [&](int j, const uint16_t* Ks, const uint16_t* Vs) {
         const int32_t tp = t0 + wp + PW * j;
         if (tp >= P) return;                          // wave-uniform
-        const uint16_t* Ks = st;
-        const uint16_t* Vs = st + SROWS * D;
         const int wrow0 = wp * RMAX + 16 * ga;
         const int32_t i = ij[j];
         const int32_t key0 = tp * pi + a0 - kw + 16 * ga;
-        const int32_t vlo = imax32(0, i - kw) - key0;
-        const int32_t vhi = (qv[j] ? imin32(n - 1, BIDIR ? i + kw : i) : -1) - key0;
-        const uint32_t vspan = (uint32_t)(vhi - vlo);
+        const int32_t vlo = qv[j] ? imax32(0, i - kw) - key0 : EMPTY;
+        const uint32_t vspan = qv[j] ? (uint32_t)(imin32(n - 1, BIDIR ? i + kw : i) - key0 - vlo) : 0u;
         const int32_t rel0 = 4 * g - vlo;
+        float mL = mrun[j] + LAZY, cst = pl[j] - (mrun[j] == -INFINITY ? 0.0f : mrun[j]);
         constexpr int KBC = 4;
         for (int32_t kb0 = 0; kb0 < NB; kb0 += KBC) {
             float sc[KBC][4];
+            float mx = -INFINITY;
 #pragma unroll
             for (int u = 0; u < KBC; ++u) {
 #pragma unroll
@@ -211,29 +334,28 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
                     }
                     const int32_t relb = rel0 + 16 * (kb0 + u);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        sc[u][r] = (uint32_t)(relb + r) <= vspan ? fmaf(s4[r], sl2, pl[j]) : -INFINITY;
+                    for (int r = 0; r < 4; ++r) sc[u][r] = (uint32_t)(relb + r) <= vspan ? s4[r] : -INFINITY;
+                    mx = fmax_ieee(mx, fmax_ieee(fmax_ieee(sc[u][0], sc[u][1]), fmax_ieee(sc[u][2], sc[u][3])));
                 }
             }
-            float mx = -INFINITY;
+            mx = fmaf(max4(mx), sl2, pl[j]);
+            if (__builtin_amdgcn_ballot_w64(mx > mL)) {
+                const float mnew = fmax_ieee(mrun[j], mx);
+                const float mu = mnew == -INFINITY ? 0.0f : mnew;
+                const float fac = exp2_fast(mrun[j] - mu);
 #pragma unroll
-            for (int u = 0; u < KBC; ++u)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) mx = mx > sc[u][r] ? mx : sc[u][r];
-            mx = max4(mx);
-            const float mnew = mrun[j] > mx ? mrun[j] : mx;
-            const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
-            const float fac = exp2_fast(mrun[j] - mu);
-#pragma unroll
-            for (int bb = 0; bb < DB; ++bb) acc[j][bb] *= fac;
-            lrun[j] *= fac;
-            mrun[j] = mnew;
+                for (int bb = 0; bb < DB; ++bb) acc[j][bb] *= fac;
+                lrun[j] *= fac;
+                mrun[j] = mnew;
+                mL = mnew + LAZY;
+                cst = pl[j] - mu;
+            }
             s16x4_t pb[KBC];
 #pragma unroll
             for (int u = 0; u < KBC; ++u) {
                 if (kb0 + u < NB) {
-                    const uint32_t w0 = cvt_pk_bf16(exp2_fast(sc[u][0] - mu), exp2_fast(sc[u][1] - mu));
-                    const uint32_t w1 = cvt_pk_bf16(exp2_fast(sc[u][2] - mu), exp2_fast(sc[u][3] - mu));
+                    const uint32_t w0 = cvt_pk_bf16(exp2_fast(fmaf(sc[u][0], sl2, cst)), exp2_fast(fmaf(sc[u][1], sl2, cst)));
+                    const uint32_t w1 = cvt_pk_bf16(exp2_fast(fmaf(sc[u][2], sl2, cst)), exp2_fast(fmaf(sc[u][3], sl2, cst)));
                     pb[u] = __builtin_bit_cast(s16x4_t, make_uint2(w0, w1));
                 } else {
                     pb[u] = s16x4_t{0, 0, 0, 0};
@@ -247,22 +369,26 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
                 if (kb0 + u + 1 < NB) {
                     const bf16x8_t pp = __builtin_bit_cast(
                         bf16x8_t, __builtin_shufflevector(pb[u], pb[u + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-                    lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pp, lsum, 0, 0, 0);
+                    bf16x8_t va[DB];
 #pragma unroll
                     for (int bb = 0; bb < DB; ++bb) {
                         const s16x4_t v0 = ld_tr16(Vs + sw(rb + tr_row, 2 * bb + (tr_col >> 3)) + (tr_col & 7));
                         const s16x4_t v1 = ld_tr16(Vs + sw(rb + 16 + tr_row, 2 * bb + (tr_col >> 3)) + (tr_col & 7));
-                        const bf16x8_t va =
-                            __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-                        acc[j][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pp, acc[j][bb], 0, 0, 0);
+                        va[bb] = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
                     }
+                    lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pp, lsum, 0, 0, 0);
+#pragma unroll
+                    for (int bb = 0; bb < DB; ++bb)
+                        acc[j][bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va[bb], pp, acc[j][bb], 0, 0, 0);
                 } else {
+                    s16x4_t va[DB];
+#pragma unroll
+                    for (int bb = 0; bb < DB; ++bb)
+                        va[bb] = ld_tr16(Vs + sw(rb + tr_row, 2 * bb + (tr_col >> 3)) + (tr_col & 7));
                     lsum = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, pb[u], lsum, 0, 0, 0);
 #pragma unroll
-                    for (int bb = 0; bb < DB; ++bb) {
-                        const s16x4_t v0 = ld_tr16(Vs + sw(rb + tr_row, 2 * bb + (tr_col >> 3)) + (tr_col & 7));
-                        acc[j][bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(v0, pb[u], acc[j][bb], 0, 0, 0);
-                    }
+                    for (int bb = 0; bb < DB; ++bb)
+                        acc[j][bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va[bb], pb[u], acc[j][bb], 0, 0, 0);
                 }
             }
             lrun[j] += 0.25f * lsum[0];   // quarter per lane; sum4 at the end restores the row sum
@@ -270,158 +396,209 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     };
 
     // ---------------------------------------------------------- skip items
-    // Item it of this wave: residue xr = a0 + 16*ag + 2*wave + it; query
-    // column col = lane % 16 is period t0 + col (valid for col < T).
+    // Item it of this wave: residue a0 + 16*ag + 2*wave + it; query column
+    // col = lane % 16 is period t0 + col (a query for col < T).
     bf16x8_t sq[IW][DC];
     f32x4_t sacc[IW][DB];
-    float sm[IW], sl[IW], sps[IW];
-    bool sqv[IW];
+    float sm[IW], sl[IW], sps[IW], smL[IW], scst[IW];
+    int32_t slo[IW], stq[IW];
+    uint32_t sspan[IW];
     const int col = x;
-    auto item_begin = [&](int ag) {
+    // LDS-direct loads of the items' query rows (lane l: period l/8, chunk
+    // l%8; one 16-byte load per lane covers the T = 8 rows of an item) and
+    // gate logits (lane l: period l%8) for a-group ag, into this wave's
+    // private slots: 4 loads.
+    auto item_dma = [&](int ag) {
 #pragma unroll
         for (int it = 0; it < IW; ++it) {
-            const int32_t tq = t0 + col;
-            const int32_t iq = a0 + 16 * ag + 2 * wave + it + tq * pi;
-            sqv[it] = col < T && tq < P && iq < n;
-            const int32_t ic = sqv[it] ? iq : 0;
+            const int32_t res = a0 + 16 * ag + 2 * wave + it;
+            const int slot = wave * IW + it;
+            const int p = lane >> 3;
+            const int32_t row = imin32(res + (t0 + p) * pi, n - 1);
+            const int lcq = ((lane & 7) ^ ((p >> 1) & 7)) << 3;
+            const uint16_t* qsrc = Qb + (int64_t)row * a.sq.t + lcq;
+            __builtin_amdgcn_global_load_lds(qsrc, (lds_void_t*)(qst + slot * QSLOT), 16, 0, 0);
+            const int32_t grow = imin32(res + (t0 + (lane & 7)) * pi, n - 1);
+            const float* gsrc = a.g + gbase + (int64_t)grow * a.sg.t;
+            __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)(gst + slot * 64), 4, 0, 0);
+        }
+    };
+    auto item_init = [&](int ag) {
 #pragma unroll
-            for (int c = 0; c < DC; ++c) {
-                uint4 u = make_uint4(0, 0, 0, 0);
-                if (sqv[it]) u = *reinterpret_cast<const uint4*>(Qb + (int64_t)ic * a.sq.t + 32 * c + 8 * g);
-                sq[it][c] = as_bf16x8(u);
-            }
-            const RowSpan sp = row_span(ic, n, a.pat);
-            const float gl = sqv[it] ? a.g[gbase + (int64_t)ic * a.sg.t] : 0.0f;
+        for (int it = 0; it < IW; ++it) {
+            const int32_t res = a0 + 16 * ag + 2 * wave + it;
+            const int32_t tq = t0 + col;
+            const int32_t pr = periods_of(res, P, pi, n);
+            const bool v = col < T && tq < pr;
+            const int slot = wave * IW + it;
+            const int xr = x & 7;                        // columns >= T read a valid row and are masked
+            const uint32_t qa = lds_addr(qst + slot * QSLOT) + 2u * (uint32_t)(xr * D);
+            float gl;
+            item_reads(qa + 16u * (uint32_t)((g ^ ((xr >> 1) & 7))), qa + 16u * (uint32_t)(((4 + g) ^ ((xr >> 1) & 7))),
+                       lds_addr(gst + slot * 64) + 4u * (uint32_t)xr, sq[it][0], sq[it][1], gl);
             float plk;
-            gate_priors(gl, sp.has_skip(), &plk, &sps[it]);
+            gate_priors(gl, has_skip_rt<BIDIR>(tq, pr, mlo, M), &plk, &sps[it]);
+            // key periods [lo, hi] (bidirectional: minus the hole |kp - tq| < mlo)
+            const int32_t lo = imax32(tq - M, 0);
+            const int32_t hi = BIDIR ? imin32(tq + M, pr - 1) : tq - mlo;
+            const bool ne = v && M >= mlo && hi >= lo;
+            slo[it] = ne ? lo : EMPTY;
+            sspan[it] = ne ? (uint32_t)(hi - lo) : 0u;
+            stq[it] = tq;
 #pragma unroll
             for (int bb = 0; bb < DB; ++bb) sacc[it][bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             sm[it] = -INFINITY;
+            smL[it] = -INFINITY;
             sl[it] = 0.0f;
+            scst[it] = sps[it];
         }
     };
-    auto item_block = [&](int ag, int kb, const uint16_t* st) {
-        const uint16_t* Ks = st;
-        const uint16_t* Vs = st + SROWS * D;
-        const int32_t tq = t0 + col;
+    auto item_unit = [&](int kb, const uint16_t* stj, auto itc) {
+        constexpr int it = decltype(itc)::value;
+        const uint32_t base = lds_addr(stj) + (uint32_t)(wave * UNIT * 2);
+        bf16x8_t kk[DC];
+        s16x4_t vv[DB];
+        static_assert(DC == 2 && DB == 4, "unit_reads shape");
+        unit_reads(base + 2 * swu(x, g), base + 2 * swu(x, 4 + g),
+                   base + 2 * (16 * D + swu(tr_row, 0 + (tr_col >> 3)) + (tr_col & 7)),
+                   base + 2 * (16 * D + swu(tr_row, 2 + (tr_col >> 3)) + (tr_col & 7)),
+                   base + 2 * (16 * D + swu(tr_row, 4 + (tr_col >> 3)) + (tr_col & 7)),
+                   base + 2 * (16 * D + swu(tr_row, 6 + (tr_col >> 3)) + (tr_col & 7)), kk[0], kk[1], vv);
         const int32_t kp0 = klo + 16 * kb + 4 * g;      // key period of this lane's value r = 0
+        f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int it = 0; it < IW; ++it) {
-            const int xx = 2 * wave + it;                // residue within the a-group
-            f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
+        for (int c = 0; c < DC; ++c) s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk[c], sq[it][c], s4, 0, 0, 0);
+        const int32_t e0 = kp0 - slo[it];
+        const int32_t h0 = kp0 - stq[it] + mlo - 1;
+        float sc[4];
 #pragma unroll
-            for (int c = 0; c < DC; ++c) {
-                const bf16x8_t kk = *reinterpret_cast<const bf16x8_t*>(Ks + sw(16 * x + xx, 4 * c + g));
-                s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, sq[it][c], s4, 0, 0, 0);
-            }
-            float sc[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int32_t kp = kp0 + r;
-                const int32_t delta = tq - kp;
-                const int32_t m = delta > 0 ? delta : -delta;
-                const bool band = m >= mlo && m <= M && (delta > 0 || (BIDIR && delta < 0));
-                const bool ok = band && sqv[it] && kp <= khi && a0 + 16 * ag + xx + kp * pi < n;
-                sc[r] = ok ? fmaf(s4[r], sl2, sps[it]) : -INFINITY;
-            }
-            float mx = sc[0] > sc[1] ? sc[0] : sc[1];
-            const float mx2 = sc[2] > sc[3] ? sc[2] : sc[3];
-            mx = max4(mx > mx2 ? mx : mx2);
-            const float mnew = sm[it] > mx ? sm[it] : mx;
-            const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
+        for (int r = 0; r < 4; ++r) {
+            bool ok = (uint32_t)(e0 + r) <= sspan[it];
+            if (BIDIR) ok = ok && (uint32_t)(h0 + r) > (uint32_t)(2 * mlo - 2);
+            sc[r] = ok ? s4[r] : -INFINITY;
+        }
+        const float mx = fmaf(max4(fmax_ieee(fmax_ieee(sc[0], sc[1]), fmax_ieee(sc[2], sc[3]))), sl2, sps[it]);
+        if (__builtin_amdgcn_ballot_w64(mx > smL[it])) {
+            const float mnew = fmax_ieee(sm[it], mx);
+            const float mu = mnew == -INFINITY ? 0.0f : mnew;
             const float fac = exp2_fast(sm[it] - mu);
 #pragma unroll
             for (int bb = 0; bb < DB; ++bb) sacc[it][bb] *= fac;
             sl[it] *= fac;
             sm[it] = mnew;
-            const uint32_t w0 = cvt_pk_bf16(exp2_fast(sc[0] - mu), exp2_fast(sc[1] - mu));
-            const uint32_t w1 = cvt_pk_bf16(exp2_fast(sc[2] - mu), exp2_fast(sc[3] - mu));
-            const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(w0, w1));
-            const f32x4_t ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, pb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            sl[it] += ls[0];                         // full column sum in every lane
-#pragma unroll
-            for (int bb = 0; bb < DB; ++bb) {
-                const s16x4_t vv = ld_tr16(Vs + sw(16 * tr_row + xx, 2 * bb + (tr_col >> 3)) + (tr_col & 7));
-                sacc[it][bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv, pb, sacc[it][bb], 0, 0, 0);
-            }
+            smL[it] = mnew + LAZY;
+            scst[it] = sps[it] - mu;
         }
+        const uint32_t w0 = cvt_pk_bf16(exp2_fast(fmaf(sc[0], sl2, scst[it])), exp2_fast(fmaf(sc[1], sl2, scst[it])));
+        const uint32_t w1 = cvt_pk_bf16(exp2_fast(fmaf(sc[2], sl2, scst[it])), exp2_fast(fmaf(sc[3], sl2, scst[it])));
+        const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(w0, w1));
+        const f32x4_t ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, pb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        sl[it] += ls[0];                         // full column sum in every lane
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb)
+            sacc[it][bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv[bb], pb, sacc[it][bb], 0, 0, 0);
     };
     // Fold the items' partial states for a-group ag into the row groups'
-    // registers, half of the head dimension per pass.
+    // registers, a quarter of the head dimension (16 values) per pass.
     auto item_merge = [&](int ag) {
         float fl[TW], fs[TW];
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-            __syncthreads();                          // buffer free (previous pass read)
+        for (int bb = 0; bb < DB; ++bb) {
+            lds_barrier();                            // buffer free (previous pass read)
 #pragma unroll
             for (int it = 0; it < IW; ++it) {
                 if (col < T) {
                     float* rp = mrec + (2 * wave + it) * RSTR + col * REC;
-                    if (g == 0 && hh == 0) {
+                    if (g == 0 && bb == 0) {
                         rp[0] = sm[it];
                         rp[1] = sl[it];
                     }
-#pragma unroll
-                    for (int q = 0; q < DB / 2; ++q) {
-                        const int bb = hh * (DB / 2) + q;
-                        *reinterpret_cast<f32x4_t*>(rp + 4 + 16 * q + 4 * g) = sacc[it][bb];
-                    }
+                    *reinterpret_cast<f32x4_t*>(rp + 4 + 4 * g) = sacc[it][bb];
                 }
             }
-            __syncthreads();
+            lds_barrier();
             if (ga == ag) {
 #pragma unroll
                 for (int j = 0; j < TW; ++j) {
                     const int cj = wp + PW * j;             // column of row group j
                     const float* rp = mrec + x * RSTR + cj * REC;
-                    if (hh == 0) {
+                    if (bb == 0) {
                         const float msk = rp[0], lsk = rp[1];
-                        const float mnew = mrun[j] > msk ? mrun[j] : msk;
-                        const float mu = (mnew == -INFINITY) ? 0.0f : mnew;
+                        const float mnew = fmax_ieee(mrun[j], msk);
+                        const float mu = mnew == -INFINITY ? 0.0f : mnew;
                         fl[j] = exp2_fast(mrun[j] - mu);
                         fs[j] = exp2_fast(msk - mu);
                         lrun[j] = lrun[j] * fl[j] + 0.25f * lsk * fs[j];
                         mrun[j] = mnew;
                     }
-#pragma unroll
-                    for (int q = 0; q < DB / 2; ++q) {
-                        const int bb = hh * (DB / 2) + q;
-                        const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(rp + 4 + 16 * q + 4 * g);
-                        acc[j][bb] = acc[j][bb] * fl[j] + sv * fs[j];
-                    }
+                    const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(rp + 4 + 4 * g);
+                    acc[j][bb] = acc[j][bb] * fl[j] + sv * fs[j];
                 }
             }
         }
     };
-    auto sstep = [&](int q, const uint16_t* st) {
-        const int ag = q / nkb, kb = q % nkb;
-        if (kb == 0) item_begin(ag);
-        item_block(ag, kb, st);
-        if (kb == nkb - 1) item_merge(ag);         // workgroup-uniform
+    // Process unit u (a-group ag, key block kb, item IT) from stage array
+    // stj after issuing unit u+3 into nxt; each wave waits only for its own
+    // loads (its slice is private), so units need no workgroup barrier.
+    // Every unit issues exactly 4 loads (past the last unit: a harmless
+    // reload of the last one), so the loads of unit u are always followed by
+    // those of units u+1..u+3 and vmcnt(12) waits for exactly unit u.
+    auto issue = [&](uint16_t* stj, int v) {
+        const int q = imin32(v, NU - 1) >> 1;          // IW == 2 units per (a-group, key block)
+        dma_unit(stj, q / nkb, q % nkb, imin32(v, NU - 1) & 1);
+    };
+    auto unit = [&](int u, const uint16_t* stj, uint16_t* nxt, auto itc) {
+        constexpr int it = decltype(itc)::value;
+        issue(nxt, u + 3);
+        __builtin_amdgcn_s_waitcnt(0xF7C);             // vmcnt(12): unit u has landed
+        const int q = u >> 1, ag = q / nkb, kb = q % nkb;
+        if (it == 0 && kb == 0) {
+            // The query/gate loads of a-group ag were issued while processing
+            // the first unit of a-group ag-1 (after that step's unit issue),
+            // so 8*nkb unit loads follow them by now: vmcnt(12) covers them
+            // once nkb >= 2.
+            if (nkb == 1) __builtin_amdgcn_s_waitcnt(0xF78);   // vmcnt(8)
+            item_init(ag);
+            if (ag + 1 < NA) item_dma(ag + 1);         // the slots were just read
+        }
+        item_unit(kb, stj, itc);
+        if (it == IW - 1 && kb == nkb - 1) item_merge(ag);   // workgroup-uniform
     };
 
     // ---------------------------------------------------------- schedule
-    dma_stage(stA, cx, win_map(0));
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    static_assert(IW == 2, "unit loop unrolled for two items");
+    dma_window(st0, st1, cx, lc0, loff, win_map(0));
     __syncthreads();
-    dma_stage(stB, cx, win_map(1));
-    local(0, stA);
+    dma_window(st2, st3, cx, lc0, loff, win_map(1));
+    local(0, st0, st1);
     __syncthreads();
-    dma_stage(stA, cx, win_map(2));
-    local(1, stB);
+    dma_window(st0, st1, cx, lc0, loff, win_map(2));
+    local(1, st2, st3);
     __syncthreads();
-    dma_stage(stB, cx, win_map(3));
-    local(2, stA);
+    dma_window(st2, st3, cx, lc0, loff, win_map(3));
+    local(2, st0, st1);
     __syncthreads();
-    if (nss > 0) dma_stage(stA, cx, own_map(0));
-    local(3, stB);
-    for (int q = 0; q < nss; q += 2) {
-        __syncthreads();
-        if (q + 1 < nss) dma_stage(stB, cx, own_map(q + 1));
-        sstep(q, stA);
-        if (q + 1 >= nss) break;
-        __syncthreads();
-        if (q + 2 < nss) dma_stage(stA, cx, own_map(q + 2));
-        sstep(q + 1, stB);
+    if (NU > 0) {
+        item_dma(0);
+        issue(st0, 0);
+        issue(st1, 1);
+    }
+    local(3, st2, st3);
+    if (NU > 0) {
+        lds_barrier();                                  // every wave is done with st2, st3
+        issue(st2, 2);
+        for (int u = 0; u < NU; u += 4) {
+            unit(u, st0, st3, I0{});
+            unit(u + 1, st1, st0, I1{});
+            if (u + 2 >= NU) break;
+            unit(u + 2, st2, st1, I0{});
+            unit(u + 3, st3, st2, I1{});
+        }
+        // the reloads issued past the last unit must land before the
+        // workgroup (and its LDS) can retire
+        __builtin_amdgcn_s_waitcnt(0xF70);             // vmcnt(0)
     }
 
     // ---- normalise and store (bf16, round to nearest even)
@@ -460,6 +637,8 @@ bool fwd_resid_supported(int dtype, const FwdArgs& a) {
     if (dtype != 1 || a.d != 64 || a.pat.pi % AT != 0) return false;
     const int64_t ts = a.sk.t > a.sv.t ? a.sk.t : a.sv.t;
     if ((int64_t)a.n * ts + D >= ((int64_t)1 << 31)) return false;
+    // row indices such as a0 + (t0 + T + 15) * pi stay in int32
+    if ((int64_t)a.n + (int64_t)(2 * T + 16) * a.pat.pi >= ((int64_t)1 << 31)) return false;
     const int64_t w = (int64_t)a.pat.k + 16 + (a.pat.bidir ? a.pat.k : 0);
     return 16 * (NA - 1) + 16 * ((w + 15) / 16) <= RMAX;
 }

@@ -32,13 +32,15 @@ __device__ __forceinline__ float sum4(float v) {
     auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
+// Maximum that propagates NaN (v_maximum3_f32 on gfx950: no input
+// canonicalisation, unlike fmaxf).
+__device__ __forceinline__ float fmax_ieee(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+
 __device__ __forceinline__ float max4(float v) {
     auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    const float a0 = __uint_as_float(a[0]), a1 = __uint_as_float(a[1]);
-    v = a0 > a1 ? a0 : a1;
+    v = fmax_ieee(__uint_as_float(a[0]), __uint_as_float(a[1]));
     auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    const float b0 = __uint_as_float(b[0]), b1 = __uint_as_float(b[1]);
-    return b0 > b1 ? b0 : b1;
+    return fmax_ieee(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
 // bf16 dot product of 8 element pairs, accumulated in fp32.
