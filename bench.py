@@ -28,8 +28,8 @@ METRIC = "π-attn fwd queries/s + achieved HBM GB/s & MFMA %, n=8192 d=64 bf16, 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16
 MALL_BYTES = 256 << 20
-KERNEL_SOURCES = ["pattern.hpp", "common.hpp", "gather.hpp", "fwd_gather.hip", "fwd_tiled.hip",
-                  "decode.hip", "api.cpp"]
+KERNEL_SOURCES = ["pattern.hpp", "common.hpp", "gather.hpp", "mfma_util.hpp", "fwd_gather.hip",
+                  "fwd_tiled.hip", "fwd_resid.hip", "decode.hip", "api.cpp"]
 
 
 def log(*a):

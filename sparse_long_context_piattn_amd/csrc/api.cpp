@@ -179,7 +179,6 @@ int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int dt = dtype == PIATTN_BF16 ? 1 : 0;
     if (fwd_resid_supported(dt, a)) return launch_status(launch_fwd_resid(a, st));
-    if (fwd_phased_supported(dt, a)) return launch_status(launch_fwd_phased(a, st));
     if (fwd_tiled_supported(dt, a)) return launch_status(launch_fwd_tiled(a, st));
     return launch_status(launch_fwd_gather(dt, a, st));
 }

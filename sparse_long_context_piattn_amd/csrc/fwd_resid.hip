@@ -52,8 +52,6 @@ constexpr int DMA_PER_WAVE = 2 * SROWS * CH / (NW * 64);
 constexpr int UNIT = 32 * D;                  // one wave's skip unit: 16 K rows + 16 V rows
 static_assert(NW * UNIT == STG, "skip units of all waves fill one stage array");
 constexpr int IW = 2;                         // skip items (residues) per wave
-constexpr int REC = 4 + 16;                   // merge record: m, l, 2 pad, a quarter of O^T
-constexpr int RSTR = T * REC + 4;             // records of one residue (padded against bank conflicts)
 constexpr int QSLOT = T * D;                  // one item's query rows (T periods)
 constexpr int32_t EMPTY = 0x40000000;         // lower bound of an empty key range
 static_assert(2 * SROWS * CH % (NW * 64) == 0, "stage split");
@@ -146,6 +144,39 @@ __device__ __forceinline__ void item_reads(uint32_t q0, uint32_t q1, uint32_t ga
         : "memory");
 }
 
+// Merge-record LDS traffic, also kept out of the compiler's view (the
+// stage arrays it uses receive LDS-direct loads at other times).  Record
+// layout: 4 f32x4 (one per 16-row block of O^T) 512 bytes apart.
+__device__ __forceinline__ void lds_write_o(uint32_t a, f32x4_t v0, f32x4_t v1, f32x4_t v2, f32x4_t v3) {
+    asm volatile(
+        "ds_write_b128 %0, %1\n\t"
+        "ds_write_b128 %0, %2 offset:512\n\t"
+        "ds_write_b128 %0, %3 offset:1024\n\t"
+        "ds_write_b128 %0, %4 offset:1536"
+        :
+        : "v"(a), "v"(v0), "v"(v1), "v"(v2), "v"(v3)
+        : "memory");
+}
+__device__ __forceinline__ void lds_write_ml(uint32_t a, float m, float l) {
+    asm volatile("ds_write2_b32 %0, %1, %2 offset1:1" : : "v"(a), "v"(m), "v"(l) : "memory");
+}
+__device__ __forceinline__ void lds_read_oml(uint32_t a, uint32_t aml, f32x4_t (&v)[4], float& m, float& l) {
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    f32x2_t ml;
+    asm volatile(
+        "ds_read_b128 %0, %5\n\t"
+        "ds_read_b128 %1, %5 offset:512\n\t"
+        "ds_read_b128 %2, %5 offset:1024\n\t"
+        "ds_read_b128 %3, %5 offset:1536\n\t"
+        "ds_read2_b32 %4, %6 offset1:1\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(ml)
+        : "v"(a), "v"(aml)
+        : "memory");
+    m = ml.x;
+    l = ml.y;
+}
+
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
 // operations, not for its loads in flight.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -174,7 +205,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     __shared__ __attribute__((aligned(16))) uint16_t st3[STG];
     __shared__ __attribute__((aligned(16))) uint16_t qst[NW * IW * QSLOT];   // items' query rows
     __shared__ __attribute__((aligned(16))) float gst[NW * IW * 64];          // items' gate logits
-    __shared__ __attribute__((aligned(16))) float mrec[16 * RSTR];
+    __shared__ __attribute__((aligned(16))) float mrec[16 * T * 2];             // items' (m, l)
 
     // XCD-aware order: each XCD gets a contiguous run of logical tiles.
     const int32_t hw = blockIdx.x;
@@ -295,9 +326,9 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
                 if (qv[j]) u = *reinterpret_cast<const uint4*>(Qb + (int64_t)ic * a.sq.t + 32 * c + 8 * g);
                 qf[j][c] = as_bf16x8(u);
             }
-            const float gl = qv[j] ? a.g[gbase + (int64_t)ic * a.sg.t] : 0.0f;
-            float psk;
-            gate_priors(gl, has_skip_rt<BIDIR>(tj, pr, mlo, M), &pl[j], &psk);
+            // gate logit; its prior is formed at the row group's first window
+            // step, so these loads are all in flight together
+            pl[j] = qv[j] ? a.g[gbase + (int64_t)ic * a.sg.t] : 0.0f;
 #pragma unroll
             for (int bb = 0; bb < DB; ++bb) acc[j][bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             mrun[j] = -INFINITY;
@@ -309,6 +340,10 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     auto local = [&](int j, const uint16_t* Ks, const uint16_t* Vs) {
         const int32_t tp = t0 + wp + PW * j;
         if (tp >= P) return;                          // wave-uniform
+        {
+            float psk;
+            gate_priors(pl[j], has_skip_rt<BIDIR>(tp, periods_of(a0 + 16 * ga + x, P, pi, n), mlo, M), &pl[j], &psk);
+        }
         const int wrow0 = wp * RMAX + 16 * ga;
         const int32_t i = ij[j];
         const int32_t key0 = tp * pi + a0 - kw + 16 * ga;
@@ -408,18 +443,29 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     // l%8; one 16-byte load per lane covers the T = 8 rows of an item) and
     // gate logits (lane l: period l%8) for a-group ag, into this wave's
     // private slots: 4 loads.
+    // lane constants: query row p = l/8 of the item, its swizzled chunk, and
+    // gate period l%8 (32-bit offsets from a uniform row base)
+    const int32_t lcq = ((lane & 7) ^ (((lane >> 3) >> 1) & 7)) << 3;
+    const uint32_t qoff = (uint32_t)(lane >> 3) * (uint32_t)pi * (uint32_t)a.sq.t + (uint32_t)lcq;
+    const uint32_t goff = (uint32_t)(lane & 7) * (uint32_t)pi * (uint32_t)a.sg.t;
     auto item_dma = [&](int ag) {
 #pragma unroll
         for (int it = 0; it < IW; ++it) {
-            const int32_t res = a0 + 16 * ag + 2 * wave + it;
+            const int32_t rb = a0 + 16 * ag + 2 * wave + it + t0 * pi;   // row of period t0
             const int slot = wave * IW + it;
-            const int p = lane >> 3;
-            const int32_t row = imin32(res + (t0 + p) * pi, n - 1);
-            const int lcq = ((lane & 7) ^ ((p >> 1) & 7)) << 3;
-            const uint16_t* qsrc = Qb + (int64_t)row * a.sq.t + lcq;
+            const bool inside = rb + (T - 1) * pi < n;
+            const uint16_t* qsrc;
+            const float* gsrc;
+            if (inside) {
+                qsrc = Qb + (int64_t)rb * a.sq.t + qoff;
+                gsrc = a.g + gbase + (int64_t)rb * a.sg.t + goff;
+            } else {
+                const int32_t row = imin32(rb + (lane >> 3) * pi, n - 1);
+                const int32_t grow = imin32(rb + (lane & 7) * pi, n - 1);
+                qsrc = Qb + (int64_t)row * a.sq.t + lcq;
+                gsrc = a.g + gbase + (int64_t)grow * a.sg.t;
+            }
             __builtin_amdgcn_global_load_lds(qsrc, (lds_void_t*)(qst + slot * QSLOT), 16, 0, 0);
-            const int32_t grow = imin32(res + (t0 + (lane & 7)) * pi, n - 1);
-            const float* gsrc = a.g + gbase + (int64_t)grow * a.sg.t;
             __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)(gst + slot * 64), 4, 0, 0);
         }
     };
@@ -499,43 +545,46 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
             sacc[it][bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv[bb], pb, sacc[it][bb], 0, 0, 0);
     };
     // Fold the items' partial states for a-group ag into the row groups'
-    // registers, a quarter of the head dimension (16 values) per pass.
-    auto item_merge = [&](int ag) {
-        float fl[TW], fs[TW];
+    // registers, in one exchange.  Each wave writes its two items' O^T
+    // (2 x 8 columns x 64 floats = its 4 KB slice) into its own slice of the
+    // stage array stj whose unit it has just consumed -- private, so no
+    // barrier before -- and m, l into mrec; after a barrier the owners of the
+    // a-group read all slices; a second barrier frees stj for the next loads.
+    // Slice layout [it][bb][g][col ^ (xx % 8)][4]: writes of a wave are
+    // contiguous and the owners' 16 residues spread over the banks.
+    auto item_merge = [&](int ag, uint16_t* stj) {
+        const uint32_t sbase = lds_addr(stj);
 #pragma unroll
-        for (int bb = 0; bb < DB; ++bb) {
-            lds_barrier();                            // buffer free (previous pass read)
-#pragma unroll
-            for (int it = 0; it < IW; ++it) {
-                if (col < T) {
-                    float* rp = mrec + (2 * wave + it) * RSTR + col * REC;
-                    if (g == 0 && bb == 0) {
-                        rp[0] = sm[it];
-                        rp[1] = sl[it];
-                    }
-                    *reinterpret_cast<f32x4_t*>(rp + 4 + 4 * g) = sacc[it][bb];
-                }
-            }
-            lds_barrier();
-            if (ga == ag) {
-#pragma unroll
-                for (int j = 0; j < TW; ++j) {
-                    const int cj = wp + PW * j;             // column of row group j
-                    const float* rp = mrec + x * RSTR + cj * REC;
-                    if (bb == 0) {
-                        const float msk = rp[0], lsk = rp[1];
-                        const float mnew = fmax_ieee(mrun[j], msk);
-                        const float mu = mnew == -INFINITY ? 0.0f : mnew;
-                        fl[j] = exp2_fast(mrun[j] - mu);
-                        fs[j] = exp2_fast(msk - mu);
-                        lrun[j] = lrun[j] * fl[j] + 0.25f * lsk * fs[j];
-                        mrun[j] = mnew;
-                    }
-                    const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(rp + 4 + 4 * g);
-                    acc[j][bb] = acc[j][bb] * fl[j] + sv * fs[j];
-                }
+        for (int it = 0; it < IW; ++it) {
+            const int xx = 2 * wave + it;
+            if (col < T) {
+                const uint32_t rec = sbase + (uint32_t)(wave * UNIT * 2) +
+                                     4u * (uint32_t)(((it * DB) * 4 + g) * 32 + ((col ^ (xx & 7)) << 2));
+                lds_write_o(rec, sacc[it][0], sacc[it][1], sacc[it][2], sacc[it][3]);
+                if (g == 0) lds_write_ml(lds_addr(mrec) + 8u * (uint32_t)(xx * T + col), sm[it], sl[it]);
             }
         }
+        lds_barrier();
+        if (ga == ag) {
+#pragma unroll
+            for (int j = 0; j < TW; ++j) {
+                const int cj = wp + PW * j;                 // column of row group j
+                const uint32_t rec = sbase + (uint32_t)((x >> 1) * UNIT * 2) +
+                                     4u * (uint32_t)((((x & 1) * DB) * 4 + g) * 32 + ((cj ^ (x & 7)) << 2));
+                f32x4_t sv[DB];
+                float msk, lsk;
+                lds_read_oml(rec, lds_addr(mrec) + 8u * (uint32_t)(x * T + cj), sv, msk, lsk);
+                const float mnew = fmax_ieee(mrun[j], msk);
+                const float mu = mnew == -INFINITY ? 0.0f : mnew;
+                const float fl = exp2_fast(mrun[j] - mu);
+                const float fs = exp2_fast(msk - mu);
+                lrun[j] = lrun[j] * fl + 0.25f * lsk * fs;
+                mrun[j] = mnew;
+#pragma unroll
+                for (int bb = 0; bb < DB; ++bb) acc[j][bb] = acc[j][bb] * fl + sv[bb] * fs;
+            }
+        }
+        lds_barrier();
     };
     // Process unit u (a-group ag, key block kb, item IT) from stage array
     // stj after issuing unit u+3 into nxt; each wave waits only for its own
@@ -562,7 +611,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
             if (ag + 1 < NA) item_dma(ag + 1);         // the slots were just read
         }
         item_unit(kb, stj, itc);
-        if (it == IW - 1 && kb == nkb - 1) item_merge(ag);   // workgroup-uniform
+        if (it == IW - 1 && kb == nkb - 1) item_merge(ag, const_cast<uint16_t*>(stj));   // workgroup-uniform
     };
 
     // ---------------------------------------------------------- schedule
@@ -635,8 +684,10 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
 
 bool fwd_resid_supported(int dtype, const FwdArgs& a) {
     if (dtype != 1 || a.d != 64 || a.pat.pi % AT != 0) return false;
-    const int64_t ts = a.sk.t > a.sv.t ? a.sk.t : a.sv.t;
-    if ((int64_t)a.n * ts + D >= ((int64_t)1 << 31)) return false;
+    int64_t ts = a.sk.t > a.sv.t ? a.sk.t : a.sv.t;
+    ts = ts > a.sq.t ? ts : a.sq.t;
+    if ((int64_t)a.n * ts + D >= ((int64_t)1 << 31)) return false;   // 32-bit row offsets
+    if ((int64_t)a.n * a.sg.t >= ((int64_t)1 << 31)) return false;
     // row indices such as a0 + (t0 + T + 15) * pi stay in int32
     if ((int64_t)a.n + (int64_t)(2 * T + 16) * a.pat.pi >= ((int64_t)1 << 31)) return false;
     const int64_t w = (int64_t)a.pat.k + 16 + (a.pat.bidir ? a.pat.k : 0);

@@ -12,11 +12,10 @@ hipError_t launch_fwd_gather(int dtype, const FwdArgs& a, hipStream_t stream);
 // small enough for the LDS stage); launch_fwd_gather serves everything else.
 bool fwd_tiled_supported(int dtype, const FwdArgs& a);
 hipError_t launch_fwd_tiled(const FwdArgs& a, hipStream_t stream);
-// Two-phase variant of the tiled prefill for head dim 64.
+// Residue-layout prefill for head dim 64 (window phase + dense skip band);
+// tried before fwd_tiled.
 bool fwd_resid_supported(int dtype, const FwdArgs& a);
 hipError_t launch_fwd_resid(const FwdArgs& a, hipStream_t stream);
-bool fwd_phased_supported(int dtype, const FwdArgs& a);
-hipError_t launch_fwd_phased(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_neighbors(int32_t n, const PiPattern& p, int32_t q_begin, int32_t q_count,
                             int32_t cap, int32_t* idx, int8_t* kind, int32_t* count,
