@@ -167,6 +167,8 @@ def bench_decode(args, w, dev):
                   period_pi=w.pi, num_skips=w.M, num_splits=splits, workspace=ws, out=out)
 
     ms_per_step = timed(step, args, dev)
+    if args.calibrate_copy:
+        calibrate_copy(dev)
     sec = ms_per_step / 1e3
     gbps = alg_bytes / sec / 1e9
     log("%.4f ms/call  %.3e row-queries/s  %.0f GB/s (%.1f%% of HBM peak)"
@@ -184,6 +186,72 @@ def bench_decode(args, w, dev):
                         "traffic": traffic_record(w.name)},
            "cpu_baseline": None}
     print(json.dumps(res), flush=True)
+
+
+COPY_ELEMS = 256 << 20          # bf16 elements of the calibration copy (512 MiB each way)
+
+
+def calibrate_copy(dev):
+    """A plain streaming copy of known size: reads and writes 512 MiB."""
+    import torch
+    src = torch.empty(COPY_ELEMS, dtype=torch.bfloat16, device=dev).normal_()
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 1.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
+def _counter_rows(d):
+    """(kernel name, counter, value, dispatch id) from a rocprofv3 csv run."""
+    import csv
+    import glob
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no *counter_collection.csv under %s" % d)
+    rows = []
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            rows.append((r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"]),
+                         r["Dispatch_Id"]))
+    return rows
+
+
+def _per_dispatch(rows, counter, match):
+    """Median over dispatches of a kernel of the summed counter value."""
+    import statistics
+    per = {}
+    for name, cn, val, disp in rows:
+        if cn == counter and match(name):
+            per[disp] = per.get(disp, 0.0) + val
+    if not per:
+        raise SystemExit("no %s dispatch matched" % counter)
+    return statistics.median(per.values()), len(per)
+
+
+def pmc_summary(args):
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the forward kernel, each
+    scaled by the reading of the same counter on the plain copy, into the
+    HBM bytes per launch that bench.py reports as roofline.traffic."""
+    fetch_rows, write_rows = _counter_rows(args.pmc_summary[0]), _counter_rows(args.pmc_summary[1])
+    is_fwd = lambda name: "fwd_" in name and "kernel" in name
+    is_copy = lambda name: "elementwise" in name and "MulFunctor" in name   # calibrate_copy
+    f_fwd, nf = _per_dispatch(fetch_rows, "FETCH_SIZE", is_fwd)
+    w_fwd, nw = _per_dispatch(write_rows, "WRITE_SIZE", is_fwd)
+    f_cp, _ = _per_dispatch(fetch_rows, "FETCH_SIZE", is_copy)
+    w_cp, _ = _per_dispatch(write_rows, "WRITE_SIZE", is_copy)
+    copy_kib = COPY_ELEMS * 2 / 1024.0
+    fs, ws = copy_kib / f_cp, copy_kib / w_cp
+    kname = next(name for name, *_ in fetch_rows if is_fwd(name))
+    rec = {"workload": args.workload, "kernel": kname, "kernel_digest": kernel_digest(),
+           "fetch_kib_per_dispatch": f_fwd, "write_kib_per_dispatch": w_fwd,
+           "dispatches": [nf, nw],
+           "copy_kib_each_way": copy_kib, "copy_fetch_kib": f_cp, "copy_write_kib": w_cp,
+           "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+           "hbm_bytes_per_launch": int(round((f_fwd * fs + w_fwd * ws) * 1024))}
+    out = os.path.join(ROOT, "profiles", "traffic_%s.json" % args.workload)
+    json.dump(rec, open(out, "w"), indent=1)
+    print(json.dumps(rec))
 
 
 def timed(step, args, dev):
@@ -212,7 +280,15 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
     ap.add_argument("--splits", type=int, default=0, help="decode key-range splits (0 = auto)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, run a plain 512 MiB bf16 copy three times "
+                         "(reference dispatches for the HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="summarise two rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE csv runs of "
+                         "'bench.py --calibrate-copy' into profiles/traffic_<workload>.json")
     args = ap.parse_args()
+    if args.pmc_summary:
+        return pmc_summary(args)
 
     if args.gpus != 1:
         log("bench.py runs on exactly one GPU: this build has no multi-GPU path "
@@ -249,6 +325,8 @@ def main():
                max_seqlen=max(lengths) if lengths else None, out=outs[j % nsets])
 
     ms_per_step = timed(step, args, dev)
+    if args.calibrate_copy:
+        calibrate_copy(dev)
     sec = ms_per_step / 1e3
     qps = rows / sec
     achieved_gbps = alg_bytes / sec / 1e9
