@@ -104,11 +104,6 @@ __device__ __forceinline__ void dma_window(uint16_t* Ks, uint16_t* Vs, const Ctx
 // (r/2) % 8 puts the 16 rows of a K-operand read on distinct banks.
 __device__ __forceinline__ int swu(int r, int c) { return r * D + ((c ^ ((r >> 1) & 7)) << 3); }
 
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-
 // All LDS reads of one skip unit -- two 16-byte K-operand chunks and four
 // transposed V-operand reads -- issued together and completed inside the
 // block.  The unit's slice was filled by this wave's own LDS-direct loads,
@@ -177,9 +172,6 @@ __device__ __forceinline__ void lds_read_oml(uint32_t a, uint32_t aml, f32x4_t (
     l = ml.y;
 }
 
-// Workgroup barrier for LDS traffic only: waits for this wave's LDS
-// operations, not for its loads in flight.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 // Number of periods t >= 0 with res + t*pi < n, for a residue res in
 // [a0, a0 + pi) of a sequence in which residue a0 has P periods.
@@ -279,7 +271,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     // Rows past the last key period any of the tile's queries uses (or past
     // the sequence) repeat the last needed row: the repeated lines are
     // fetched once per load, and the rows are masked out.
-    auto dma_unit = [&](uint16_t* stj, int ag, int kb, int it) {
+    auto dma_unit = [&](uint16_t* stj, int ag, int kb, int it) __attribute__((always_inline)) {
         const int32_t res = a0 + 16 * ag + 2 * wave + it;
         const int32_t row0 = res + (klo + 16 * kb) * pi;
         const int32_t umax = imin32(khi, periods_of(res, P, pi, n) - 1) - (klo + 16 * kb);
@@ -337,7 +329,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     }
 
     // ---------------------------------------------------------- window step
-    auto local = [&](int j, const uint16_t* Ks, const uint16_t* Vs) {
+    auto local = [&](int j, const uint16_t* Ks, const uint16_t* Vs) __attribute__((always_inline)) {
         const int32_t tp = t0 + wp + PW * j;
         if (tp >= P) return;                          // wave-uniform
         {
@@ -448,7 +440,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     const int32_t lcq = ((lane & 7) ^ (((lane >> 3) >> 1) & 7)) << 3;
     const uint32_t qoff = (uint32_t)(lane >> 3) * (uint32_t)pi * (uint32_t)a.sq.t + (uint32_t)lcq;
     const uint32_t goff = (uint32_t)(lane & 7) * (uint32_t)pi * (uint32_t)a.sg.t;
-    auto item_dma = [&](int ag) {
+    auto item_dma = [&](int ag) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < IW; ++it) {
             const int32_t rb = a0 + 16 * ag + 2 * wave + it + t0 * pi;   // row of period t0
@@ -469,7 +461,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
             __builtin_amdgcn_global_load_lds(gsrc, (lds_void_t*)(gst + slot * 64), 4, 0, 0);
         }
     };
-    auto item_init = [&](int ag) {
+    auto item_init = [&](int ag) __attribute__((always_inline)) {
 #pragma unroll
         for (int it = 0; it < IW; ++it) {
             const int32_t res = a0 + 16 * ag + 2 * wave + it;
@@ -499,7 +491,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
             scst[it] = sps[it];
         }
     };
-    auto item_unit = [&](int kb, const uint16_t* stj, auto itc) {
+    auto item_unit = [&](int kb, const uint16_t* stj, auto itc) __attribute__((always_inline)) {
         constexpr int it = decltype(itc)::value;
         const uint32_t base = lds_addr(stj) + (uint32_t)(wave * UNIT * 2);
         bf16x8_t kk[DC];
@@ -552,7 +544,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     // a-group read all slices; a second barrier frees stj for the next loads.
     // Slice layout [it][bb][g][col ^ (xx % 8)][4]: writes of a wave are
     // contiguous and the owners' 16 residues spread over the banks.
-    auto item_merge = [&](int ag, uint16_t* stj) {
+    auto item_merge = [&](int ag, uint16_t* stj) __attribute__((always_inline)) {
         const uint32_t sbase = lds_addr(stj);
 #pragma unroll
         for (int it = 0; it < IW; ++it) {
@@ -592,11 +584,11 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     // Every unit issues exactly 4 loads (past the last unit: a harmless
     // reload of the last one), so the loads of unit u are always followed by
     // those of units u+1..u+3 and vmcnt(12) waits for exactly unit u.
-    auto issue = [&](uint16_t* stj, int v) {
+    auto issue = [&](uint16_t* stj, int v) __attribute__((always_inline)) {
         const int q = imin32(v, NU - 1) >> 1;          // IW == 2 units per (a-group, key block)
         dma_unit(stj, q / nkb, q % nkb, imin32(v, NU - 1) & 1);
     };
-    auto unit = [&](int u, const uint16_t* stj, uint16_t* nxt, auto itc) {
+    auto unit = [&](int u, const uint16_t* stj, uint16_t* nxt, auto itc) __attribute__((always_inline)) {
         constexpr int it = decltype(itc)::value;
         issue(nxt, u + 3);
         __builtin_amdgcn_s_waitcnt(0xF7C);             // vmcnt(12): unit u has landed

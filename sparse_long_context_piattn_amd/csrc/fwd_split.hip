@@ -1,0 +1,593 @@
+// fwd_split.hip -- split prefill for head dim 64 or 128 (gfx950, bf16 MFMA):
+// a skip pass in residue layout, then a window pass in sequence layout that
+// merges the two partial softmaxes.
+//
+// Skip pass ("pi-Skip Attention").  Row i = a + t*pi has its skip keys at
+// the same residue a in the periods t -/+ m, m in [floor(k/pi)+1, M].  One
+// wave takes one residue and sweeps its periods in chunks of 16 query periods
+// (the 16 MFMA columns); the keys of a chunk are the NK = ceil(M/16)+1
+// (bidirectional: 2 ceil(M/16)+1) 16-period key blocks around it.  Per key
+// block ("unit") the wave stages the 16 K and V rows into its private LDS
+// slice with LDS-direct loads, several units ahead, and runs S^T = K Q^T, the
+// band mask, an online softmax and O^T += V^T P^T.  At the end of a chunk it
+// writes the normalised skip partial O_s (bf16) into the output rows and its
+// log-sum-exp (log2 units, without the gate prior) into a float buffer.
+// Each key block is staged NK times per residue instead of once per query.
+//
+// Window pass ("Ring-Local Attention" + "Dynamic Adaptive Fusion").  A
+// workgroup takes 128 consecutive query rows of one (sequence, head); the
+// keys [i-k, i] (bidirectional [i-k, i+k]) of all its rows stream through a
+// ring of three LDS slots of 64 rows, two slots ahead of the compute.  Each
+// wave owns 16 rows: S^T = K Q^T on v_mfma_f32_16x16x32_bf16, window mask,
+// log(alpha) prior, online softmax, O^T += V^T P^T.  In the epilogue, rows
+// that have skip keys combine their window partial with the skip partial
+// (whose log-sum-exp gets the log(1-alpha) prior here): one softmax over the
+// union of window and skip keys.
+//
+// Both passes keep the LDS-direct loads out of the compiler's view (dma16)
+// and wait for them explicitly, so no compiler-inserted wait drains the
+// pipelines.  Rows outside the sequence are loaded from a clamped valid row
+// and masked.
+#include "kernels.hpp"
+#include "mfma_util.hpp"
+
+#include <type_traits>
+
+namespace {
+
+constexpr int32_t EMPTY = 0x40000000;   // lower bound of an empty key range
+
+template <int D>
+struct Geo {
+    static constexpr int DC = D / 32;    // QK^T depth chunks (16x16x32)
+    static constexpr int DB = D / 16;    // O^T row blocks
+    static constexpr int CH = D / 8;     // 16-byte chunks per row
+    static constexpr int RPI = 64 / CH;  // rows covered by one 64-lane 16-byte load
+};
+
+// Element offset of 16-byte chunk c of row r of a row-major [rows][D] tile
+// whose chunks are XOR-swizzled by r % 8.
+template <int D>
+__device__ __forceinline__ int swr(int r, int c) { return r * D + ((c ^ (r & 7)) << 3); }
+
+// Same, swizzled by (r / 2) % 8: the 16 rows of a K-operand read then fall
+// on distinct banks when a row is 128 bytes.
+template <int D>
+__device__ __forceinline__ int swu(int r, int c) { return r * D + ((c ^ ((r >> 1) & 7)) << 3); }
+
+// 4-byte LDS-direct load of each active lane (lane l writes lds + 4 l).
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("global_load_lds_dword %0, %1" : : "v"(voff), "s"(uniform_ptr(sbase)),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+// Whether row (residue a, period t) with pr periods in its residue has any
+// skip key.
+template <bool BIDIR>
+__device__ __forceinline__ bool row_has_skip(int32_t t, int32_t pr, int32_t mlo, int32_t M) {
+    return M >= mlo && (t >= mlo || (BIDIR && t + mlo < pr));
+}
+
+// Tile order: consecutive logical tiles go to the same XCD.
+__device__ __forceinline__ int32_t xcd_logical(int32_t hw, int32_t total) {
+    const int32_t per = total / 8, rem = total % 8;
+    const int32_t xcd = hw % 8, loc = hw / 8;
+    return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+}
+
+// ================================================================= skip pass
+constexpr int SW = 4;                    // waves per skip workgroup (one residue each)
+
+template <int D>
+struct SkipGeo {
+    static constexpr int NS = D == 64 ? 3 : 2;       // unit slots per wave
+    static constexpr int PF = NS - 1;                // units in flight ahead
+    static constexpr int UNIT = 32 * D;              // elements: 16 K rows, then 16 V rows
+    static constexpr int LPU = UNIT * 2 / 1024;      // 1 KB loads per unit
+    static constexpr int QROWS = 16 * D;             // elements: the chunk's 16 query rows
+    static constexpr int LPQ = QROWS * 2 / 1024;     // 1 KB loads per query chunk
+};
+
+template <int D, bool BIDIR>
+__global__ __launch_bounds__(SW * 64) void fwd_skip_kernel(FwdArgs a, float* lse_s, int32_t rgroups,
+                                                           int32_t total) {
+    using G = Geo<D>;
+    using S = SkipGeo<D>;
+    constexpr int DC = G::DC, DB = G::DB, CH = G::CH, RPI = G::RPI;
+    constexpr int NS = S::NS, PF = S::PF, UNIT = S::UNIT, LPU = S::LPU, LPQ = S::LPQ;
+    __shared__ __attribute__((aligned(16))) uint16_t us[NS * SW * UNIT];   // NS unit slots
+    __shared__ __attribute__((aligned(16))) uint16_t qs[SW * S::QROWS];
+    uint16_t* const u0s = us;
+    uint16_t* const u1s = us + SW * UNIT;
+    uint16_t* const u2s = us + (NS - 1) * SW * UNIT;
+
+    const int32_t logical = xcd_logical(blockIdx.x, total);
+    const int32_t rg = logical % rgroups;
+    const int32_t rest = logical / rgroups;
+    const int32_t h = rest % a.H, b = rest / a.H;
+    int32_t n = a.n;
+    int64_t tok0 = 0;
+    if (a.cu) {
+        tok0 = a.cu[b];
+        n = a.cu[b + 1] - a.cu[b];
+    }
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, x = lane & 15, g = lane >> 4;
+    const int32_t pi = a.pat.pi, kw = a.pat.k, M = a.pat.M, mlo = kw / pi + 1;
+    const int32_t res = rg * SW + wave;
+    if (res >= pi || res >= n) return;                // no barriers in this kernel
+    const int32_t pr = (n - 1 - res) / pi + 1;        // periods of this residue
+    const int32_t nch = (pr + 15) >> 4;
+    const int32_t NBL = (M + 15) >> 4;
+    const int32_t NK = BIDIR ? 2 * NBL + 1 : NBL + 1;
+    const int32_t NU = nch * NK;
+
+    const int64_t bq = a.cu ? 0 : (int64_t)b;
+    const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + bq * a.sq.s + h * a.sq.h + tok0 * a.sq.t;
+    const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + bq * a.sk.s + h * a.sk.h + tok0 * a.sk.t;
+    const uint16_t* Vb = static_cast<const uint16_t*>(a.v) + bq * a.sv.s + h * a.sv.h + tok0 * a.sv.t;
+    uint16_t* Ob = static_cast<uint16_t*>(a.o) + bq * a.so.s + h * a.so.h + tok0 * a.so.t;
+    float* Ls = lse_s + ((int64_t)b * a.H + h) * a.n;
+    const int32_t sqt = (int32_t)a.sq.t, skt = (int32_t)a.sk.t, svt = (int32_t)a.sv.t;
+
+    // Lane constants of the loads: within load j of a 16-row block the lane
+    // takes row j*RPI + lane/CH (period offset u) and physical chunk lane%CH,
+    // which holds logical chunk (lane%CH) ^ ((u/2)%8).
+    int32_t lrow[16 / RPI], lch[16 / RPI];
+#pragma unroll
+    for (int j = 0; j < 16 / RPI; ++j) {
+        lrow[j] = j * RPI + lane / CH;
+        lch[j] = ((lane % CH) ^ ((lrow[j] >> 1) & 7)) << 3;
+    }
+    // 16 rows of residue res at periods p0 .. p0+15 (clamped into [0, pr-1])
+    // from src (token stride st) to LDS dst: 16/RPI loads.
+    auto load_rows = [&](const uint16_t* src, int32_t st, int32_t p0, uint16_t* dst) __attribute__((always_inline)) {
+        const bool inside = p0 >= 0 && p0 + 15 < pr;
+        const int32_t pb = imin32(imax32(p0, 0), pr - 1);   // base period (offsets below are >= 0)
+        const uint16_t* ub = src + (int64_t)(res + pb * pi) * st;
+#pragma unroll
+        for (int j = 0; j < 16 / RPI; ++j) {
+            const int32_t p = imin32(imax32(p0 + lrow[j], 0), pr - 1) - pb;
+            const uint32_t off = inside ? (uint32_t)(lrow[j] * pi * st + lch[j]) : (uint32_t)(p * pi * st + lch[j]);
+            dma16(ub, off * 2u, lds_addr(dst + j * RPI * D));
+        }
+    };
+    auto issue = [&](uint16_t* slot, int32_t v) __attribute__((always_inline)) {
+        v = imin32(v, NU - 1);                        // past the last unit: harmless reload
+        const int32_t c = v / NK, kb = c - NBL + v % NK;
+        uint16_t* ud = slot + wave * UNIT;
+        load_rows(Kb, skt, 16 * kb, ud);
+        load_rows(Vb, svt, 16 * kb, ud + 16 * D);
+    };
+    auto issue_q = [&](int32_t c) __attribute__((always_inline)) { load_rows(Qb, sqt, 16 * imin32(c, nch - 1), qs + wave * S::QROWS); };
+    static_assert(LPU == 2 * (16 / RPI) && LPQ == 16 / RPI, "load counts");
+
+    const float sl2 = a.scale_log2;
+    const int tr_row = 4 * g + (x >> 2);
+    const int tr_col = 4 * (x & 3);
+    const s16x4_t ones4 = __builtin_bit_cast(s16x4_t, make_uint2(0x3f803f80u, 0x3f803f80u));
+
+    // ---- state of the current chunk (query periods 16c + col, col = x)
+    bf16x8_t sq[DC];
+    f32x4_t sacc[DB];
+    float sm = -INFINITY, sl = 0.0f, smL = -INFINITY, scst = 0.0f;
+    int32_t slo = EMPTY, stq = 0;
+    uint32_t sspan = 0;
+    bool shs = false;
+
+    auto chunk_init = [&](int32_t c) __attribute__((always_inline)) {
+        const uint16_t* qd = qs + wave * S::QROWS;
+#pragma unroll
+        for (int cc = 0; cc < DC; ++cc)
+            sq[cc] = *reinterpret_cast<const bf16x8_t*>(qd + swu<D>(x, 4 * cc + g));
+        const int32_t tq = 16 * c + x;
+        shs = tq < pr && row_has_skip<BIDIR>(tq, pr, mlo, M);
+        const int32_t lo = imax32(tq - M, 0);
+        const int32_t hi = BIDIR ? imin32(tq + M, pr - 1) : tq - mlo;
+        slo = shs ? lo : EMPTY;
+        sspan = shs ? (uint32_t)(hi - lo) : 0u;
+        stq = tq;
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) sacc[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        sm = -INFINITY;
+        smL = -INFINITY;
+        sl = 0.0f;
+        scst = 0.0f;
+    };
+    auto chunk_store = [&](int32_t c) __attribute__((always_inline)) {
+        if (!shs) return;                             // no skip key: the window pass leaves the row alone
+        const float ltot = sl;                        // every lane holds its column's full sum
+        const float inv = 1.0f / ltot;
+        const int32_t row = res + (16 * c + x) * pi;
+        uint16_t* orow = Ob + (int64_t)row * a.so.t;
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) {
+            uint2 w;
+            w.x = cvt_pk_bf16(sacc[bb][0] * inv, sacc[bb][1] * inv);
+            w.y = cvt_pk_bf16(sacc[bb][2] * inv, sacc[bb][3] * inv);
+            *reinterpret_cast<uint2*>(orow + 16 * bb + 4 * g) = w;
+        }
+        if (g == 0) Ls[row] = sm + __log2f(ltot);
+    };
+    auto unit_compute = [&](int32_t kb, const uint16_t* slot) __attribute__((always_inline)) {
+        const uint16_t* Ks = slot + wave * UNIT;
+        const uint16_t* Vs = Ks + 16 * D;
+        f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int cc = 0; cc < DC; ++cc) {
+            const bf16x8_t kk = *reinterpret_cast<const bf16x8_t*>(Ks + swu<D>(x, 4 * cc + g));
+            s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, sq[cc], s4, 0, 0, 0);
+        }
+        const int32_t kp0 = 16 * kb + 4 * g;          // key period of this lane's value r = 0
+        const int32_t e0 = kp0 - slo;
+        const int32_t h0 = kp0 - stq + mlo - 1;
+        float sc[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            bool ok = (uint32_t)(e0 + r) <= sspan;
+            if (BIDIR) ok = ok && (uint32_t)(h0 + r) > (uint32_t)(2 * mlo - 2);
+            sc[r] = ok ? s4[r] : -INFINITY;
+        }
+        const float mx = max4(fmax_ieee(fmax_ieee(sc[0], sc[1]), fmax_ieee(sc[2], sc[3]))) * sl2;
+        if (__builtin_amdgcn_ballot_w64(mx > smL)) {
+            const float mnew = fmax_ieee(sm, mx);
+            const float mu = mnew == -INFINITY ? 0.0f : mnew;
+            const float fac = exp2_fast(sm - mu);
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb) sacc[bb] *= fac;
+            sl *= fac;
+            sm = mnew;
+            smL = mnew + LAZY;
+            scst = -mu;
+        }
+        const uint32_t w0 = cvt_pk_bf16(exp2_fast(fmaf(sc[0], sl2, scst)), exp2_fast(fmaf(sc[1], sl2, scst)));
+        const uint32_t w1 = cvt_pk_bf16(exp2_fast(fmaf(sc[2], sl2, scst)), exp2_fast(fmaf(sc[3], sl2, scst)));
+        const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(w0, w1));
+        s16x4_t vv[DB];
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) vv[bb] = ld_tr16(Vs + swu<D>(tr_row, 2 * bb + (tr_col >> 3)) + (tr_col & 7));
+        const f32x4_t ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, pb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        sl += ls[0];
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb)
+            sacc[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv[bb], pb, sacc[bb], 0, 0, 0);
+    };
+    // Unit u: issue unit u+PF into nxt (its slot was consumed at unit u-1),
+    // wait until this wave's loads of unit u have landed, compute.  The query
+    // rows of chunk c+1 are loaded right after chunk c has read its own.
+    auto unit = [&](int32_t u, const uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
+        issue(nxt, u + PF);
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(PF * LPU));
+        const int32_t c = u / NK, kbi = u - c * NK;
+        if (kbi == 0) {
+            chunk_init(c);
+            __builtin_amdgcn_s_waitcnt(0xC07F);       // lgkmcnt(0): query rows read
+            issue_q(c + 1);
+        }
+        unit_compute(c - NBL + kbi, cur);
+        if (kbi == NK - 1) chunk_store(c);
+    };
+
+    // The query rows of chunk c are issued while chunk c-1 starts, and NK >= 2
+    // >= PF units' loads follow them before chunk c's first wait: that wait
+    // also covers them.
+    issue_q(0);
+    issue(u0s, 0);
+    if (PF > 1) issue(u1s, 1);
+    if (NS == 3) {
+        for (int32_t u = 0; u < NU; u += 3) {
+            unit(u, u0s, u2s);
+            if (u + 1 >= NU) break;
+            unit(u + 1, u1s, u0s);
+            if (u + 2 >= NU) break;
+            unit(u + 2, u2s, u1s);
+        }
+    } else {
+        for (int32_t u = 0; u < NU; u += 2) {
+            unit(u, u0s, u1s);
+            if (u + 1 >= NU) break;
+            unit(u + 1, u1s, u0s);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));       // reloads past the end land before the LDS retires
+}
+
+// =============================================================== window pass
+constexpr int QT = 128;                  // query rows per workgroup (8 waves x 16)
+constexpr int KT = 64;                   // key rows per LDS slot
+
+template <int D, bool BIDIR>
+__global__ __launch_bounds__(NT) void fwd_window_kernel(FwdArgs a, const float* lse_s, int32_t q_tiles,
+                                                        int32_t total, int32_t merge) {
+    using G = Geo<D>;
+    constexpr int DC = G::DC, DB = G::DB, CH = G::CH, RPI = G::RPI;
+    constexpr int LPW = KT / RPI / (NW / 2);            // loads per wave per slot (waves 0-3 K, 4-7 V)
+    static_assert(KT % (RPI * (NW / 2)) == 0, "slot split");
+    static_assert(2 * KT >= QT, "query rows are staged through one slot pair");
+    __shared__ __attribute__((aligned(16))) uint16_t k0s[KT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t k1s[KT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t k2s[KT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t v0s[KT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t v1s[KT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t v2s[KT * D];
+    __shared__ __attribute__((aligned(16))) float gls[QT];
+
+    const int32_t logical = xcd_logical(blockIdx.x, total);
+    const int32_t qt = logical % q_tiles;
+    const int32_t rest = logical / q_tiles;
+    const int32_t h = rest % a.H, b = rest / a.H;
+    int32_t n = a.n;
+    int64_t tok0 = 0;
+    if (a.cu) {
+        tok0 = a.cu[b];
+        n = a.cu[b + 1] - a.cu[b];
+    }
+    const int32_t q0 = qt * QT;
+    if (q0 >= n) return;                                // workgroup-uniform
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, x = lane & 15, g = lane >> 4;
+    const int32_t pi = a.pat.pi, kw = a.pat.k, M = a.pat.M, mlo = kw / pi + 1;
+
+    const int64_t bq = a.cu ? 0 : (int64_t)b;
+    const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + bq * a.sq.s + h * a.sq.h + tok0 * a.sq.t;
+    const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + bq * a.sk.s + h * a.sk.h + tok0 * a.sk.t;
+    const uint16_t* Vb = static_cast<const uint16_t*>(a.v) + bq * a.sv.s + h * a.sv.h + tok0 * a.sv.t;
+    uint16_t* Ob = static_cast<uint16_t*>(a.o) + bq * a.so.s + h * a.so.h + tok0 * a.so.t;
+    const float* Gb = a.g + bq * a.sg.s + h * a.sg.h + tok0 * a.sg.t;
+    const float* Ls = lse_s ? lse_s + ((int64_t)b * a.H + h) * a.n : nullptr;
+
+    const int32_t klo = imax32(0, q0 - kw);
+    const int32_t khi = imin32(n - 1, q0 + QT - 1 + (BIDIR ? kw : 0));
+    const int32_t ntiles = (khi - klo) / KT + 1;
+
+    // ---- staging: slot rows r0 .. r0+RPI-1 per load; lane row r0 + lane/CH,
+    // physical chunk lane%CH = logical chunk (lane%CH) ^ (row%8)
+    const bool isv = wave >= NW / 2;
+    const uint16_t* src0 = isv ? Vb : Kb;
+    const int32_t st = isv ? (int32_t)a.sv.t : (int32_t)a.sk.t;
+    auto stage_rows = [&](const uint16_t* src, int32_t stt, int32_t s0, int r0, uint16_t* dst) __attribute__((always_inline)) {
+        const int rl = r0 + lane / CH;
+        const int lc = ((lane % CH) ^ (rl & 7)) << 3;
+        const bool inside = s0 >= 0 && s0 + RPI - 1 < n;
+        const uint16_t* ub = inside ? src + (int64_t)s0 * stt : src;
+        const uint32_t off = inside ? (uint32_t)((lane / CH) * stt + lc)
+                                    : (uint32_t)(imin32(imax32(s0 + lane / CH, 0), n - 1) * stt + lc);
+        dma16(ub, off * 2u, lds_addr(dst + r0 * D));
+    };
+    auto issue = [&](uint16_t* Ks, uint16_t* Vs, int32_t t) __attribute__((always_inline)) {
+        t = imin32(t, ntiles - 1);                       // past the last tile: harmless reload
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const int r0 = ((wave % (NW / 2)) * LPW + j) * RPI;
+            stage_rows(src0, st, klo + t * KT + r0, r0, isv ? Vs : Ks);
+        }
+    };
+
+    // ---- prologue: key tiles 0 and 1, the 128 query rows through slot 2
+    // (rows 0-63 in k2s, 64-127 in v2s) and the gate logits
+    issue(k0s, v0s, 0);
+    {
+#pragma unroll
+        for (int j = 0; j < LPW; ++j) {
+            const int r0 = ((wave % (NW / 2)) * LPW + j) * RPI;
+            stage_rows(Qb, (int32_t)a.sq.t, q0 + (isv ? KT : 0) + r0, r0, isv ? v2s : k2s);
+        }
+        if (wave == 0) {
+            const int32_t rr = imin32(q0 + lane, n - 1), rr2 = imin32(q0 + 64 + lane, n - 1);
+            dma4(Gb, (uint32_t)(rr * (int32_t)a.sg.t) * 4u, lds_addr(gls));
+            dma4(Gb, (uint32_t)(rr2 * (int32_t)a.sg.t) * 4u, lds_addr(gls + 64));
+        }
+    }
+    issue(k1s, v1s, 1);
+
+    const float sl2 = a.scale_log2;
+    const int tr_row = 4 * g + (x >> 2);
+    const int tr_col = 4 * (x & 3);
+    const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
+    const s16x4_t ones4 = __builtin_bit_cast(s16x4_t, make_uint2(0x3f803f80u, 0x3f803f80u));
+
+    // ---- the lane's query row
+    const int32_t i = q0 + 16 * wave + x;
+    const bool qv = i < n;
+    const int32_t ic = qv ? i : n - 1;
+    const int32_t ti = ic / pi, ai = ic - ti * pi;
+    const int32_t pr = (n - 1 - ai) / pi + 1;
+    const bool hs = row_has_skip<BIDIR>(ti, pr, mlo, M);
+    const int32_t lo = qv ? imax32(0, i - kw) : EMPTY;
+    const uint32_t span = qv ? (uint32_t)(imin32(n - 1, BIDIR ? i + kw : i) - lo) : 0u;
+    const int32_t w0 = q0 + 16 * wave;                  // the wave's key span
+    const int32_t wlo = imax32(0, w0 - kw);
+    const int32_t whi = w0 < n ? imin32(n - 1, imin32(w0 + 15, n - 1) + (BIDIR ? kw : 0)) : -1;
+
+    // wait for tile 0, the query rows and the gates (tile 1 may be in flight)
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPW));
+    lds_barrier();
+    bf16x8_t qf[DC];
+    float pl, ps;
+    {
+        const int qr = 16 * wave + x;                   // slot 2 holds rows 0-63 in K, 64-127 in V
+        const uint16_t* qsrc = qr < KT ? k2s : v2s;
+        const int rr = qr & (KT - 1);
+#pragma unroll
+        for (int c = 0; c < DC; ++c) qf[c] = *reinterpret_cast<const bf16x8_t*>(qsrc + swr<D>(rr, 4 * c + g));
+        gate_priors(gls[qr], hs, &pl, &ps);
+    }
+    lds_barrier();                                       // slot 2 is free for tile 2
+
+    f32x4_t acc[DB];
+#pragma unroll
+    for (int bb = 0; bb < DB; ++bb) acc[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float mrun = -INFINITY, lrun = 0.0f, mL = -INFINITY, cst = pl;
+
+    auto compute = [&](int32_t t, const uint16_t* Ks, const uint16_t* Vs) __attribute__((always_inline)) {
+        const int32_t kt0 = klo + t * KT;
+        if (kt0 > whi || kt0 + KT - 1 < wlo) return;    // wave-uniform
+        float sc[4][4];
+        bool act[4];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int32_t kb0 = kt0 + 16 * u;
+            act[u] = kb0 <= whi && kb0 + 15 >= wlo;     // wave-uniform
+#pragma unroll
+            for (int r = 0; r < 4; ++r) sc[u][r] = -INFINITY;
+            if (act[u]) {
+                f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < DC; ++c) {
+                    const bf16x8_t kk = *reinterpret_cast<const bf16x8_t*>(Ks + swr<D>(16 * u + x, 4 * c + g));
+                    s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qf[c], s4, 0, 0, 0);
+                }
+                const int32_t rel = kb0 + 4 * g - lo;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) sc[u][r] = (uint32_t)(rel + r) <= span ? s4[r] : -INFINITY;
+                mx = fmax_ieee(mx, fmax_ieee(fmax_ieee(sc[u][0], sc[u][1]), fmax_ieee(sc[u][2], sc[u][3])));
+            }
+        }
+        mx = fmaf(max4(mx), sl2, pl);
+        if (__builtin_amdgcn_ballot_w64(mx > mL)) {
+            const float mnew = fmax_ieee(mrun, mx);
+            const float mu = mnew == -INFINITY ? 0.0f : mnew;
+            const float fac = exp2_fast(mrun - mu);
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb) acc[bb] *= fac;
+            lrun *= fac;
+            mrun = mnew;
+            mL = mnew + LAZY;
+            cst = pl - mu;
+        }
+        s16x4_t pb[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const uint32_t w0 = cvt_pk_bf16(exp2_fast(fmaf(sc[u][0], sl2, cst)), exp2_fast(fmaf(sc[u][1], sl2, cst)));
+            const uint32_t w1 = cvt_pk_bf16(exp2_fast(fmaf(sc[u][2], sl2, cst)), exp2_fast(fmaf(sc[u][3], sl2, cst)));
+            pb[u] = __builtin_bit_cast(s16x4_t, make_uint2(w0, w1));
+        }
+        f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int u = 0; u < 4; u += 2) {
+            if (!act[u] && !act[u + 1]) continue;
+            const bf16x8_t pp =
+                __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(pb[u], pb[u + 1], 0, 1, 2, 3, 4, 5, 6, 7));
+            lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pp, lsum, 0, 0, 0);
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb) {
+                const s16x4_t v0 = ld_tr16(Vs + swr<D>(16 * u + tr_row, 2 * bb + (tr_col >> 3)) + (tr_col & 7));
+                const s16x4_t v1 = ld_tr16(Vs + swr<D>(16 * u + 16 + tr_row, 2 * bb + (tr_col >> 3)) + (tr_col & 7));
+                const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
+                acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pp, acc[bb], 0, 0, 0);
+            }
+        }
+        lrun += 0.25f * lsum[0];                        // quarter per lane; sum4 restores the row sum
+    };
+    // step t: wait for this wave's loads of tile t (tile t+1 may be in
+    // flight), barrier (everyone's tile t landed, tile t-1 fully read), issue
+    // tile t+2 into the slot of tile t-1, compute tile t
+    auto step = [&](int32_t t, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn) __attribute__((always_inline)) {
+        if (t > 0) {
+            __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPW));
+            lds_barrier();
+        }
+        issue(Kn, Vn, t + 2);
+        compute(t, Kc, Vc);
+    };
+    for (int32_t t = 0; t < ntiles; t += 3) {
+        step(t, k0s, v0s, k2s, v2s);
+        if (t + 1 >= ntiles) break;
+        step(t + 1, k1s, v1s, k0s, v0s);
+        if (t + 2 >= ntiles) break;
+        step(t + 2, k2s, v2s, k1s, v1s);
+    }
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));         // reloads past the end land before the LDS retires
+
+    // ---- epilogue: window partial, merged with the skip partial when the
+    // row has skip keys (its lse gets the log(1-alpha) prior here)
+    const float ltot = sum4(lrun);
+    if (!qv) return;
+    const float lw = mrun + __log2f(ltot);              // log2-sum-exp of the window part
+    float fw = 1.0f / ltot, fs = 0.0f, lfin = lw;
+    uint16_t* orow = Ob + (int64_t)i * a.so.t;
+    uint2 os[DB];
+    if (merge && hs) {
+        const float lsk = Ls[i] + ps;
+        const float mx = fmaxf(lw, lsk);
+        const float aw = exp2_fast(lw - mx), as = exp2_fast(lsk - mx);
+        const float inv = 1.0f / (aw + as);
+        fw = ltot > 0.0f ? aw * inv / ltot : 0.0f;     // alpha = 0: the window part is empty
+        fs = as * inv;
+        lfin = mx + __log2f(aw + as);
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) os[bb] = *reinterpret_cast<const uint2*>(orow + 16 * bb + 4 * g);
+    } else {
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) os[bb] = make_uint2(0, 0);
+    }
+#pragma unroll
+    for (int bb = 0; bb < DB; ++bb) {
+        uint2 w;
+        w.x = cvt_pk_bf16(fmaf(acc[bb][0], fw, bf16lo(os[bb].x) * fs), fmaf(acc[bb][1], fw, bf16hi(os[bb].x) * fs));
+        w.y = cvt_pk_bf16(fmaf(acc[bb][2], fw, bf16lo(os[bb].y) * fs), fmaf(acc[bb][3], fw, bf16hi(os[bb].y) * fs));
+        *reinterpret_cast<uint2*>(orow + 16 * bb + 4 * g) = w;
+    }
+    if (a.lse && g == 0) a.lse[bq * a.sg.s + h * a.sg.h + (tok0 + i) * a.sg.t] = lfin * PIATTN_LN2;
+}
+
+template <int D, bool BIDIR>
+hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
+    const int32_t mlo = a.pat.k / a.pat.pi + 1;
+    const bool skips = a.pat.M >= mlo;
+    float* lse_s = nullptr;
+    if (skips) {
+        const size_t bytes = (size_t)a.B * a.H * a.n * sizeof(float);
+        hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&lse_s), bytes, stream);
+        if (e != hipSuccess) return e;
+        const int32_t rgroups = (imin32(a.pat.pi, a.n) + SW - 1) / SW;
+        const int64_t total = (int64_t)rgroups * a.H * a.B;
+        if (total > 0x7fffffff) {
+            (void)hipFreeAsync(lse_s, stream);
+            return hipErrorInvalidConfiguration;
+        }
+        hipLaunchKernelGGL((fwd_skip_kernel<D, BIDIR>), dim3((uint32_t)total), dim3(SW * 64), 0, stream, a, lse_s,
+                           rgroups, (int32_t)total);
+        e = hipGetLastError();
+        if (e != hipSuccess) {
+            (void)hipFreeAsync(lse_s, stream);
+            return e;
+        }
+    }
+    const int32_t q_tiles = (a.n + QT - 1) / QT;
+    const int64_t total = (int64_t)q_tiles * a.H * a.B;
+    hipError_t e = hipSuccess;
+    if (total > 0x7fffffff) {
+        e = hipErrorInvalidConfiguration;
+    } else {
+        hipLaunchKernelGGL((fwd_window_kernel<D, BIDIR>), dim3((uint32_t)total), dim3(NT), 0, stream, a, lse_s,
+                           q_tiles, (int32_t)total, skips ? 1 : 0);
+        e = hipGetLastError();
+    }
+    if (lse_s) {
+        const hipError_t f = hipFreeAsync(lse_s, stream);
+        if (e == hipSuccess) e = f;
+    }
+    return e;
+}
+
+}  // namespace
+
+bool fwd_split_supported(int dtype, const FwdArgs& a) {
+    if (dtype != 1 || (a.d != 64 && a.d != 128)) return false;
+    // 32-bit element offsets: rows of the sequence, and the lane offsets of
+    // 16 rows one period apart
+    int64_t ts = a.sk.t > a.sv.t ? a.sk.t : a.sv.t;
+    ts = ts > a.sq.t ? ts : a.sq.t;
+    ts = ts > 2 * a.sg.t ? ts : 2 * a.sg.t;            // the gate's byte offsets are twice as large
+    const int64_t span = (int64_t)a.n + 16LL * a.pat.pi + a.d;
+    return span * ts < ((int64_t)1 << 31) && (int64_t)a.n + 2LL * a.pat.k + QT < ((int64_t)1 << 30);
+}
+
+hipError_t launch_fwd_split(const FwdArgs& a, hipStream_t stream) {
+    if (a.d == 64) return a.pat.bidir ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
+    return a.pat.bidir ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
+}

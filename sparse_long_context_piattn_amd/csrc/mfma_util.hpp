@@ -76,3 +76,33 @@ template <int D>
 __device__ __forceinline__ int swz(int r, int c) {
     return r * D + ((c ^ (r & 7)) << 3);
 }
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS
+// operations, not for its loads in flight.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// the wave are outstanding (loads complete in order), other counters free.
+constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// LDS-direct 16-byte loads issued through inline assembly: lane l's 16 bytes
+// at sbase + voff land at LDS byte address lds + 16*l.  The compiler does not
+// see these loads, so it adds no (pipeline-draining) waits for them: the
+// caller waits with vm_wait_imm before reading the data, and no compiler-
+// visible load may be consumed while they are in flight unless an explicit
+// wait covers them.  sbase must be wave-uniform.
+__device__ __forceinline__ const void* uniform_ptr(const void* p) {
+    const uint64_t v = reinterpret_cast<uint64_t>(p);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(uniform_ptr(sbase)),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
