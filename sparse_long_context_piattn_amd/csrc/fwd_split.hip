@@ -293,6 +293,204 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_kernel(FwdArgs a, float* lse
     __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));       // reloads past the end land before the LDS retires
 }
 
+// Register-ring variant of the skip pass for head dim 64 and short bands
+// (NK = NBL+1, or 2 NBL+1 bidirectional, <= 5 blocks).  The key blocks of a
+// residue form a stream: entry j is block j - NBL, chunk c uses entries
+// c .. c+NK-1, and each chunk adds exactly one.  Every entry is staged into
+// LDS once (two entries ahead), then its MFMA operands -- the K chunks and
+// the transposed V^T chunks -- are read into a ring of NK register sets and
+// reused by all NK chunks that need them, so K and V are fetched once per
+// residue instead of NK times.  The loop starts NK-1 "virtual" chunks early,
+// which only fill the ring.
+template <int NBL, bool BIDIR>
+__global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float* lse_s, int32_t rgroups,
+                                                                int32_t total) {
+    constexpr int D = 64;
+    using G = Geo<D>;
+    constexpr int DC = G::DC, DB = G::DB, CH = G::CH, RPI = G::RPI;
+    constexpr int NK = BIDIR ? 2 * NBL + 1 : NBL + 1;
+    constexpr int BLK = 32 * D;                          // elements of one staged entry: 16 K + 16 V rows
+    constexpr int QR = 16 * D;                           // elements of one chunk's query rows
+    constexpr int WSLICE = 3 * BLK + 2 * QR;             // per wave: 3 entry slots, 2 query slots
+    __shared__ __attribute__((aligned(16))) uint16_t lds[SW * WSLICE];
+
+    const int32_t logical = xcd_logical(blockIdx.x, total);
+    const int32_t rg = logical % rgroups;
+    const int32_t rest = logical / rgroups;
+    const int32_t h = rest % a.H, b = rest / a.H;
+    int32_t n = a.n;
+    int64_t tok0 = 0;
+    if (a.cu) {
+        tok0 = a.cu[b];
+        n = a.cu[b + 1] - a.cu[b];
+    }
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, x = lane & 15, g = lane >> 4;
+    const int32_t pi = a.pat.pi, kw = a.pat.k, M = a.pat.M, mlo = kw / pi + 1;
+    const int32_t res = rg * SW + wave;
+    if (res >= pi || res >= n) return;                  // no barriers in this kernel
+    const int32_t pr = (n - 1 - res) / pi + 1;
+    const int32_t nch = (pr + 15) >> 4;
+
+    const int64_t bq = a.cu ? 0 : (int64_t)b;
+    const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + bq * a.sq.s + h * a.sq.h + tok0 * a.sq.t;
+    const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + bq * a.sk.s + h * a.sk.h + tok0 * a.sk.t;
+    const uint16_t* Vb = static_cast<const uint16_t*>(a.v) + bq * a.sv.s + h * a.sv.h + tok0 * a.sv.t;
+    uint16_t* Ob = static_cast<uint16_t*>(a.o) + bq * a.so.s + h * a.so.h + tok0 * a.so.t;
+    float* Ls = lse_s + ((int64_t)b * a.H + h) * a.n;
+    const int32_t sqt = (int32_t)a.sq.t, skt = (int32_t)a.sk.t, svt = (int32_t)a.sv.t;
+    uint16_t* const ws = lds + wave * WSLICE;
+
+    int32_t lrow[16 / RPI], lch[16 / RPI];
+#pragma unroll
+    for (int j = 0; j < 16 / RPI; ++j) {
+        lrow[j] = j * RPI + lane / CH;
+        lch[j] = ((lane % CH) ^ ((lrow[j] >> 1) & 7)) << 3;
+    }
+    auto load_rows = [&](const uint16_t* src, int32_t st, int32_t p0, uint16_t* dst) __attribute__((always_inline)) {
+        const bool inside = p0 >= 0 && p0 + 15 < pr;
+        const int32_t pb = imin32(imax32(p0, 0), pr - 1);
+        const uint16_t* ub = src + (int64_t)(res + pb * pi) * st;
+#pragma unroll
+        for (int j = 0; j < 16 / RPI; ++j) {
+            const int32_t p = imin32(imax32(p0 + lrow[j], 0), pr - 1) - pb;
+            const uint32_t off = inside ? (uint32_t)(lrow[j] * pi * st + lch[j]) : (uint32_t)(p * pi * st + lch[j]);
+            dma16(ub, off * 2u, lds_addr(dst + j * RPI * D));
+        }
+    };
+    // stream entry j (block j - NBL) into entry slot j % 3: 4 loads
+    auto issue_entry = [&](int32_t j) __attribute__((always_inline)) {
+        uint16_t* d = ws + (((j % 3) + 3) % 3) * BLK;
+        load_rows(Kb, skt, 16 * (j - NBL), d);
+        load_rows(Vb, svt, 16 * (j - NBL), d + 16 * D);
+    };
+    // query rows of chunk c (clamped into the residue) into query slot c % 2: 2 loads
+    auto issue_q = [&](int32_t c) __attribute__((always_inline)) {
+        load_rows(Qb, sqt, 16 * imin32(imax32(c, 0), nch - 1), ws + 3 * BLK + (c & 1) * QR);
+    };
+
+    const float sl2 = a.scale_log2;
+    const int tr_row = 4 * g + (x >> 2);
+    const int tr_col = 4 * (x & 3);
+    const s16x4_t ones4 = __builtin_bit_cast(s16x4_t, make_uint2(0x3f803f80u, 0x3f803f80u));
+
+    bf16x8_t kr[NK][DC];                                  // ring of entry operands
+    s16x4_t vr[NK][DB];
+    bf16x8_t sq[DC];
+#pragma unroll
+    for (int e = 0; e < NK; ++e) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) kr[e][c] = bf16x8_t{};
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) vr[e][bb] = s16x4_t{0, 0, 0, 0};
+    }
+
+    // chunk c (>= -(NK-1)); RS = (entry c+NK-1) % NK, the ring slot it fills
+    auto chunk = [&](int32_t c, auto rsc) __attribute__((always_inline)) {
+        constexpr int RS = decltype(rsc)::value;
+        const int32_t e = c + NK - 1;
+        // entry e and the query rows of chunk c have landed: after them only
+        // entry e+1 and the query rows of chunk c+1 were issued (4 + 2 loads)
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(6));
+        {
+            const uint16_t* es = ws + ((e % 3 + 3) % 3) * BLK;
+#pragma unroll
+            for (int cc = 0; cc < DC; ++cc)
+                kr[RS][cc] = *reinterpret_cast<const bf16x8_t*>(es + swu<D>(x, 4 * cc + g));
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb)
+                vr[RS][bb] = ld_tr16(es + 16 * D + swu<D>(tr_row, 2 * bb + (tr_col >> 3)) + (tr_col & 7));
+        }
+        if (c >= 0) {
+            const uint16_t* qd = ws + 3 * BLK + (c & 1) * QR;
+#pragma unroll
+            for (int cc = 0; cc < DC; ++cc) sq[cc] = *reinterpret_cast<const bf16x8_t*>(qd + swu<D>(x, 4 * cc + g));
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0): both slots read
+        issue_entry(e + 2);
+        issue_q(c + 2);
+        if (c < 0) return;                                // wave-uniform: filling the ring
+
+        const int32_t tq = 16 * c + x;
+        const bool hs = tq < pr && row_has_skip<BIDIR>(tq, pr, mlo, M);
+        const int32_t lo = imax32(tq - M, 0);
+        const int32_t hi = BIDIR ? imin32(tq + M, pr - 1) : tq - mlo;
+        const int32_t slo = hs ? lo : EMPTY;
+        const uint32_t sspan = hs ? (uint32_t)(hi - lo) : 0u;
+        f32x4_t sacc[DB];
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) sacc[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        float sm = -INFINITY, sl = 0.0f, smL = -INFINITY, scst = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int slot = (RS + 1 + i) % NK;           // entry c + i
+            const int32_t kb = c + i - NBL;
+            f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int cc = 0; cc < DC; ++cc) s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[slot][cc], sq[cc], s4, 0, 0, 0);
+            const int32_t kp0 = 16 * kb + 4 * g;
+            const int32_t e0 = kp0 - slo;
+            const int32_t h0 = kp0 - tq + mlo - 1;
+            float sc[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                bool ok = (uint32_t)(e0 + r) <= sspan;
+                if (BIDIR) ok = ok && (uint32_t)(h0 + r) > (uint32_t)(2 * mlo - 2);
+                sc[r] = ok ? s4[r] : -INFINITY;
+            }
+            const float mx = max4(fmax_ieee(fmax_ieee(sc[0], sc[1]), fmax_ieee(sc[2], sc[3]))) * sl2;
+            if (__builtin_amdgcn_ballot_w64(mx > smL)) {
+                const float mnew = fmax_ieee(sm, mx);
+                const float mu = mnew == -INFINITY ? 0.0f : mnew;
+                const float fac = exp2_fast(sm - mu);
+#pragma unroll
+                for (int bb = 0; bb < DB; ++bb) sacc[bb] *= fac;
+                sl *= fac;
+                sm = mnew;
+                smL = mnew + LAZY;
+                scst = -mu;
+            }
+            const uint32_t w0 = cvt_pk_bf16(exp2_fast(fmaf(sc[0], sl2, scst)), exp2_fast(fmaf(sc[1], sl2, scst)));
+            const uint32_t w1 = cvt_pk_bf16(exp2_fast(fmaf(sc[2], sl2, scst)), exp2_fast(fmaf(sc[3], sl2, scst)));
+            const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(w0, w1));
+            const f32x4_t ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, pb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            sl += ls[0];
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb)
+                sacc[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[slot][bb], pb, sacc[bb], 0, 0, 0);
+        }
+        if (!hs) return;
+        const float inv = 1.0f / sl;
+        const int32_t row = res + tq * pi;
+        uint16_t* orow = Ob + (int64_t)row * a.so.t;
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) {
+            uint2 w;
+            w.x = cvt_pk_bf16(sacc[bb][0] * inv, sacc[bb][1] * inv);
+            w.y = cvt_pk_bf16(sacc[bb][2] * inv, sacc[bb][3] * inv);
+            *reinterpret_cast<uint2*>(orow + 16 * bb + 4 * g) = w;
+        }
+        if (g == 0) Ls[row] = sm + __log2f(sl);
+    };
+
+    // entries 0, 1 and the query rows of chunks c0, c0+1 in the order the
+    // chunk loop keeps (entry, query, entry, query)
+    const int32_t c0 = -(NK - 1);
+    issue_entry(0);
+    issue_q(c0);
+    issue_entry(1);
+    issue_q(c0 + 1);
+    for (int32_t c = c0; c < nch; c += NK) {
+        chunk(c, std::integral_constant<int, 0>{});
+        if (NK > 1) { if (c + 1 >= nch) break; chunk(c + 1, std::integral_constant<int, 1 % NK>{}); }
+        if (NK > 2) { if (c + 2 >= nch) break; chunk(c + 2, std::integral_constant<int, 2 % NK>{}); }
+        if (NK > 3) { if (c + 3 >= nch) break; chunk(c + 3, std::integral_constant<int, 3 % NK>{}); }
+        if (NK > 4) { if (c + 4 >= nch) break; chunk(c + 4, std::integral_constant<int, 4 % NK>{}); }
+    }
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));         // loads issued past the end land before the LDS retires
+}
+
 // =============================================================== window pass
 constexpr int QT = 128;                  // query rows per workgroup (8 waves x 16)
 constexpr int KT = 64;                   // key rows per LDS slot
@@ -549,8 +747,19 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
             (void)hipFreeAsync(lse_s, stream);
             return hipErrorInvalidConfiguration;
         }
-        hipLaunchKernelGGL((fwd_skip_kernel<D, BIDIR>), dim3((uint32_t)total), dim3(SW * 64), 0, stream, a, lse_s,
-                           rgroups, (int32_t)total);
+        const int32_t nbl = (a.pat.M + 15) / 16;
+        if (D == 64 && nbl <= (BIDIR ? 2 : 4)) {
+            // short bands: every key block staged once per residue (register ring)
+            auto ring = nbl == 1 ? fwd_skip_ring_kernel<1, BIDIR>
+                      : nbl == 2 ? fwd_skip_ring_kernel<2, BIDIR>
+                      : nbl == 3 ? fwd_skip_ring_kernel<BIDIR ? 2 : 3, BIDIR>
+                                 : fwd_skip_ring_kernel<BIDIR ? 2 : 4, BIDIR>;
+            hipLaunchKernelGGL(ring, dim3((uint32_t)total), dim3(SW * 64), 0, stream, a, lse_s, rgroups,
+                               (int32_t)total);
+        } else {
+            hipLaunchKernelGGL((fwd_skip_kernel<D, BIDIR>), dim3((uint32_t)total), dim3(SW * 64), 0, stream, a,
+                               lse_s, rgroups, (int32_t)total);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) {
             (void)hipFreeAsync(lse_s, stream);
