@@ -68,11 +68,18 @@ __device__ __forceinline__ bool row_has_skip(int32_t t, int32_t pr, int32_t mlo,
     return M >= mlo && (t >= mlo || (BIDIR && t + mlo < pr));
 }
 
-// Tile order: consecutive logical tiles go to the same XCD.
+// Tile order.  Workgroup hw runs on XCD hw % 8 as that XCD's (hw / 8)-th.
+// Logical tiles are dealt to the XCDs in runs of XG consecutive tiles, run
+// r to XCD r % 8: neighbouring tiles (which share halo rows) share an L2,
+// and the runs of long and short sequences spread over all XCDs.
+constexpr int32_t XG = 16;
 __device__ __forceinline__ int32_t xcd_logical(int32_t hw, int32_t total) {
-    const int32_t per = total / 8, rem = total % 8;
     const int32_t xcd = hw % 8, loc = hw / 8;
-    return (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+    const int32_t logical = ((loc / XG) * 8 + xcd) * XG + loc % XG;
+    // the last, partial round of runs: fall back to the plain order so that
+    // every logical tile below total is produced exactly once
+    const int32_t full = total / (8 * XG) * (8 * XG);
+    return hw < full ? logical : hw;
 }
 
 // ================================================================= skip pass
