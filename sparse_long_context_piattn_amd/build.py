@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libpiattn.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.cpp", "neighbors.hip", "fwd_gather.hip", "fwd_tiled.hip", "fwd_resid.hip",
+SOURCES = ["api.cpp", "neighbors.hip", "fwd_gather.hip", "fwd_resid.hip",
            "fwd_split.hip", "decode.hip"]
 
 # Packed-fp32 VALU forms are kept out of the device code (plain fp32 only).

@@ -179,20 +179,18 @@ int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
     a.scale_log2 = scale_log2(pattern, d);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int dt = dtype == PIATTN_BF16 ? 1 : 0;
-    // Kernel choice.  PIATTN_FWD_KERNEL = resid | split | tiled | gather forces
+    // Kernel choice.  PIATTN_FWD_KERNEL = split | resid | gather forces
     // one kernel (testing and measurement; EUNSUPPORTED if it cannot take the
     // call); unset or "auto" picks the first that can.
     const char* force = getenv("PIATTN_FWD_KERNEL");
     if (force && *force && strcmp(force, "auto") != 0) {
         if (!strcmp(force, "resid") && fwd_resid_supported(dt, a)) return launch_status(launch_fwd_resid(a, st));
         if (!strcmp(force, "split") && fwd_split_supported(dt, a)) return launch_status(launch_fwd_split(a, st));
-        if (!strcmp(force, "tiled") && fwd_tiled_supported(dt, a)) return launch_status(launch_fwd_tiled(a, st));
         if (!strcmp(force, "gather")) return launch_status(launch_fwd_gather(dt, a, st));
         return fail(PIATTN_EUNSUPPORTED, "PIATTN_FWD_KERNEL=%s cannot take this call", force);
     }
     if (fwd_split_supported(dt, a)) return launch_status(launch_fwd_split(a, st));
     if (fwd_resid_supported(dt, a)) return launch_status(launch_fwd_resid(a, st));
-    if (fwd_tiled_supported(dt, a)) return launch_status(launch_fwd_tiled(a, st));
     return launch_status(launch_fwd_gather(dt, a, st));
 }
 

@@ -11,8 +11,8 @@
 // according to the key's kind (pi-Attention "Dynamic Adaptive Fusion":
 // log(alpha) on local logits, log(1 - alpha) on skip logits, one softmax).
 //
-// This path serves fp32, d = 32, and patterns the tiled prefill kernel does
-// not take, and is the building block of split-K decode.
+// This path serves fp32 and d = 32 prefill (the MFMA kernels take bf16 with
+// d = 64 or 128), and is the building block of split-K decode.
 #pragma once
 
 #include "common.hpp"

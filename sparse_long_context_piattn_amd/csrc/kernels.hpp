@@ -8,12 +8,8 @@
 
 // dtype: 0 = fp32, 1 = bf16 (same values as piattn_dtype).
 hipError_t launch_fwd_gather(int dtype, const FwdArgs& a, hipStream_t stream);
-// Residue-tiled MFMA prefill (bf16, d 64/128, pi a multiple of 64, window
-// small enough for the LDS stage); launch_fwd_gather serves everything else.
-bool fwd_tiled_supported(int dtype, const FwdArgs& a);
-hipError_t launch_fwd_tiled(const FwdArgs& a, hipStream_t stream);
-// Residue-layout prefill for head dim 64 (window phase + dense skip band);
-// tried before fwd_tiled.
+// Residue-layout single-kernel prefill for head dim 64 (window phase + dense
+// skip band merged in LDS); selectable with PIATTN_FWD_KERNEL=resid.
 bool fwd_resid_supported(int dtype, const FwdArgs& a);
 hipError_t launch_fwd_resid(const FwdArgs& a, hipStream_t stream);
 // Split prefill (bf16, d 64/128, any pi): skip pass in residue layout, then a

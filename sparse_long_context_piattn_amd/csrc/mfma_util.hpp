@@ -1,4 +1,4 @@
-// mfma_util.hpp -- small gfx950 helpers shared by the tiled prefill kernels:
+// mfma_util.hpp -- small gfx950 helpers shared by the MFMA prefill kernels:
 // bf16 vector types, hardware bf16 packing, 4-lane reductions with
 // v_permlane16/32_swap, the transposing LDS read and the XOR swizzle of the
 // [rows][D] LDS tiles.

@@ -1,7 +1,7 @@
 """GPU parity of every prefill kernel, each forced through PIATTN_FWD_KERNEL.
 
 The default dispatch runs one kernel per call shape; these tests pin each
-kernel (residue-layout, split, residue-tiled, gather) to the fp64 oracle on
+kernel (split, residue-layout, gather) to the fp64 oracle on
 the cases it accepts, so that a kernel the dispatch does not pick for the
 headline shapes stays covered.  Tolerances as in test_gpu_parity.
 """
@@ -22,7 +22,7 @@ pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
 
 DEV = "cuda:0"
-KERNELS = ["resid", "split", "tiled", "gather"]
+KERNELS = ["split", "resid", "gather"]
 
 
 def run_fwd(x, w, kernel, **kw):

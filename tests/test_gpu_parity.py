@@ -114,7 +114,7 @@ SMALL = [
     ("tiles_d64_pi128", "bf16", 2, 2, 4096 + 77, 64, 64, 128, 16, False),
     ("tiles_d128_pi256", "bf16", 1, 2, 9000, 128, 128, 256, 20, False),
     ("tiles_bidir_pi64", "bf16", 1, 2, 5000, 64, 32, 64, 32, True),
-    # residue-tiled MFMA path (pi a multiple of 64, d 64/128)
+    # larger shapes: several MFMA tiles, chunks and ragged tails
     ("tiled_pi64_d64", "bf16", 2, 3, 3000, 64, 20, 64, 10, False),
     ("tiled_pi_le_k", "bf16", 1, 2, 2000, 64, 70, 64, 5, False),
     ("tiled_no_skips", "bf16", 1, 2, 1500, 64, 64, 128, 0, False),
