@@ -24,8 +24,12 @@
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The
  *     piattn_pattern struct is host memory, read during the call only.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
- *     and the call returns without synchronising.  The library allocates no
- *     memory and keeps no state besides a thread-local error string.
+ *     and the call returns without synchronising.  The library keeps no
+ *     state besides a thread-local error string and allocates no memory,
+ *     with one exception: piattn_fwd on its bf16 d = 64 / 128 path takes a
+ *     stream-ordered temporary of B*H*n floats (hipMallocAsync, released
+ *     with hipFreeAsync on `stream`) for the per-row log-sum-exp that its
+ *     skip pass hands to its window pass.
  *   - Every argument is validated before anything is launched.  A non-zero
  *     status is returned on error and piattn_last_error() describes it.
  *     Nothing aborts and nothing throws across the ABI.

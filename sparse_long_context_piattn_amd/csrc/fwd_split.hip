@@ -10,8 +10,8 @@
 // block ("unit") the wave stages the 16 K and V rows into its private LDS
 // slice with LDS-direct loads, several units ahead, and runs S^T = K Q^T, the
 // band mask, an online softmax and O^T += V^T P^T.  At the end of a chunk it
-// writes the normalised skip partial O_s (bf16) into the output rows and its
-// log-sum-exp (log2 units, without the gate prior) into a float buffer.
+// writes the normalised skip partial O_s (fp16, scaled) into the output rows
+// and its log-sum-exp (log2 units, without the gate prior) into a temporary.
 // Each key block is staged NK times per residue instead of once per query.
 //
 // Window pass ("Ring-Local Attention" + "Dynamic Adaptive Fusion").  A
@@ -82,6 +82,45 @@ __device__ __forceinline__ int32_t xcd_logical(int32_t hw, int32_t total) {
     return hw < full ? logical : hw;
 }
 
+// Skip partial of one row, handed from the skip pass to the window pass.
+// The normalised O_s goes into the row's output slots as fp16 scaled by
+// 2^-e, e chosen from the row's largest magnitude m so that m 2^-e lies in
+// [2^14, 2^15): no overflow, full fp16 precision (4x that of bf16, so the
+// merge adds well under a quarter ulp of the final bf16 rounding).  Its
+// log2-sum-exp and e go into the row's two-float record of the temporary.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_pk_f16(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
+}
+__device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[0]; }
+__device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[1]; }
+
+template <int DB>
+__device__ __forceinline__ void store_skip_partial(uint16_t* orow, const f32x4_t (&sacc)[DB], float inv, float lse2,
+                                                   float* rec, int g) {
+    float mloc = 0.0f;
+#pragma unroll
+    for (int bb = 0; bb < DB; ++bb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) mloc = fmax_ieee(mloc, fabsf(sacc[bb][r]));
+    const float m = max4(mloc) * inv;
+    const int32_t ex = (int32_t)((__float_as_uint(m) >> 23) & 0xff);   // m < 2^(ex - 126)
+    const int32_t e = imax32(-64, ex - 141);                           // m * 2^-e in [2^14, 2^15)
+    const float sc = __builtin_amdgcn_ldexpf(inv, -e);
+#pragma unroll
+    for (int bb = 0; bb < DB; ++bb) {
+        uint2 w;
+        w.x = cvt_pk_f16(sacc[bb][0] * sc, sacc[bb][1] * sc);
+        w.y = cvt_pk_f16(sacc[bb][2] * sc, sacc[bb][3] * sc);
+        *reinterpret_cast<uint2*>(orow + 16 * bb + 4 * g) = w;
+    }
+    if (g == 0) {
+        rec[0] = lse2;
+        rec[1] = (float)e;
+    }
+}
+
 // ================================================================= skip pass
 constexpr int SW = 4;                    // waves per skip workgroup (one residue each)
 
@@ -135,7 +174,7 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_kernel(FwdArgs a, float* lse
     const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + bq * a.sk.s + h * a.sk.h + tok0 * a.sk.t;
     const uint16_t* Vb = static_cast<const uint16_t*>(a.v) + bq * a.sv.s + h * a.sv.h + tok0 * a.sv.t;
     uint16_t* Ob = static_cast<uint16_t*>(a.o) + bq * a.so.s + h * a.so.h + tok0 * a.so.t;
-    float* Ls = lse_s + ((int64_t)b * a.H + h) * a.n;
+    float* Ls = lse_s + ((int64_t)b * a.H + h) * a.n * 2;
     const int32_t sqt = (int32_t)a.sq.t, skt = (int32_t)a.sk.t, svt = (int32_t)a.sv.t;
 
     // Lane constants of the loads: within load j of a 16-row block the lane
@@ -204,18 +243,8 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_kernel(FwdArgs a, float* lse
     };
     auto chunk_store = [&](int32_t c) __attribute__((always_inline)) {
         if (!shs) return;                             // no skip key: the window pass leaves the row alone
-        const float ltot = sl;                        // every lane holds its column's full sum
-        const float inv = 1.0f / ltot;
-        const int32_t row = res + (16 * c + x) * pi;
-        uint16_t* orow = Ob + (int64_t)row * a.so.t;
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) {
-            uint2 w;
-            w.x = cvt_pk_bf16(sacc[bb][0] * inv, sacc[bb][1] * inv);
-            w.y = cvt_pk_bf16(sacc[bb][2] * inv, sacc[bb][3] * inv);
-            *reinterpret_cast<uint2*>(orow + 16 * bb + 4 * g) = w;
-        }
-        if (g == 0) Ls[row] = sm + __log2f(ltot);
+        const int32_t row = res + (16 * c + x) * pi;   // every lane holds its column's full sum sl
+        store_skip_partial<DB>(Ob + (int64_t)row * a.so.t, sacc, 1.0f / sl, sm + __log2f(sl), Ls + 2 * row, g);
     };
     auto unit_compute = [&](int32_t kb, const uint16_t* slot) __attribute__((always_inline)) {
         const uint16_t* Ks = slot + wave * UNIT;
@@ -345,7 +374,7 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
     const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + bq * a.sk.s + h * a.sk.h + tok0 * a.sk.t;
     const uint16_t* Vb = static_cast<const uint16_t*>(a.v) + bq * a.sv.s + h * a.sv.h + tok0 * a.sv.t;
     uint16_t* Ob = static_cast<uint16_t*>(a.o) + bq * a.so.s + h * a.so.h + tok0 * a.so.t;
-    float* Ls = lse_s + ((int64_t)b * a.H + h) * a.n;
+    float* Ls = lse_s + ((int64_t)b * a.H + h) * a.n * 2;
     const int32_t sqt = (int32_t)a.sq.t, skt = (int32_t)a.sk.t, svt = (int32_t)a.sv.t;
     uint16_t* const ws = lds + wave * WSLICE;
 
@@ -468,17 +497,8 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
                 sacc[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[slot][bb], pb, sacc[bb], 0, 0, 0);
         }
         if (!hs) return;
-        const float inv = 1.0f / sl;
         const int32_t row = res + tq * pi;
-        uint16_t* orow = Ob + (int64_t)row * a.so.t;
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) {
-            uint2 w;
-            w.x = cvt_pk_bf16(sacc[bb][0] * inv, sacc[bb][1] * inv);
-            w.y = cvt_pk_bf16(sacc[bb][2] * inv, sacc[bb][3] * inv);
-            *reinterpret_cast<uint2*>(orow + 16 * bb + 4 * g) = w;
-        }
-        if (g == 0) Ls[row] = sm + __log2f(sl);
+        store_skip_partial<DB>(Ob + (int64_t)row * a.so.t, sacc, 1.0f / sl, sm + __log2f(sl), Ls + 2 * row, g);
     };
 
     // entries 0, 1 and the query rows of chunks c0, c0+1 in the order the
@@ -541,7 +561,7 @@ __global__ __launch_bounds__(NT) void fwd_window_kernel(FwdArgs a, const float* 
     const uint16_t* Vb = static_cast<const uint16_t*>(a.v) + bq * a.sv.s + h * a.sv.h + tok0 * a.sv.t;
     uint16_t* Ob = static_cast<uint16_t*>(a.o) + bq * a.so.s + h * a.so.h + tok0 * a.so.t;
     const float* Gb = a.g + bq * a.sg.s + h * a.sg.h + tok0 * a.sg.t;
-    const float* Ls = lse_s ? lse_s + ((int64_t)b * a.H + h) * a.n : nullptr;
+    const float* Ls = lse_s ? lse_s + ((int64_t)b * a.H + h) * a.n * 2 : nullptr;
 
     const int32_t klo = imax32(0, q0 - kw);
     const int32_t khi = imin32(n - 1, q0 + QT - 1 + (BIDIR ? kw : 0));
@@ -716,12 +736,13 @@ __global__ __launch_bounds__(NT) void fwd_window_kernel(FwdArgs a, const float* 
     uint16_t* orow = Ob + (int64_t)i * a.so.t;
     uint2 os[DB];
     if (merge && hs) {
-        const float lsk = Ls[i] + ps;
+        const f32x2_t rec = *reinterpret_cast<const f32x2_t*>(Ls + 2 * i);   // (log2-sum-exp, e)
+        const float lsk = rec[0] + ps;
         const float mx = fmaxf(lw, lsk);
         const float aw = exp2_fast(lw - mx), as = exp2_fast(lsk - mx);
         const float inv = 1.0f / (aw + as);
         fw = ltot > 0.0f ? aw * inv / ltot : 0.0f;     // alpha = 0: the window part is empty
-        fs = as * inv;
+        fs = __builtin_amdgcn_ldexpf(as * inv, (int)rec[1]);   // undo the fp16 scaling
         lfin = mx + __log2f(aw + as);
 #pragma unroll
         for (int bb = 0; bb < DB; ++bb) os[bb] = *reinterpret_cast<const uint2*>(orow + 16 * bb + 4 * g);
@@ -732,8 +753,8 @@ __global__ __launch_bounds__(NT) void fwd_window_kernel(FwdArgs a, const float* 
 #pragma unroll
     for (int bb = 0; bb < DB; ++bb) {
         uint2 w;
-        w.x = cvt_pk_bf16(fmaf(acc[bb][0], fw, bf16lo(os[bb].x) * fs), fmaf(acc[bb][1], fw, bf16hi(os[bb].x) * fs));
-        w.y = cvt_pk_bf16(fmaf(acc[bb][2], fw, bf16lo(os[bb].y) * fs), fmaf(acc[bb][3], fw, bf16hi(os[bb].y) * fs));
+        w.x = cvt_pk_bf16(fmaf(acc[bb][0], fw, f16lo(os[bb].x) * fs), fmaf(acc[bb][1], fw, f16hi(os[bb].x) * fs));
+        w.y = cvt_pk_bf16(fmaf(acc[bb][2], fw, f16lo(os[bb].y) * fs), fmaf(acc[bb][3], fw, f16hi(os[bb].y) * fs));
         *reinterpret_cast<uint2*>(orow + 16 * bb + 4 * g) = w;
     }
     if (a.lse && g == 0) a.lse[bq * a.sg.s + h * a.sg.h + (tok0 + i) * a.sg.t] = lfin * PIATTN_LN2;
@@ -745,7 +766,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     const bool skips = a.pat.M >= mlo;
     float* lse_s = nullptr;
     if (skips) {
-        const size_t bytes = (size_t)a.B * a.H * a.n * sizeof(float);
+        const size_t bytes = (size_t)a.B * a.H * a.n * 2 * sizeof(float);   // (log2-sum-exp, e) per row
         hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&lse_s), bytes, stream);
         if (e != hipSuccess) return e;
         const int32_t rgroups = (imin32(a.pat.pi, a.n) + SW - 1) / SW;
