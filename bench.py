@@ -87,15 +87,15 @@ def algorithmic(w, lengths=None):
 
 
 def traffic_record(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if
-    it was taken on the current kernel sources."""
+    """HBM bytes per step (all kernels of one hot-path pass) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel sources."""
     p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
     if rec.get("kernel_digest") != kernel_digest():
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec.get("hbm_bytes_per_step")
 
 
 def cpu_baseline(w, x, budget_s: float):
@@ -218,37 +218,41 @@ def _counter_rows(d):
 
 
 def _per_dispatch(rows, counter, match):
-    """Median over dispatches of a kernel of the summed counter value."""
+    """Per matching kernel, the median over its dispatches of the summed
+    counter value; returned summed over the kernels (one step launches each
+    matching kernel once), with the number of dispatches and kernel names."""
     import statistics
     per = {}
     for name, cn, val, disp in rows:
         if cn == counter and match(name):
-            per[disp] = per.get(disp, 0.0) + val
+            d = per.setdefault(name, {})
+            d[disp] = d.get(disp, 0.0) + val
     if not per:
         raise SystemExit("no %s dispatch matched" % counter)
-    return statistics.median(per.values()), len(per)
+    total = sum(statistics.median(d.values()) for d in per.values())
+    return total, sum(len(d) for d in per.values()), sorted(per)
 
 
 def pmc_summary(args):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the forward kernel, each
-    scaled by the reading of the same counter on the plain copy, into the
-    HBM bytes per launch that bench.py reports as roofline.traffic."""
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the forward kernels, each
+    scaled by the reading of the same counter on the plain copy, summed over
+    the kernels of one step into the HBM bytes per step that bench.py
+    reports as roofline.traffic."""
     fetch_rows, write_rows = _counter_rows(args.pmc_summary[0]), _counter_rows(args.pmc_summary[1])
     is_fwd = lambda name: "fwd_" in name and "kernel" in name
     is_copy = lambda name: "elementwise" in name and "MulFunctor" in name   # calibrate_copy
-    f_fwd, nf = _per_dispatch(fetch_rows, "FETCH_SIZE", is_fwd)
-    w_fwd, nw = _per_dispatch(write_rows, "WRITE_SIZE", is_fwd)
-    f_cp, _ = _per_dispatch(fetch_rows, "FETCH_SIZE", is_copy)
-    w_cp, _ = _per_dispatch(write_rows, "WRITE_SIZE", is_copy)
+    f_fwd, nf, knames = _per_dispatch(fetch_rows, "FETCH_SIZE", is_fwd)
+    w_fwd, nw, _ = _per_dispatch(write_rows, "WRITE_SIZE", is_fwd)
+    f_cp, _, _ = _per_dispatch(fetch_rows, "FETCH_SIZE", is_copy)
+    w_cp, _, _ = _per_dispatch(write_rows, "WRITE_SIZE", is_copy)
     copy_kib = COPY_ELEMS * 2 / 1024.0
     fs, ws = copy_kib / f_cp, copy_kib / w_cp
-    kname = next(name for name, *_ in fetch_rows if is_fwd(name))
-    rec = {"workload": args.workload, "kernel": kname, "kernel_digest": kernel_digest(),
-           "fetch_kib_per_dispatch": f_fwd, "write_kib_per_dispatch": w_fwd,
+    rec = {"workload": args.workload, "kernels": knames, "kernel_digest": kernel_digest(),
+           "fetch_kib_per_step": f_fwd, "write_kib_per_step": w_fwd,
            "dispatches": [nf, nw],
            "copy_kib_each_way": copy_kib, "copy_fetch_kib": f_cp, "copy_write_kib": w_cp,
            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
-           "hbm_bytes_per_launch": int(round((f_fwd * fs + w_fwd * ws) * 1024))}
+           "hbm_bytes_per_step": int(round((f_fwd * fs + w_fwd * ws) * 1024))}
     out = os.path.join(ROOT, "profiles", "traffic_%s.json" % args.workload)
     json.dump(rec, open(out, "w"), indent=1)
     print(json.dumps(rec))
