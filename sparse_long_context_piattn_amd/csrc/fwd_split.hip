@@ -641,6 +641,21 @@ __global__ __launch_bounds__(NT) void fwd_window_kernel(FwdArgs a, const float* 
     }
     lds_barrier();                                       // slot 2 is free for tile 2
 
+    // the skip partial of the lane's row (written by the skip pass), loaded
+    // now so that its latency hides behind the window loop
+    const bool mg = merge && hs && qv;
+    uint16_t* orow = Ob + (int64_t)ic * a.so.t;
+    uint2 os[DB];
+    f32x2_t rec = {0.0f, 0.0f};                          // (log2-sum-exp, e)
+    if (mg) {
+        rec = *reinterpret_cast<const f32x2_t*>(Ls + 2 * ic);
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) os[bb] = *reinterpret_cast<const uint2*>(orow + 16 * bb + 4 * g);
+    } else {
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) os[bb] = make_uint2(0, 0);
+    }
+
     f32x4_t acc[DB];
 #pragma unroll
     for (int bb = 0; bb < DB; ++bb) acc[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -733,10 +748,7 @@ __global__ __launch_bounds__(NT) void fwd_window_kernel(FwdArgs a, const float* 
     if (!qv) return;
     const float lw = mrun + __log2f(ltot);              // log2-sum-exp of the window part
     float fw = 1.0f / ltot, fs = 0.0f, lfin = lw;
-    uint16_t* orow = Ob + (int64_t)i * a.so.t;
-    uint2 os[DB];
-    if (merge && hs) {
-        const f32x2_t rec = *reinterpret_cast<const f32x2_t*>(Ls + 2 * i);   // (log2-sum-exp, e)
+    if (mg) {
         const float lsk = rec[0] + ps;
         const float mx = fmaxf(lw, lsk);
         const float aw = exp2_fast(lw - mx), as = exp2_fast(lsk - mx);
@@ -744,11 +756,6 @@ __global__ __launch_bounds__(NT) void fwd_window_kernel(FwdArgs a, const float* 
         fw = ltot > 0.0f ? aw * inv / ltot : 0.0f;     // alpha = 0: the window part is empty
         fs = __builtin_amdgcn_ldexpf(as * inv, (int)rec[1]);   // undo the fp16 scaling
         lfin = mx + __log2f(aw + as);
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) os[bb] = *reinterpret_cast<const uint2*>(orow + 16 * bb + 4 * g);
-    } else {
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) os[bb] = make_uint2(0, 0);
     }
 #pragma unroll
     for (int bb = 0; bb < DB; ++bb) {
