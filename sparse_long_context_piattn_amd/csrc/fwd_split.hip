@@ -329,22 +329,24 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_kernel(FwdArgs a, float* lse
     __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));       // reloads past the end land before the LDS retires
 }
 
-// Register-ring variant of the skip pass for head dim 64 and short bands
-// (NK = NBL+1, or 2 NBL+1 bidirectional, <= 5 blocks).  The key blocks of a
+// Register-ring variant of the skip pass for short bands (NK = NBL+1, or
+// 2 NBL+1 bidirectional, <= 5 blocks).  The key blocks of a
 // residue form a stream: entry j is block j - NBL, chunk c uses entries
 // c .. c+NK-1, and each chunk adds exactly one.  Every entry is staged into
 // LDS once (two entries ahead), then its MFMA operands -- the K chunks and
 // the transposed V^T chunks -- are read into a ring of NK register sets and
 // reused by all NK chunks that need them, so K and V are fetched once per
 // residue instead of NK times.  The loop starts NK-1 "virtual" chunks early,
-// which only fill the ring.
-template <int NBL, bool BIDIR>
+// which only fill the ring.  At head dim 128 a ring of five entries takes
+// 160 registers per lane and a wave's LDS slice 32 KB: one wave per SIMD,
+// its loads two entries deep.
+template <int D, int NBL, bool BIDIR>
 __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float* lse_s, int32_t rgroups,
                                                                 int32_t total) {
-    constexpr int D = 64;
     using G = Geo<D>;
     constexpr int DC = G::DC, DB = G::DB, CH = G::CH, RPI = G::RPI;
     constexpr int NK = BIDIR ? 2 * NBL + 1 : NBL + 1;
+    constexpr int LPB = 16 / RPI;                        // 1 KB loads per 16-row block
     constexpr int BLK = 32 * D;                          // elements of one staged entry: 16 K + 16 V rows
     constexpr int QR = 16 * D;                           // elements of one chunk's query rows
     constexpr int WSLICE = 3 * BLK + 2 * QR;             // per wave: 3 entry slots, 2 query slots
@@ -395,13 +397,13 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
             dma16(ub, off * 2u, lds_addr(dst + j * RPI * D));
         }
     };
-    // stream entry j (block j - NBL) into entry slot j % 3: 4 loads
+    // stream entry j (block j - NBL) into entry slot j % 3: 2 blocks
     auto issue_entry = [&](int32_t j) __attribute__((always_inline)) {
         uint16_t* d = ws + (((j % 3) + 3) % 3) * BLK;
         load_rows(Kb, skt, 16 * (j - NBL), d);
         load_rows(Vb, svt, 16 * (j - NBL), d + 16 * D);
     };
-    // query rows of chunk c (clamped into the residue) into query slot c % 2: 2 loads
+    // query rows of chunk c (clamped into the residue) into query slot c % 2: 1 block
     auto issue_q = [&](int32_t c) __attribute__((always_inline)) {
         load_rows(Qb, sqt, 16 * imin32(imax32(c, 0), nch - 1), ws + 3 * BLK + (c & 1) * QR);
     };
@@ -427,8 +429,8 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
         constexpr int RS = decltype(rsc)::value;
         const int32_t e = c + NK - 1;
         // entry e and the query rows of chunk c have landed: after them only
-        // entry e+1 and the query rows of chunk c+1 were issued (4 + 2 loads)
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(6));
+        // entry e+1 and the query rows of chunk c+1 were issued (2 + 1 blocks)
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(3 * LPB));
         {
             const uint16_t* es = ws + ((e % 3 + 3) % 3) * BLK;
 #pragma unroll
@@ -783,12 +785,12 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
             return hipErrorInvalidConfiguration;
         }
         const int32_t nbl = (a.pat.M + 15) / 16;
-        if (D == 64 && nbl <= (BIDIR ? 2 : 4)) {
+        if (nbl <= (BIDIR ? 2 : 4)) {
             // short bands: every key block staged once per residue (register ring)
-            auto ring = nbl == 1 ? fwd_skip_ring_kernel<1, BIDIR>
-                      : nbl == 2 ? fwd_skip_ring_kernel<2, BIDIR>
-                      : nbl == 3 ? fwd_skip_ring_kernel<BIDIR ? 2 : 3, BIDIR>
-                                 : fwd_skip_ring_kernel<BIDIR ? 2 : 4, BIDIR>;
+            auto ring = nbl == 1 ? fwd_skip_ring_kernel<D, 1, BIDIR>
+                      : nbl == 2 ? fwd_skip_ring_kernel<D, 2, BIDIR>
+                      : nbl == 3 ? fwd_skip_ring_kernel<D, BIDIR ? 2 : 3, BIDIR>
+                                 : fwd_skip_ring_kernel<D, BIDIR ? 2 : 4, BIDIR>;
             hipLaunchKernelGGL(ring, dim3((uint32_t)total), dim3(SW * 64), 0, stream, a, lse_s, rgroups,
                                (int32_t)total);
         } else {

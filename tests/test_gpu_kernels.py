@@ -63,6 +63,10 @@ CASES = [
     ("d128_bidir", 1, 2, 3000, 128, 24, 128, 9, True),
     ("d128_no_skips", 1, 2, 1000, 128, 50, 128, 0, False),
     ("d128_short_n", 1, 2, 50, 128, 10, 16, 4, False),
+    ("d128_M40", 1, 2, 6000, 128, 64, 64, 40, False),
+    ("d128_M64_pi256", 1, 1, 20000, 128, 128, 256, 64, False),
+    ("d128_bidir_M30", 1, 2, 4000, 128, 40, 64, 30, True),
+    ("d128_bidir_M12", 1, 2, 3100, 128, 20, 96, 12, True),
 ]
 
 
