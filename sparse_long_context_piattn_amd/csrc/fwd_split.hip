@@ -521,17 +521,34 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
 }
 
 // =============================================================== window pass
-constexpr int QT = 128;                  // query rows per workgroup (8 waves x 16)
-constexpr int KT = 64;                   // key rows per LDS slot
+
+// Window-pass shape: WW waves of 16 query rows (a 64-row tile), KT key rows
+// per LDS slot.  Small workgroups with small slots keep several tiles in
+// flight per CU, each at a different point of its load / compute cycle:
+// 24 KB of LDS at d = 64 (four workgroups per CU, the register budget set
+// for four waves per SIMD), 48 KB at d = 128 (three per CU).  A 128-row
+// tile with 64-key slots, which halves the halo re-reads, measured slower
+// at both head dims: 97 KB of LDS at d = 128 allow one workgroup per CU,
+// whose loads then stall at every tile start.
+template <int D>
+struct WinShape {
+    static constexpr int WW = 4;
+    static constexpr int KT = 32;
+    static constexpr int QTW = 16 * WW;
+    static constexpr int EU = D == 64 ? 4 : 3;           // waves per SIMD the register budget must allow
+};
 
 template <int D, bool BIDIR>
-__global__ __launch_bounds__(NT) void fwd_window_kernel(FwdArgs a, const float* lse_s, int32_t q_tiles,
-                                                        int32_t total, int32_t merge) {
+__global__ __launch_bounds__(WinShape<D>::WW * 64, WinShape<D>::EU) void fwd_window_kernel(FwdArgs a, const float* lse_s,
+                                                                        int32_t q_tiles, int32_t total,
+                                                                        int32_t merge) {
     using G = Geo<D>;
     constexpr int DC = G::DC, DB = G::DB, CH = G::CH, RPI = G::RPI;
-    constexpr int LPW = KT / RPI / (NW / 2);            // loads per wave per slot (waves 0-3 K, 4-7 V)
-    static_assert(KT % (RPI * (NW / 2)) == 0, "slot split");
-    static_assert(2 * KT >= QT, "query rows are staged through one slot pair");
+    constexpr int WW = WinShape<D>::WW, KT = WinShape<D>::KT, QT = WinShape<D>::QTW, NB = KT / 16;
+    constexpr int LPW = KT / RPI / (WW / 2);            // loads per wave per slot (first half K, second V)
+    static_assert(KT % (RPI * (WW / 2)) == 0, "slot split");
+    static_assert(2 * KT == QT, "query rows are staged through one slot pair");
+    static_assert(NB % 2 == 0, "PV runs on pairs of 16-key blocks");
     __shared__ __attribute__((aligned(16))) uint16_t k0s[KT * D];
     __shared__ __attribute__((aligned(16))) uint16_t k1s[KT * D];
     __shared__ __attribute__((aligned(16))) uint16_t k2s[KT * D];
@@ -571,7 +588,7 @@ __global__ __launch_bounds__(NT) void fwd_window_kernel(FwdArgs a, const float* 
 
     // ---- staging: slot rows r0 .. r0+RPI-1 per load; lane row r0 + lane/CH,
     // physical chunk lane%CH = logical chunk (lane%CH) ^ (row%8)
-    const bool isv = wave >= NW / 2;
+    const bool isv = wave >= WW / 2;
     const uint16_t* src0 = isv ? Vb : Kb;
     const int32_t st = isv ? (int32_t)a.sv.t : (int32_t)a.sk.t;
     auto stage_rows = [&](const uint16_t* src, int32_t stt, int32_t s0, int r0, uint16_t* dst) __attribute__((always_inline)) {
@@ -587,7 +604,7 @@ __global__ __launch_bounds__(NT) void fwd_window_kernel(FwdArgs a, const float* 
         t = imin32(t, ntiles - 1);                       // past the last tile: harmless reload
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
-            const int r0 = ((wave % (NW / 2)) * LPW + j) * RPI;
+            const int r0 = ((wave % (WW / 2)) * LPW + j) * RPI;
             stage_rows(src0, st, klo + t * KT + r0, r0, isv ? Vs : Ks);
         }
     };
@@ -598,13 +615,15 @@ __global__ __launch_bounds__(NT) void fwd_window_kernel(FwdArgs a, const float* 
     {
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
-            const int r0 = ((wave % (NW / 2)) * LPW + j) * RPI;
+            const int r0 = ((wave % (WW / 2)) * LPW + j) * RPI;
             stage_rows(Qb, (int32_t)a.sq.t, q0 + (isv ? KT : 0) + r0, r0, isv ? v2s : k2s);
         }
         if (wave == 0) {
-            const int32_t rr = imin32(q0 + lane, n - 1), rr2 = imin32(q0 + 64 + lane, n - 1);
-            dma4(Gb, (uint32_t)(rr * (int32_t)a.sg.t) * 4u, lds_addr(gls));
-            dma4(Gb, (uint32_t)(rr2 * (int32_t)a.sg.t) * 4u, lds_addr(gls + 64));
+#pragma unroll
+            for (int j = 0; j < QT / 64; ++j) {
+                const int32_t rr = imin32(q0 + 64 * j + lane, n - 1);
+                dma4(Gb, (uint32_t)(rr * (int32_t)a.sg.t) * 4u, lds_addr(gls + 64 * j));
+            }
         }
     }
     issue(k1s, v1s, 1);
@@ -634,7 +653,7 @@ __global__ __launch_bounds__(NT) void fwd_window_kernel(FwdArgs a, const float* 
     bf16x8_t qf[DC];
     float pl, ps;
     {
-        const int qr = 16 * wave + x;                   // slot 2 holds rows 0-63 in K, 64-127 in V
+        const int qr = 16 * wave + x;                   // slot 2 holds rows 0..KT-1 in K, the rest in V
         const uint16_t* qsrc = qr < KT ? k2s : v2s;
         const int rr = qr & (KT - 1);
 #pragma unroll
@@ -666,11 +685,11 @@ __global__ __launch_bounds__(NT) void fwd_window_kernel(FwdArgs a, const float* 
     auto compute = [&](int32_t t, const uint16_t* Ks, const uint16_t* Vs) __attribute__((always_inline)) {
         const int32_t kt0 = klo + t * KT;
         if (kt0 > whi || kt0 + KT - 1 < wlo) return;    // wave-uniform
-        float sc[4][4];
-        bool act[4];
+        float sc[NB][4];
+        bool act[NB];
         float mx = -INFINITY;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < NB; ++u) {
             const int32_t kb0 = kt0 + 16 * u;
             act[u] = kb0 <= whi && kb0 + 15 >= wlo;     // wave-uniform
 #pragma unroll
@@ -700,16 +719,16 @@ __global__ __launch_bounds__(NT) void fwd_window_kernel(FwdArgs a, const float* 
             mL = mnew + LAZY;
             cst = pl - mu;
         }
-        s16x4_t pb[4];
+        s16x4_t pb[NB];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < NB; ++u) {
             const uint32_t w0 = cvt_pk_bf16(exp2_fast(fmaf(sc[u][0], sl2, cst)), exp2_fast(fmaf(sc[u][1], sl2, cst)));
             const uint32_t w1 = cvt_pk_bf16(exp2_fast(fmaf(sc[u][2], sl2, cst)), exp2_fast(fmaf(sc[u][3], sl2, cst)));
             pb[u] = __builtin_bit_cast(s16x4_t, make_uint2(w0, w1));
         }
         f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int u = 0; u < 4; u += 2) {
+        for (int u = 0; u < NB; u += 2) {
             if (!act[u] && !act[u + 1]) continue;
             const bf16x8_t pp =
                 __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(pb[u], pb[u + 1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -803,14 +822,15 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
             return e;
         }
     }
-    const int32_t q_tiles = (a.n + QT - 1) / QT;
+    constexpr int QTW = WinShape<D>::QTW;
+    const int32_t q_tiles = (a.n + QTW - 1) / QTW;
     const int64_t total = (int64_t)q_tiles * a.H * a.B;
     hipError_t e = hipSuccess;
     if (total > 0x7fffffff) {
         e = hipErrorInvalidConfiguration;
     } else {
-        hipLaunchKernelGGL((fwd_window_kernel<D, BIDIR>), dim3((uint32_t)total), dim3(NT), 0, stream, a, lse_s,
-                           q_tiles, (int32_t)total, skips ? 1 : 0);
+        hipLaunchKernelGGL((fwd_window_kernel<D, BIDIR>), dim3((uint32_t)total), dim3(WinShape<D>::WW * 64), 0,
+                           stream, a, lse_s, q_tiles, (int32_t)total, skips ? 1 : 0);
         e = hipGetLastError();
     }
     if (lse_s) {
@@ -830,7 +850,8 @@ bool fwd_split_supported(int dtype, const FwdArgs& a) {
     ts = ts > a.sq.t ? ts : a.sq.t;
     ts = ts > 2 * a.sg.t ? ts : 2 * a.sg.t;            // the gate's byte offsets are twice as large
     const int64_t span = (int64_t)a.n + 16LL * a.pat.pi + a.d;
-    return span * ts < ((int64_t)1 << 31) && (int64_t)a.n + 2LL * a.pat.k + QT < ((int64_t)1 << 30);
+    return span * ts < ((int64_t)1 << 31) &&
+           (int64_t)a.n + 2LL * a.pat.k + WinShape<64>::QTW < ((int64_t)1 << 30);
 }
 
 hipError_t launch_fwd_split(const FwdArgs& a, hipStream_t stream) {
