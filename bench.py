@@ -321,12 +321,17 @@ def main():
     sets = [wl.make_fwd_inputs(w, device=dev, seed=w.seed + s, lengths=lengths)
             for s in range(nsets)]
     outs = [torch.empty_like(x["q"]) for x in sets]
+    # one workspace for every step (the steps are ordered on one stream)
+    nb = pa.fwd_workspace_bytes(1 if w.dtype == "bf16" else 0, len(lengths) if lengths else w.B, w.H,
+                                max(lengths) if lengths else w.n, w.d,
+                                pa.make_pattern(w.k, w.pi, w.M, w.bidir, w.scale))
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
 
     def step(j):
         x = sets[j % nsets]
         pa.fwd(x["q"], x["k"], x["v"], x["g"], window_k=w.k, period_pi=w.pi, num_skips=w.M,
                bidirectional=w.bidir, cu_seqlens=x.get("cu_seqlens"),
-               max_seqlen=max(lengths) if lengths else None, out=outs[j % nsets])
+               max_seqlen=max(lengths) if lengths else None, out=outs[j % nsets], workspace=ws)
 
     ms_per_step = timed(step, args, dev)
     if args.calibrate_copy:

@@ -25,11 +25,9 @@
  *     piattn_pattern struct is host memory, read during the call only.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and the call returns without synchronising.  The library keeps no
- *     state besides a thread-local error string and allocates no memory,
- *     with one exception: piattn_fwd on its bf16 d = 64 / 128 path takes a
- *     stream-ordered temporary of B*H*n floats (hipMallocAsync, released
- *     with hipFreeAsync on `stream`) for the per-row log-sum-exp that its
- *     skip pass hands to its window pass.
+ *     state besides a thread-local error string and allocates no memory:
+ *     scratch space is a caller-provided workspace (see the *_workspace_bytes
+ *     queries).
  *   - Every argument is validated before anything is launched.  A non-zero
  *     status is returned on error and piattn_last_error() describes it.
  *     Nothing aborts and nothing throws across the ABI.
@@ -54,7 +52,7 @@ enum {
     PIATTN_OK = 0,
     PIATTN_EINVAL = 1,       /* bad pointer, size, stride, alignment or pattern */
     PIATTN_EUNSUPPORTED = 2, /* valid request this build does not implement */
-    PIATTN_EWORKSPACE = 3,   /* decode workspace missing or too small */
+    PIATTN_EWORKSPACE = 3,   /* workspace missing or too small */
     PIATTN_EHIP = 4          /* the HIP runtime reported a launch error */
 };
 
@@ -99,13 +97,33 @@ typedef struct {
  * v, out pointers are 16-byte aligned and their strides multiples of 8
  * elements; for PIATTN_F32, 16-byte aligned and multiples of 4 elements.
  * The output must not alias an input.  Indices must fit in int64.
- * Returns PIATTN_OK, PIATTN_EINVAL, PIATTN_EUNSUPPORTED or PIATTN_EHIP.
+ *
+ * workspace: device scratch of at least piattn_fwd_workspace_bytes(dtype, B,
+ * H, n, d, pattern) bytes, 256-byte aligned; may be NULL when that is 0.
+ * The bf16 d = 64 / 128 path splits the work into a skip pass and a window
+ * pass and hands one (log-sum-exp, exponent) float pair per row from the
+ * first to the second through it.  Calls that share a workspace must be
+ * ordered (the same stream, or synchronised); its contents are scratch
+ * before and after a call.
+ * Returns PIATTN_OK, PIATTN_EINVAL, PIATTN_EUNSUPPORTED, PIATTN_EWORKSPACE
+ * (workspace NULL or too small) or PIATTN_EHIP.
  */
 int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d,
                const void *q, const void *k, const void *v,
                const float *gate_logits, void *out, float *lse_out,
                const int64_t strides[5][3], const int32_t *cu_seqlens,
-               const piattn_pattern *pattern, void *stream);
+               const piattn_pattern *pattern, void *workspace,
+               size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace piattn_fwd needs for these sizes and pattern: 8*B*H*n bytes for
+ * PIATTN_BF16 with d in {64, 128} when the pattern has skip keys
+ * (num_skips_M > window_k / period_pi), else 0.  0 also for invalid
+ * arguments (piattn_fwd reports those).
+ */
+size_t piattn_fwd_workspace_bytes(piattn_dtype dtype, int32_t B, int32_t H,
+                                  int32_t n, int32_t d,
+                                  const piattn_pattern *pattern);
 
 /*
  * piattn_decode -- one new query per sequence against its KV cache (the

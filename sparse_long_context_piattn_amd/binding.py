@@ -21,7 +21,7 @@ PIATTN_F32, PIATTN_BF16 = 0, 1
 STATUS = {0: "PIATTN_OK", 1: "PIATTN_EINVAL", 2: "PIATTN_EUNSUPPORTED", 3: "PIATTN_EWORKSPACE",
           4: "PIATTN_EHIP"}
 
-EXPORTS = ["piattn_fwd", "piattn_decode", "piattn_decode_workspace_bytes",
+EXPORTS = ["piattn_fwd", "piattn_fwd_workspace_bytes", "piattn_decode", "piattn_decode_workspace_bytes",
            "piattn_decode_auto_splits", "piattn_neighbors", "piattn_neighbors_cap",
            "piattn_last_error", "piattn_version"]
 
@@ -54,8 +54,10 @@ def lib():
         vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
         pat = ctypes.POINTER(Pattern)
         L.piattn_fwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
-                                 ctypes.POINTER(Strides), vp, pat, vp]
+                                 ctypes.POINTER(Strides), vp, pat, vp, sz, vp]
         L.piattn_fwd.restype = ctypes.c_int
+        L.piattn_fwd_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, pat]
+        L.piattn_fwd_workspace_bytes.restype = sz
         L.piattn_decode.argtypes = [ctypes.c_int, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp,
                                     ctypes.POINTER(Strides), pat, i32, vp, sz, vp]
         L.piattn_decode.restype = ctypes.c_int
@@ -106,15 +108,22 @@ def _need_cuda(*ts):
             raise ValueError("tensors must live on the GPU")
 
 
+def fwd_workspace_bytes(dtype_code: int, B: int, H: int, n: int, d: int, pattern: Pattern) -> int:
+    return int(lib().piattn_fwd_workspace_bytes(dtype_code, B, H, n, d, ctypes.byref(pattern)))
+
+
 def fwd(q, k, v, g, *, window_k: int, period_pi: int, num_skips: int, bidirectional=False,
         scale: float = 0.0, cu_seqlens=None, max_seqlen: int | None = None, out=None,
-        lse=None):
+        lse=None, workspace=None):
     """pi-Attention prefill.
 
     Dense: q, k, v [B, H, n, d] (any strides, last dim contiguous), g [B, H, n].
     Varlen: q, k, v [T, H, d], g [T, H], cu_seqlens int32 [B + 1] on the GPU.
     Returns out (same shape and dtype as q); lse, if given, is written with
-    the natural-log normaliser of each row (shape of g, fp32).
+    the natural-log normaliser of each row (shape of g, fp32).  workspace, if
+    given, is a uint8 device tensor of at least fwd_workspace_bytes(...)
+    bytes; otherwise one is taken from torch's allocator on the current
+    stream for the call.
     """
     code = _dtype_code(q)
     _need_cuda(q, k, v, g, out, lse, cu_seqlens)
@@ -166,9 +175,14 @@ def fwd(q, k, v, g, *, window_k: int, period_pi: int, num_skips: int, bidirectio
             raise ValueError("the head dimension must be contiguous")
     strides = Strides(*[x for s in st4 for x in s], *gst)
     pat = make_pattern(window_k, period_pi, num_skips, bidirectional, scale)
+    need = fwd_workspace_bytes(code, B, H, n, d, pat)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _need_cuda(workspace)
+    wbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     rc = lib().piattn_fwd(code, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out),
                           _ptr(lse), ctypes.byref(strides), cu_ptr, ctypes.byref(pat),
-                          ctypes.c_void_p(_stream(q.device)))
+                          _ptr(workspace), wbytes, ctypes.c_void_p(_stream(q.device)))
     _check(rc)
     return out
 

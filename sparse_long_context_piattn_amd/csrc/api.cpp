@@ -126,10 +126,26 @@ int piattn_neighbors(int32_t n, const piattn_pattern* pattern, int32_t q_begin, 
                                           static_cast<hipStream_t>(stream)));
 }
 
+// Workspace of the split prefill path: one (log2-sum-exp, exponent) float
+// pair per row, written by its skip pass and read by its window pass.  Only
+// bf16 at d = 64 / 128 with a non-empty skip set can take that path.
+static size_t fwd_split_workspace(int dtype, int32_t B, int32_t H, int32_t n, int32_t d, const PiPattern& p) {
+    if (dtype != PIATTN_BF16 || (d != 64 && d != 128)) return 0;
+    if (p.M < p.k / p.pi + 1) return 0;
+    return (size_t)B * H * n * 2 * sizeof(float);
+}
+
+size_t piattn_fwd_workspace_bytes(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d,
+                                  const piattn_pattern* pattern) {
+    PiPattern p;
+    if (check_pattern(pattern, &p) != PIATTN_OK || B < 1 || H < 1 || n < 1) return 0;
+    return fwd_split_workspace(dtype, B, H, n, d, p);
+}
+
 int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, const void* q,
                const void* k, const void* v, const float* gate_logits, void* out, float* lse_out,
                const int64_t strides[5][3], const int32_t* cu_seqlens,
-               const piattn_pattern* pattern, void* stream) {
+               const piattn_pattern* pattern, void* workspace, size_t workspace_bytes, void* stream) {
     if (dtype != PIATTN_F32 && dtype != PIATTN_BF16)
         return fail(PIATTN_EINVAL, "dtype=%d is not PIATTN_F32 or PIATTN_BF16", (int)dtype);
     PiPattern p;
@@ -182,14 +198,25 @@ int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
     // Kernel choice.  PIATTN_FWD_KERNEL = split | resid | gather forces
     // one kernel (testing and measurement; EUNSUPPORTED if it cannot take the
     // call); unset or "auto" picks the first that can.
+    // The split path checks the workspace first (the other kernels take none).
+    auto split = [&]() -> int {
+        const size_t need = fwd_split_workspace(dtype, B, H, n, d, p);
+        if (need) {
+            if (!workspace) return fail(PIATTN_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+            if (workspace_bytes < need)
+                return fail(PIATTN_EWORKSPACE, "workspace of %zu bytes is smaller than %zu", workspace_bytes, need);
+            if (!aligned(workspace, 256)) return fail(PIATTN_EINVAL, "workspace is not 256-byte aligned");
+        }
+        return launch_status(launch_fwd_split(a, need ? static_cast<float*>(workspace) : nullptr, st));
+    };
     const char* force = getenv("PIATTN_FWD_KERNEL");
     if (force && *force && strcmp(force, "auto") != 0) {
         if (!strcmp(force, "resid") && fwd_resid_supported(dt, a)) return launch_status(launch_fwd_resid(a, st));
-        if (!strcmp(force, "split") && fwd_split_supported(dt, a)) return launch_status(launch_fwd_split(a, st));
+        if (!strcmp(force, "split") && fwd_split_supported(dt, a)) return split();
         if (!strcmp(force, "gather")) return launch_status(launch_fwd_gather(dt, a, st));
         return fail(PIATTN_EUNSUPPORTED, "PIATTN_FWD_KERNEL=%s cannot take this call", force);
     }
-    if (fwd_split_supported(dt, a)) return launch_status(launch_fwd_split(a, st));
+    if (fwd_split_supported(dt, a)) return split();
     if (fwd_resid_supported(dt, a)) return launch_status(launch_fwd_resid(a, st));
     return launch_status(launch_fwd_gather(dt, a, st));
 }

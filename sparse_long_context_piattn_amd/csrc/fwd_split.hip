@@ -11,13 +11,15 @@
 // slice with LDS-direct loads, several units ahead, and runs S^T = K Q^T, the
 // band mask, an online softmax and O^T += V^T P^T.  At the end of a chunk it
 // writes the normalised skip partial O_s (fp16, scaled) into the output rows
-// and its log-sum-exp (log2 units, without the gate prior) into a temporary.
-// Each key block is staged NK times per residue instead of once per query.
+// and its log-sum-exp (log2 units, without the gate prior) into the caller's
+// workspace.  For short bands (NK <= 5) each key block is staged once per
+// residue and its operands reused from a register ring; otherwise it is
+// staged NK times.
 //
 // Window pass ("Ring-Local Attention" + "Dynamic Adaptive Fusion").  A
-// workgroup takes 128 consecutive query rows of one (sequence, head); the
+// workgroup takes 64 consecutive query rows of one (sequence, head); the
 // keys [i-k, i] (bidirectional [i-k, i+k]) of all its rows stream through a
-// ring of three LDS slots of 64 rows, two slots ahead of the compute.  Each
+// ring of three LDS slots of 32 rows, two slots ahead of the compute.  Each
 // wave owns 16 rows: S^T = K Q^T on v_mfma_f32_16x16x32_bf16, window mask,
 // log(alpha) prior, online softmax, O^T += V^T P^T.  In the epilogue, rows
 // that have skip keys combine their window partial with the skip partial
@@ -87,7 +89,7 @@ __device__ __forceinline__ int32_t xcd_logical(int32_t hw, int32_t total) {
 // 2^-e, e chosen from the row's largest magnitude m so that m 2^-e lies in
 // [2^14, 2^15): no overflow, full fp16 precision (4x that of bf16, so the
 // merge adds well under a quarter ulp of the final bf16 rounding).  Its
-// log2-sum-exp and e go into the row's two-float record of the temporary.
+// log2-sum-exp and e go into the row's two-float record of the workspace.
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t cvt_pk_f16(float lo, float hi) {
@@ -788,21 +790,17 @@ __global__ __launch_bounds__(WinShape<D>::WW * 64, WinShape<D>::EU) void fwd_win
     if (a.lse && g == 0) a.lse[bq * a.sg.s + h * a.sg.h + (tok0 + i) * a.sg.t] = lfin * PIATTN_LN2;
 }
 
+// lse_s: the caller's workspace of B*H*n (log2-sum-exp, e) float pairs, or
+// null when the pattern has no skip keys.
 template <int D, bool BIDIR>
-hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_t(const FwdArgs& a, float* lse_s, hipStream_t stream) {
     const int32_t mlo = a.pat.k / a.pat.pi + 1;
     const bool skips = a.pat.M >= mlo;
-    float* lse_s = nullptr;
     if (skips) {
-        const size_t bytes = (size_t)a.B * a.H * a.n * 2 * sizeof(float);   // (log2-sum-exp, e) per row
-        hipError_t e = hipMallocAsync(reinterpret_cast<void**>(&lse_s), bytes, stream);
-        if (e != hipSuccess) return e;
+        if (!lse_s) return hipErrorInvalidValue;
         const int32_t rgroups = (imin32(a.pat.pi, a.n) + SW - 1) / SW;
         const int64_t total = (int64_t)rgroups * a.H * a.B;
-        if (total > 0x7fffffff) {
-            (void)hipFreeAsync(lse_s, stream);
-            return hipErrorInvalidConfiguration;
-        }
+        if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
         const int32_t nbl = (a.pat.M + 15) / 16;
         if (nbl <= (BIDIR ? 2 : 4)) {
             // short bands: every key block staged once per residue (register ring)
@@ -816,11 +814,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
             hipLaunchKernelGGL((fwd_skip_kernel<D, BIDIR>), dim3((uint32_t)total), dim3(SW * 64), 0, stream, a,
                                lse_s, rgroups, (int32_t)total);
         }
-        e = hipGetLastError();
-        if (e != hipSuccess) {
-            (void)hipFreeAsync(lse_s, stream);
-            return e;
-        }
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
     }
     constexpr int QTW = WinShape<D>::QTW;
     const int32_t q_tiles = (a.n + QTW - 1) / QTW;
@@ -830,12 +825,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
         e = hipErrorInvalidConfiguration;
     } else {
         hipLaunchKernelGGL((fwd_window_kernel<D, BIDIR>), dim3((uint32_t)total), dim3(WinShape<D>::WW * 64), 0,
-                           stream, a, lse_s, q_tiles, (int32_t)total, skips ? 1 : 0);
+                           stream, a, skips ? lse_s : nullptr, q_tiles, (int32_t)total, skips ? 1 : 0);
         e = hipGetLastError();
-    }
-    if (lse_s) {
-        const hipError_t f = hipFreeAsync(lse_s, stream);
-        if (e == hipSuccess) e = f;
     }
     return e;
 }
@@ -854,7 +845,7 @@ bool fwd_split_supported(int dtype, const FwdArgs& a) {
            (int64_t)a.n + 2LL * a.pat.k + WinShape<64>::QTW < ((int64_t)1 << 30);
 }
 
-hipError_t launch_fwd_split(const FwdArgs& a, hipStream_t stream) {
-    if (a.d == 64) return a.pat.bidir ? launch_t<64, true>(a, stream) : launch_t<64, false>(a, stream);
-    return a.pat.bidir ? launch_t<128, true>(a, stream) : launch_t<128, false>(a, stream);
+hipError_t launch_fwd_split(const FwdArgs& a, float* ws, hipStream_t stream) {
+    if (a.d == 64) return a.pat.bidir ? launch_t<64, true>(a, ws, stream) : launch_t<64, false>(a, ws, stream);
+    return a.pat.bidir ? launch_t<128, true>(a, ws, stream) : launch_t<128, false>(a, ws, stream);
 }

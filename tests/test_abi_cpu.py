@@ -56,12 +56,12 @@ def _strides(vals=None):
 
 
 def _fwd(dtype=1, B=1, H=1, n=64, d=64, q=A, k=A2, v=A3, g=A, out=OUT, lse=None,
-         strides=None, cu=None, pat=None):
+         strides=None, cu=None, pat=None, ws=None, wsb=0):
     L = pa.lib()
     st = strides if strides is not None else _strides()
     p = pat if pat is not None else pa.make_pattern(4, 16, 2)
     rc = L.piattn_fwd(dtype, B, H, n, d, q, k, v, g, out, lse, ctypes.byref(st), cu,
-                      ctypes.byref(p), None)
+                      ctypes.byref(p), ws, wsb, None)
     return rc, L.piattn_last_error().decode()
 
 
@@ -84,6 +84,10 @@ def _fwd(dtype=1, B=1, H=1, n=64, d=64, q=A, k=A2, v=A3, g=A, out=OUT, lse=None,
     (dict(pat=binding.Pattern(4, 16, 2, 0, float("nan"))), EINVAL),
     (dict(strides=_strides([8 * 64 * 64, 64 * 64, 60] * 4 + [64, 64, 1])), EINVAL),
     (dict(strides=_strides([-64, 64 * 64, 64] * 4 + [64, 64, 1])), EINVAL),
+    # the split path (bf16, d = 64, skips) needs 8 bytes per row of workspace
+    (dict(ws=None), EWORKSPACE),
+    (dict(ws=ctypes.c_void_p(1 << 24), wsb=8 * 64 - 1), EWORKSPACE),
+    (dict(ws=ctypes.c_void_p((1 << 24) + 16), wsb=8 * 64), EINVAL),   # not 256-aligned
 ])
 def test_fwd_rejects_bad_arguments(kw, expect):
     rc, msg = _fwd(**kw)
@@ -93,8 +97,23 @@ def test_fwd_rejects_bad_arguments(kw, expect):
 def test_fwd_strides_null_rejected():
     L = pa.lib()
     p = pa.make_pattern(4, 16, 2)
-    rc = L.piattn_fwd(1, 1, 1, 64, 64, A, A2, A3, A, OUT, None, None, None, ctypes.byref(p), None)
+    rc = L.piattn_fwd(1, 1, 1, 64, 64, A, A2, A3, A, OUT, None, None, None, ctypes.byref(p),
+                      None, 0, None)
     assert rc == EINVAL
+
+
+def test_fwd_workspace_query():
+    # 8 bytes per (sequence, head, row) on the bf16 d = 64 / 128 path with skip keys
+    p = pa.make_pattern(64, 128, 16)
+    assert pa.fwd_workspace_bytes(1, 4, 16, 8192, 64, p) == 8 * 4 * 16 * 8192
+    assert pa.fwd_workspace_bytes(1, 1, 32, 131072, 128, p) == 8 * 32 * 131072
+    assert pa.fwd_workspace_bytes(0, 4, 16, 8192, 64, p) == 0            # fp32: gather path
+    assert pa.fwd_workspace_bytes(1, 4, 16, 8192, 32, p) == 0            # d = 32: gather path
+    assert pa.fwd_workspace_bytes(1, 4, 16, 8192, 64, pa.make_pattern(64, 128, 0)) == 0  # no skips
+    assert pa.fwd_workspace_bytes(1, 4, 16, 8192, 64, pa.make_pattern(300, 128, 2)) == 0  # all skips in window
+    assert pa.fwd_workspace_bytes(1, 4, 16, 8192, 64, pa.make_pattern(300, 128, 3)) > 0
+    assert pa.fwd_workspace_bytes(1, 0, 16, 8192, 64, p) == 0            # invalid sizes
+    assert pa.fwd_workspace_bytes(1, 4, 16, 8192, 64, pa.make_pattern(4, 0, 2)) == 0
 
 
 def test_fp32_stride_multiple_of_four_is_accepted_by_validation_only():

@@ -137,3 +137,24 @@ def test_split_and_resid_agree_on_prefill_8k():
     b = run_fwd(x, w, "split")
     torch.cuda.synchronize()
     assert (a.float() - b.float()).abs().max().item() <= 2 * BF16_TOL
+
+
+def test_split_workspace_reused_and_checked():
+    """One caller workspace serves consecutive calls on a stream; a short one is refused."""
+    w = wl.Workload("ws", "fwd", "bf16", B=2, H=3, n=1500, d=64, k=20, pi=64, M=10, bidir=False, seed=7)
+    x1 = wl.make_fwd_inputs(w, device=DEV)
+    x2 = wl.make_fwd_inputs(w, device=DEV, seed=8)
+    kw = dict(window_k=w.k, period_pi=w.pi, num_skips=w.M, bidirectional=w.bidir)
+    need = pa.fwd_workspace_bytes(1, w.B, w.H, w.n, w.d, pa.make_pattern(w.k, w.pi, w.M))
+    assert need == 8 * w.B * w.H * w.n
+    ws = torch.empty(need, dtype=torch.uint8, device=DEV)
+    a1 = pa.fwd(x1["q"], x1["k"], x1["v"], x1["g"], workspace=ws, **kw)
+    a2 = pa.fwd(x2["q"], x2["k"], x2["v"], x2["g"], workspace=ws, **kw)
+    b1 = pa.fwd(x1["q"], x1["k"], x1["v"], x1["g"], **kw)
+    b2 = pa.fwd(x2["q"], x2["k"], x2["v"], x2["g"], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(a1, b1) and torch.equal(a2, b2)
+    assert max_err(a2, oracle_dense_fwd(x2, w), "fwd workspace reuse") <= BF16_TOL
+    with pytest.raises(pa.PiattnError) as e:
+        pa.fwd(x1["q"], x1["k"], x1["v"], x1["g"], workspace=ws[: need - 8], **kw)
+    assert e.value.code == 3
