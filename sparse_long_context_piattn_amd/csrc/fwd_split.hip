@@ -73,8 +73,11 @@ __device__ __forceinline__ bool row_has_skip(int32_t t, int32_t pr, int32_t mlo,
 // Tile order.  Workgroup hw runs on XCD hw % 8 as that XCD's (hw / 8)-th.
 // Logical tiles are dealt to the XCDs in runs of XG consecutive tiles, run
 // r to XCD r % 8: neighbouring tiles (which share halo rows) share an L2,
-// and the runs of long and short sequences spread over all XCDs.
-constexpr int32_t XG = 16;
+// and the runs of long and short sequences spread over all XCDs.  With
+// runs of 32 the window pass's halo rows come from L2 (its HBM reads fall
+// to q, k, v, the partial and the records once each); with runs of 16 about
+// 70% of them were fetched again.
+constexpr int32_t XG = 32;
 __device__ __forceinline__ int32_t xcd_logical(int32_t hw, int32_t total) {
     const int32_t xcd = hw % 8, loc = hw / 8;
     const int32_t logical = ((loc / XG) * 8 + xcd) * XG + loc % XG;
