@@ -503,9 +503,42 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
             for (int bb = 0; bb < DB; ++bb)
                 sacc[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[slot][bb], pb, sacc[bb], 0, 0, 0);
         }
-        if (!hs) return;
-        const int32_t row = res + tq * pi;
-        store_skip_partial<DB>(Ob + (int64_t)row * a.so.t, sacc, 1.0f / sl, sm + __log2f(sl), Ls + 2 * row, g);
+        // The chunk's skip partial, fp16 scaled by 2^-e per row (as in
+        // store_skip_partial), goes through the slot of entry e -- free
+        // until entry e+3 is issued after the next chunk's LDS reads -- so
+        // that every store instruction writes whole rows: 16 B per lane, a
+        // row's 2D bytes from 2D/16 neighbouring lanes.
+        {
+            const float inv = 1.0f / sl;                  // rows without skip keys are not stored
+            float mloc = 0.0f;
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) mloc = fmax_ieee(mloc, fabsf(sacc[bb][r]));
+            const float m = max4(mloc) * inv;
+            const int32_t ex = (int32_t)((__float_as_uint(m) >> 23) & 0xff);
+            const int32_t es = imax32(-64, ex - 141);     // m * 2^-es in [2^14, 2^15)
+            const float sc = __builtin_amdgcn_ldexpf(inv, -es);
+            uint16_t* tt = ws + ((e % 3 + 3) % 3) * BLK;
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb) {
+                uint2 w;
+                w.x = cvt_pk_f16(sacc[bb][0] * sc, sacc[bb][1] * sc);
+                w.y = cvt_pk_f16(sacc[bb][2] * sc, sacc[bb][3] * sc);
+                *reinterpret_cast<uint2*>(tt + swr<D>(x, 2 * bb + (g >> 1)) + 4 * (g & 1)) = w;
+            }
+            if (hs && g == 0)
+                *reinterpret_cast<f32x2_t*>(Ls + 2 * (res + tq * pi)) = f32x2_t{sm + __log2f(sl), (float)es};
+#pragma unroll
+            for (int j = 0; j < 32 * D / 1024; ++j) {
+                const int o = 1024 * j + 16 * lane;       // byte offset in the [16][D] fp16 tile
+                const int r = o / (2 * D), cc = (o % (2 * D)) / 16;
+                const uint4 val = *reinterpret_cast<const uint4*>(tt + swr<D>(r, cc));
+                const int32_t tr = 16 * c + r;
+                if (tr < pr && row_has_skip<BIDIR>(tr, pr, mlo, M))
+                    *reinterpret_cast<uint4*>(Ob + (int64_t)(res + tr * pi) * a.so.t + 8 * cc) = val;
+            }
+        }
     };
 
     // entries 0, 1 and the query rows of chunks c0, c0+1 in the order the
