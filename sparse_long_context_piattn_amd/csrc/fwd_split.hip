@@ -638,8 +638,21 @@ __global__ __launch_bounds__(WinShape<D>::WW * 64, WinShape<D>::EU) void fwd_win
                                     : (uint32_t)(imin32(imax32(s0 + lane / CH, 0), n - 1) * stt + lc);
         dma16(ub, off * 2u, lds_addr(dst + r0 * D));
     };
+    // Stage t < ntiles: key tile t.  Stage ntiles, when skip partials are
+    // merged: the tile's fp16 skip partial rows, each wave its own 16 rows
+    // (the layout of the query rows: rows 0..KT-1 in the K array, the rest
+    // in the V array).  Later stages: a harmless reload of the last key
+    // tile, which keeps every wave's count of loads in flight uniform.
     auto issue = [&](uint16_t* Ks, uint16_t* Vs, int32_t t) __attribute__((always_inline)) {
-        t = imin32(t, ntiles - 1);                       // past the last tile: harmless reload
+        if (merge && t == ntiles) {
+#pragma unroll
+            for (int j = 0; j < LPW; ++j) {
+                const int r0 = ((wave % (WW / 2)) * LPW + j) * RPI;
+                stage_rows(Ob, (int32_t)a.so.t, q0 + (isv ? KT : 0) + r0, r0, isv ? Vs : Ks);
+            }
+            return;
+        }
+        t = imin32(t, ntiles - 1);
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const int r0 = ((wave % (WW / 2)) * LPW + j) * RPI;
@@ -700,20 +713,11 @@ __global__ __launch_bounds__(WinShape<D>::WW * 64, WinShape<D>::EU) void fwd_win
     }
     lds_barrier();                                       // slot 2 is free for tile 2
 
-    // the skip partial of the lane's row (written by the skip pass), loaded
-    // now so that its latency hides behind the window loop
+    // the record of the lane's row (written by the skip pass), loaded now so
+    // that its latency hides behind the window loop
     const bool mg = merge && hs && qv;
-    uint16_t* orow = Ob + (int64_t)ic * a.so.t;
-    uint2 os[DB];
     f32x2_t rec = {0.0f, 0.0f};                          // (log2-sum-exp, e)
-    if (mg) {
-        rec = *reinterpret_cast<const f32x2_t*>(Ls + 2 * ic);
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) os[bb] = *reinterpret_cast<const uint2*>(orow + 16 * bb + 4 * g);
-    } else {
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) os[bb] = make_uint2(0, 0);
-    }
+    if (mg) rec = *reinterpret_cast<const f32x2_t*>(Ls + 2 * ic);
 
     f32x4_t acc[DB];
 #pragma unroll
@@ -781,10 +785,59 @@ __global__ __launch_bounds__(WinShape<D>::WW * 64, WinShape<D>::EU) void fwd_win
         }
         lrun += 0.25f * lsum[0];                        // quarter per lane; sum4 restores the row sum
     };
+    // Epilogue, with the slot of stage ntiles (P):
+    // the window partial, merged with the skip partial (read from P) when
+    // the row has skip keys (its lse gets the log(1-alpha) prior here); the
+    // bf16 rows then go back through the wave's own rows of P so that each
+    // store instruction writes whole rows.
+    auto epilogue = [&](uint16_t* Kp, uint16_t* Vp) __attribute__((always_inline)) {
+        // stage ntiles landed (stage ntiles+1 may be in flight); the
+        // barrier also lets every wave's reload into P land when P holds no
+        // partials
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPW));
+        lds_barrier();
+        uint16_t* prow = (16 * wave < KT ? Kp : Vp);
+        const int qr = 16 * wave + x, rr = qr & (KT - 1), rr0 = (16 * wave) & (KT - 1);
+        const float ltot = sum4(lrun);
+        const float lw = mrun + __log2f(ltot);          // log2-sum-exp of the window part
+        float fw = 1.0f / ltot, fs = 0.0f, lfin = lw;
+        uint2 os[DB];
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) os[bb] = make_uint2(0, 0);
+        if (mg) {
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb)
+                os[bb] = *reinterpret_cast<const uint2*>(prow + swr<D>(rr, 2 * bb + (g >> 1)) + 4 * (g & 1));
+            const float lsk = rec[0] + ps;
+            const float mx = fmaxf(lw, lsk);
+            const float aw = exp2_fast(lw - mx), as = exp2_fast(lsk - mx);
+            const float inv = 1.0f / (aw + as);
+            fw = ltot > 0.0f ? aw * inv / ltot : 0.0f; // alpha = 0: the window part is empty
+            fs = __builtin_amdgcn_ldexpf(as * inv, (int)rec[1]);   // undo the fp16 scaling
+            lfin = mx + __log2f(aw + as);
+        }
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) {
+            uint2 w;
+            w.x = cvt_pk_bf16(fmaf(acc[bb][0], fw, f16lo(os[bb].x) * fs), fmaf(acc[bb][1], fw, f16hi(os[bb].x) * fs));
+            w.y = cvt_pk_bf16(fmaf(acc[bb][2], fw, f16lo(os[bb].y) * fs), fmaf(acc[bb][3], fw, f16hi(os[bb].y) * fs));
+            *reinterpret_cast<uint2*>(prow + swr<D>(rr, 2 * bb + (g >> 1)) + 4 * (g & 1)) = w;
+        }
+        if (a.lse && qv && g == 0) a.lse[bq * a.sg.s + h * a.sg.h + (tok0 + i) * a.sg.t] = lfin * PIATTN_LN2;
+#pragma unroll
+        for (int j = 0; j < 32 * D / 1024; ++j) {
+            const int o = 1024 * j + 16 * lane;           // byte offset in the wave's [16][D] bf16 rows
+            const int r = o / (2 * D), cc = (o % (2 * D)) / 16;
+            const uint4 val = *reinterpret_cast<const uint4*>(prow + swr<D>(rr0 + r, cc));
+            const int32_t row = q0 + 16 * wave + r;
+            if (row < n) *reinterpret_cast<uint4*>(Ob + (int64_t)row * a.so.t + 8 * cc) = val;
+        }
+    };
     // step t: wait for this wave's loads of tile t (tile t+1 may be in
     // flight), barrier (everyone's tile t landed, tile t-1 fully read), issue
-    // tile t+2 into the slot of tile t-1, compute tile t
-    auto step = [&](int32_t t, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn) __attribute__((always_inline)) {
+    // stage t+2 into the slot of tile t-1, compute tile t
+    auto step = [&](int32_t t, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn)
+        __attribute__((always_inline)) {
         if (t > 0) {
             __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPW));
             lds_barrier();
@@ -799,31 +852,10 @@ __global__ __launch_bounds__(WinShape<D>::WW * 64, WinShape<D>::EU) void fwd_win
         if (t + 2 >= ntiles) break;
         step(t + 2, k2s, v2s, k1s, v1s);
     }
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));         // reloads past the end land before the LDS retires
-
-    // ---- epilogue: window partial, merged with the skip partial when the
-    // row has skip keys (its lse gets the log(1-alpha) prior here)
-    const float ltot = sum4(lrun);
-    if (!qv) return;
-    const float lw = mrun + __log2f(ltot);              // log2-sum-exp of the window part
-    float fw = 1.0f / ltot, fs = 0.0f, lfin = lw;
-    if (mg) {
-        const float lsk = rec[0] + ps;
-        const float mx = fmaxf(lw, lsk);
-        const float aw = exp2_fast(lw - mx), as = exp2_fast(lsk - mx);
-        const float inv = 1.0f / (aw + as);
-        fw = ltot > 0.0f ? aw * inv / ltot : 0.0f;     // alpha = 0: the window part is empty
-        fs = __builtin_amdgcn_ldexpf(as * inv, (int)rec[1]);   // undo the fp16 scaling
-        lfin = mx + __log2f(aw + as);
-    }
-#pragma unroll
-    for (int bb = 0; bb < DB; ++bb) {
-        uint2 w;
-        w.x = cvt_pk_bf16(fmaf(acc[bb][0], fw, f16lo(os[bb].x) * fs), fmaf(acc[bb][1], fw, f16hi(os[bb].x) * fs));
-        w.y = cvt_pk_bf16(fmaf(acc[bb][2], fw, f16lo(os[bb].y) * fs), fmaf(acc[bb][3], fw, f16hi(os[bb].y) * fs));
-        *reinterpret_cast<uint2*>(orow + 16 * bb + 4 * g) = w;
-    }
-    if (a.lse && g == 0) a.lse[bq * a.sg.s + h * a.sg.h + (tok0 + i) * a.sg.t] = lfin * PIATTN_LN2;
+    // stage ntiles went to slot ntiles % 3
+    const int pslot = ntiles % 3;
+    epilogue(pslot == 0 ? k0s : pslot == 1 ? k1s : k2s, pslot == 0 ? v0s : pslot == 1 ? v1s : v2s);
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));         // loads past the end land before the LDS retires
 }
 
 // lse_s: the caller's workspace of B*H*n (log2-sum-exp, e) float pairs, or
