@@ -101,9 +101,21 @@ __device__ __forceinline__ uint32_t cvt_pk_f16(float lo, float hi) {
 __device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[0]; }
 __device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[1]; }
 
-template <int DB>
-__device__ __forceinline__ void store_skip_partial(uint16_t* orow, const f32x4_t (&sacc)[DB], float inv, float lse2,
-                                                   float* rec, int g) {
+// One wave's chunk of the skip partial -- query periods 16c .. 16c+15 of
+// residue res -- goes through the free LDS tile tt (16 D elements) so that
+// every store instruction writes whole rows: the lanes write their MFMA
+// layout (lane (x, g) holds d = 16 bb + 4 g + 0..3 of row x), then read back
+// 16 bytes each, a row's 2D bytes from 2D/16 neighbouring lanes.  Rows past
+// the residue or without skip keys are not stored; hs says whether row x has
+// skip keys (its record (lse2, e) is written then).
+template <int D, bool BIDIR>
+__device__ __forceinline__ void store_skip_chunk(uint16_t* tt, const f32x4_t (&sacc)[D / 16], float sl, float sm,
+                                                 bool hs, int32_t c, int32_t res, int32_t pr, int32_t pi,
+                                                 int32_t mlo, int32_t M, uint16_t* Ob, int64_t sot, float* Ls,
+                                                 int lane) {
+    constexpr int DB = D / 16;
+    const int x = lane & 15, g = lane >> 4;
+    const float inv = 1.0f / sl;
     float mloc = 0.0f;
 #pragma unroll
     for (int bb = 0; bb < DB; ++bb)
@@ -118,11 +130,18 @@ __device__ __forceinline__ void store_skip_partial(uint16_t* orow, const f32x4_t
         uint2 w;
         w.x = cvt_pk_f16(sacc[bb][0] * sc, sacc[bb][1] * sc);
         w.y = cvt_pk_f16(sacc[bb][2] * sc, sacc[bb][3] * sc);
-        *reinterpret_cast<uint2*>(orow + 16 * bb + 4 * g) = w;
+        *reinterpret_cast<uint2*>(tt + swr<D>(x, 2 * bb + (g >> 1)) + 4 * (g & 1)) = w;
     }
-    if (g == 0) {
-        rec[0] = lse2;
-        rec[1] = (float)e;
+    if (hs && g == 0)
+        *reinterpret_cast<f32x2_t*>(Ls + 2 * (res + (16 * c + x) * pi)) = f32x2_t{sm + __log2f(sl), (float)e};
+#pragma unroll
+    for (int j = 0; j < 32 * D / 1024; ++j) {
+        const int o = 1024 * j + 16 * lane;               // byte offset in the [16][D] fp16 tile
+        const int r = o / (2 * D), cc = (o % (2 * D)) / 16;
+        const uint4 val = *reinterpret_cast<const uint4*>(tt + swr<D>(r, cc));
+        const int32_t tr = 16 * c + r;
+        if (tr < pr && row_has_skip<BIDIR>(tr, pr, mlo, M))
+            *reinterpret_cast<uint4*>(Ob + (int64_t)(res + tr * pi) * sot + 8 * cc) = val;
     }
 }
 
@@ -246,10 +265,11 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_kernel(FwdArgs a, float* lse
         sl = 0.0f;
         scst = 0.0f;
     };
-    auto chunk_store = [&](int32_t c) __attribute__((always_inline)) {
-        if (!shs) return;                             // no skip key: the window pass leaves the row alone
-        const int32_t row = res + (16 * c + x) * pi;   // every lane holds its column's full sum sl
-        store_skip_partial<DB>(Ob + (int64_t)row * a.so.t, sacc, 1.0f / sl, sm + __log2f(sl), Ls + 2 * row, g);
+    // (through the slot of the chunk's last unit: the next unit issues into
+    // it only after these stores, which wait for their LDS reads)
+    auto chunk_store = [&](int32_t c, uint16_t* slot) __attribute__((always_inline)) {
+        store_skip_chunk<D, BIDIR>(slot + wave * UNIT, sacc, sl, sm, shs, c, res, pr, pi, mlo, M, Ob, a.so.t, Ls,
+                                   lane);
     };
     auto unit_compute = [&](int32_t kb, const uint16_t* slot) __attribute__((always_inline)) {
         const uint16_t* Ks = slot + wave * UNIT;
@@ -297,7 +317,7 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_kernel(FwdArgs a, float* lse
     // Unit u: issue unit u+PF into nxt (its slot was consumed at unit u-1),
     // wait until this wave's loads of unit u have landed, compute.  The query
     // rows of chunk c+1 are loaded right after chunk c has read its own.
-    auto unit = [&](int32_t u, const uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
+    auto unit = [&](int32_t u, uint16_t* cur, uint16_t* nxt) __attribute__((always_inline)) {
         issue(nxt, u + PF);
         __builtin_amdgcn_s_waitcnt(vm_wait_imm(PF * LPU));
         const int32_t c = u / NK, kbi = u - c * NK;
@@ -307,7 +327,7 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_kernel(FwdArgs a, float* lse
             issue_q(c + 1);
         }
         unit_compute(c - NBL + kbi, cur);
-        if (kbi == NK - 1) chunk_store(c);
+        if (kbi == NK - 1) chunk_store(c, cur);
     };
 
     // The query rows of chunk c are issued while chunk c-1 starts, and NK >= 2
@@ -503,42 +523,10 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
             for (int bb = 0; bb < DB; ++bb)
                 sacc[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[slot][bb], pb, sacc[bb], 0, 0, 0);
         }
-        // The chunk's skip partial, fp16 scaled by 2^-e per row (as in
-        // store_skip_partial), goes through the slot of entry e -- free
-        // until entry e+3 is issued after the next chunk's LDS reads -- so
-        // that every store instruction writes whole rows: 16 B per lane, a
-        // row's 2D bytes from 2D/16 neighbouring lanes.
-        {
-            const float inv = 1.0f / sl;                  // rows without skip keys are not stored
-            float mloc = 0.0f;
-#pragma unroll
-            for (int bb = 0; bb < DB; ++bb)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) mloc = fmax_ieee(mloc, fabsf(sacc[bb][r]));
-            const float m = max4(mloc) * inv;
-            const int32_t ex = (int32_t)((__float_as_uint(m) >> 23) & 0xff);
-            const int32_t es = imax32(-64, ex - 141);     // m * 2^-es in [2^14, 2^15)
-            const float sc = __builtin_amdgcn_ldexpf(inv, -es);
-            uint16_t* tt = ws + ((e % 3 + 3) % 3) * BLK;
-#pragma unroll
-            for (int bb = 0; bb < DB; ++bb) {
-                uint2 w;
-                w.x = cvt_pk_f16(sacc[bb][0] * sc, sacc[bb][1] * sc);
-                w.y = cvt_pk_f16(sacc[bb][2] * sc, sacc[bb][3] * sc);
-                *reinterpret_cast<uint2*>(tt + swr<D>(x, 2 * bb + (g >> 1)) + 4 * (g & 1)) = w;
-            }
-            if (hs && g == 0)
-                *reinterpret_cast<f32x2_t*>(Ls + 2 * (res + tq * pi)) = f32x2_t{sm + __log2f(sl), (float)es};
-#pragma unroll
-            for (int j = 0; j < 32 * D / 1024; ++j) {
-                const int o = 1024 * j + 16 * lane;       // byte offset in the [16][D] fp16 tile
-                const int r = o / (2 * D), cc = (o % (2 * D)) / 16;
-                const uint4 val = *reinterpret_cast<const uint4*>(tt + swr<D>(r, cc));
-                const int32_t tr = 16 * c + r;
-                if (tr < pr && row_has_skip<BIDIR>(tr, pr, mlo, M))
-                    *reinterpret_cast<uint4*>(Ob + (int64_t)(res + tr * pi) * a.so.t + 8 * cc) = val;
-            }
-        }
+        // the chunk's skip partial, through the slot of entry e: free until
+        // entry e+3 is issued after the next chunk's LDS reads
+        store_skip_chunk<D, BIDIR>(ws + ((e % 3 + 3) % 3) * BLK, sacc, sl, sm, hs, c, res, pr, pi, mlo, M, Ob,
+                                   a.so.t, Ls, lane);
     };
 
     // entries 0, 1 and the query rows of chunks c0, c0+1 in the order the

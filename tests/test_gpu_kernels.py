@@ -67,6 +67,10 @@ CASES = [
     ("d128_M64_pi256", 1, 1, 20000, 128, 128, 256, 64, False),
     ("d128_bidir_M30", 1, 2, 4000, 128, 40, 64, 30, True),
     ("d128_bidir_M12", 1, 2, 3100, 128, 20, 96, 12, True),
+    # bands of more than five key blocks: the skip pass without the register ring
+    ("d128_big_M", 1, 1, 6000, 128, 16, 32, 90, False),
+    ("d128_bidir_M40", 1, 1, 5000, 128, 24, 64, 40, True),
+    ("d64_bidir_M50", 1, 2, 4000, 64, 16, 48, 50, True),
 ]
 
 
