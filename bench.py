@@ -127,9 +127,19 @@ def cpu_baseline(w, x, budget_s: float):
         if elapsed >= budget_s * 0.5 or count >= total_rows:
             break
         count = min(total_rows, int(count * max(2.0, budget_s / max(elapsed, 1e-3))))
-    return {"value": count / elapsed, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": "%d uniformly sampled query rows of the %s workload (of %d), fp64, "
-                      "OpenMP over rows, %.1f s" % (count, w.name, total_rows, elapsed)}
+    passes = 1
+    if elapsed < budget_s * 0.5:
+        # the whole workload is a small sample: repeat it up to half the budget
+        passes = max(1, min(200, int(budget_s * 0.5 / max(elapsed, 1e-3))))
+        t0 = time.perf_counter()
+        for _ in range(passes):
+            oracle.fwd(q, k, v, g, cu, w.k, w.pi, w.M, w.bidir, w.scale, rows=rows)
+        elapsed = time.perf_counter() - t0
+    what = ("%d uniformly sampled query rows" % count if count < total_rows
+            else "all query rows, %d pass%s," % (passes, "es" if passes > 1 else ""))
+    return {"value": passes * count / elapsed, "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": "%s of the %s workload (%d rows), fp64, OpenMP over rows, %.1f s"
+                      % (what, w.name, total_rows, elapsed)}
 
 
 def decode_algorithmic(w):
