@@ -21,15 +21,18 @@
 // keys [i-k, i] (bidirectional [i-k, i+k]) of all its rows stream through a
 // ring of three LDS slots of 32 rows, two slots ahead of the compute.  Each
 // wave owns 16 rows: S^T = K Q^T on v_mfma_f32_16x16x32_bf16, window mask,
-// log(alpha) prior, online softmax, O^T += V^T P^T.  In the epilogue, rows
-// that have skip keys combine their window partial with the skip partial
-// (whose log-sum-exp gets the log(1-alpha) prior here): one softmax over the
-// union of window and skip keys.
+// log(alpha) prior, online softmax, O^T += V^T P^T.  The tile's skip partial
+// rows arrive as one more stage of the ring; in the epilogue, rows that have
+// skip keys combine their window partial with the skip partial (whose
+// log-sum-exp gets the log(1-alpha) prior here): one softmax over the union
+// of window and skip keys.
 //
 // Both passes keep the LDS-direct loads out of the compiler's view (dma16)
 // and wait for them explicitly, so no compiler-inserted wait drains the
 // pipelines.  Rows outside the sequence are loaded from a clamped valid row
-// and masked.
+// and masked.  Row data leaves (and the partial re-enters) through LDS as
+// whole rows: 16 bytes per lane, a row from neighbouring lanes, rather than
+// the MFMA layout's 8 bytes of each of 16 rows per instruction.
 #include "kernels.hpp"
 #include "mfma_util.hpp"
 
