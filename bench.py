@@ -37,13 +37,20 @@ def log(*a):
 
 
 def kernel_digest() -> str:
+    """Digest of the kernel sources with comments and blank space removed, so
+    that counters stay matched to the code they were taken on across edits
+    that change no code."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_long_context_piattn_amd", "csrc")
     for name in KERNEL_SOURCES:
         p = os.path.join(csrc, name)
         if os.path.exists(p):
+            text = open(p).read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
             h.update(name.encode())
-            h.update(open(p, "rb").read())
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
