@@ -484,10 +484,10 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
         const int32_t hi = BIDIR ? imin32(tq + M, pr - 1) : tq - mlo;
         const int32_t slo = hs ? lo : EMPTY;
         const uint32_t sspan = hs ? (uint32_t)(hi - lo) : 0u;
-        f32x4_t sacc[DB];
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) sacc[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        float sm = -INFINITY, sl = 0.0f, smL = -INFINITY, scst = 0.0f;
+        // All NK score blocks first, then one softmax over the chunk's keys
+        // with the exact row max: no running max, no rescaling.
+        float sc[NK][4];
+        float mxl = -INFINITY;
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
             const int slot = (RS + 1 + i) % NK;           // entry c + i
@@ -498,34 +498,32 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
             const int32_t kp0 = 16 * kb + 4 * g;
             const int32_t e0 = kp0 - slo;
             const int32_t h0 = kp0 - tq + mlo - 1;
-            float sc[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 bool ok = (uint32_t)(e0 + r) <= sspan;
                 if (BIDIR) ok = ok && (uint32_t)(h0 + r) > (uint32_t)(2 * mlo - 2);
-                sc[r] = ok ? s4[r] : -INFINITY;
+                sc[i][r] = ok ? s4[r] : -INFINITY;
             }
-            const float mx = max4(fmax_ieee(fmax_ieee(sc[0], sc[1]), fmax_ieee(sc[2], sc[3]))) * sl2;
-            if (__builtin_amdgcn_ballot_w64(mx > smL)) {
-                const float mnew = fmax_ieee(sm, mx);
-                const float mu = mnew == -INFINITY ? 0.0f : mnew;
-                const float fac = exp2_fast(sm - mu);
+            mxl = fmax_ieee(mxl, fmax_ieee(fmax_ieee(sc[i][0], sc[i][1]), fmax_ieee(sc[i][2], sc[i][3])));
+        }
+        const float sm = max4(mxl) * sl2;                 // the column's max, log2 units
+        const float scst = sm == -INFINITY ? 0.0f : -sm;
+        f32x4_t sacc[DB];
 #pragma unroll
-                for (int bb = 0; bb < DB; ++bb) sacc[bb] *= fac;
-                sl *= fac;
-                sm = mnew;
-                smL = mnew + LAZY;
-                scst = -mu;
-            }
-            const uint32_t w0 = cvt_pk_bf16(exp2_fast(fmaf(sc[0], sl2, scst)), exp2_fast(fmaf(sc[1], sl2, scst)));
-            const uint32_t w1 = cvt_pk_bf16(exp2_fast(fmaf(sc[2], sl2, scst)), exp2_fast(fmaf(sc[3], sl2, scst)));
+        for (int bb = 0; bb < DB; ++bb) sacc[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int slot = (RS + 1 + i) % NK;
+            const uint32_t w0 = cvt_pk_bf16(exp2_fast(fmaf(sc[i][0], sl2, scst)), exp2_fast(fmaf(sc[i][1], sl2, scst)));
+            const uint32_t w1 = cvt_pk_bf16(exp2_fast(fmaf(sc[i][2], sl2, scst)), exp2_fast(fmaf(sc[i][3], sl2, scst)));
             const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(w0, w1));
-            const f32x4_t ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, pb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-            sl += ls[0];
+            lsum = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, pb, lsum, 0, 0, 0);
 #pragma unroll
             for (int bb = 0; bb < DB; ++bb)
                 sacc[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[slot][bb], pb, sacc[bb], 0, 0, 0);
         }
+        const float sl = lsum[0];
         // the chunk's skip partial, through the slot of entry e: free until
         // entry e+3 is issued after the next chunk's LDS reads
         store_skip_chunk<D, BIDIR>(ws + ((e % 3 + 3) % 3) * BLK, sacc, sl, sm, hs, c, res, pr, pi, mlo, M, Ob,
