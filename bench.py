@@ -173,6 +173,18 @@ def bench_decode(args, w, dev):
     log("workload %s: %d (sequence, head) rows x (%d local + %d skip) keys, %.1f MB/call"
         % (w.name, rows, loc, sk, alg_bytes / 1e6))
     x = wl.make_decode_inputs(w, device=dev)
+    slots = None
+    if args.rolling:
+        # a rolling cache of W = max(k, M pi) + 1 rows holding the last W positions
+        slots = pa.rolling_slots(w.k, w.pi, w.M)
+        j = torch.arange(w.n - slots, w.n, device=dev)
+        for name in ("k_cache", "v_cache"):
+            ring = torch.empty((w.B, w.H, slots, w.d), dtype=x[name].dtype, device=dev)
+            for s0 in range(0, w.B, 8):
+                ring[s0:s0 + 8][:, :, j % slots] = x[name][s0:s0 + 8][:, :, j]
+            x[name] = ring
+            torch.cuda.empty_cache()
+        log("rolling cache of %d rows per (sequence, head)" % slots)
     out = torch.empty_like(x["q"])
     pat = pa.make_pattern(w.k, w.pi, w.M)
     splits = args.splits
@@ -181,7 +193,8 @@ def bench_decode(args, w, dev):
 
     def step(_j):
         pa.decode(x["q"], x["k_cache"], x["v_cache"], x["lens"], x["g"], window_k=w.k,
-                  period_pi=w.pi, num_skips=w.M, num_splits=splits, workspace=ws, out=out)
+                  period_pi=w.pi, num_skips=w.M, num_splits=splits, workspace=ws, out=out,
+                  rolling=bool(args.rolling))
 
     ms_per_step = timed(step, args, dev)
     if args.calibrate_copy:
@@ -196,7 +209,8 @@ def bench_decode(args, w, dev):
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
            "data": "synthetic (seeded N(0,1) cache, query and gate logits)",
            "config": {"workload": w.name, "sequences": w.B, "H": w.H, "cache_len": w.n,
-                      "d": w.d, "k": w.k, "pi": w.pi, "M": w.M, "num_splits": splits},
+                      "d": w.d, "k": w.k, "pi": w.pi, "M": w.M, "num_splits": splits,
+                      "cache": "rolling, %d rows" % slots if slots else "linear"},
            "hbm_gbps_algorithmic": round(gbps, 1), "kernel_digest": kernel_digest(),
            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
@@ -303,6 +317,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
     ap.add_argument("--splits", type=int, default=0, help="decode key-range splits (0 = auto)")
+    ap.add_argument("--rolling", action="store_true",
+                    help="decode over a rolling cache of max(k, M pi) + 1 rows")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the timed steps, run a plain 512 MiB bf16 copy three times "
                          "(reference dispatches for the HBM byte counters)")

@@ -170,6 +170,56 @@ int32_t piattn_decode_auto_splits(int32_t S, int32_t H, int32_t d,
                                   const piattn_pattern *pattern);
 
 /*
+ * Rolling KV cache for decode.  The pages note that at inference the cache
+ * is updated in constant time because a new token only touches positions
+ * modulo pi (gist.science section 2 "Execution & Scheduling", item
+ * "Inference"), and a sliding-window model keeps its keys and values in a
+ * buffer of w rows, position i in row i mod w, overwriting the oldest
+ * (Ultralytics glossary "Sliding Window Attention", section "Wie das
+ * Fenster mit der Tiefe wächst").  Here the newest position i attends to
+ * i-k .. i and i - m*pi, m <= M, so a cache of W = max(k, M*pi) + 1 rows
+ * (k + 1 when the pattern has no skip keys outside the window), position j
+ * in row j mod W, holds every key it needs, whatever the sequence length.
+ */
+
+/* W for this pattern (-1 for an invalid pattern or W >= 2^30). */
+int32_t piattn_rolling_slots(const piattn_pattern *pattern);
+
+/*
+ * Append one token per sequence: for every (s, h), the key and value rows
+ * k_new[s, h, :] and v_new[s, h, :] are written to row positions[s] mod
+ * cache_slots of k_cache[s, h] and v_cache[s, h].  positions is a device
+ * int32 array [S]; a negative entry leaves that sequence's rows alone.
+ * strides[0], strides[1]: {s0, s1, -} of k_new, v_new ([S, H, d]);
+ * strides[2], strides[3]: {s0, s1, row} of the caches ([S, H, cache_slots, d]).
+ * Pointers need the element alignment only.  Returns PIATTN_OK,
+ * PIATTN_EINVAL, PIATTN_EUNSUPPORTED (d) or PIATTN_EHIP.
+ */
+int piattn_cache_append(piattn_dtype dtype, int32_t S, int32_t H, int32_t d,
+                        const void *k_new, const void *v_new, void *k_cache,
+                        void *v_cache, const int32_t *positions,
+                        int32_t cache_slots, const int64_t strides[4][3],
+                        void *stream);
+
+/*
+ * piattn_decode over a rolling cache: arguments as for piattn_decode, with
+ * cache_slots rows per (sequence, head) holding position j in row j mod
+ * cache_slots.  cache_lens[s] (the number of tokens so far; the query sits
+ * at position cache_lens[s] - 1, already appended) may exceed cache_slots;
+ * a length below 1 gives a NaN row, and lengths must stay below 2^30.
+ * cache_slots must be at least piattn_rolling_slots(pattern) (else
+ * PIATTN_EINVAL).  The result equals piattn_decode on a linear cache that
+ * holds the same positions.
+ */
+int piattn_decode_rolling(piattn_dtype dtype, int32_t S, int32_t H, int32_t d,
+                          const void *q, const void *k_cache, const void *v_cache,
+                          const int32_t *cache_lens, int32_t cache_slots,
+                          const float *gate_logits, void *out,
+                          const int64_t strides[5][3], const piattn_pattern *pattern,
+                          int32_t num_splits, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
  * piattn_neighbors -- debug dump of the neighbour lists that the compute
  * kernels enumerate, for queries q_begin .. q_begin+q_count-1 of a sequence
  * of length n.  Row r of idx [q_count, cap] (device int32) receives the keys

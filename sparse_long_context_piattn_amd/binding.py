@@ -22,7 +22,8 @@ STATUS = {0: "PIATTN_OK", 1: "PIATTN_EINVAL", 2: "PIATTN_EUNSUPPORTED", 3: "PIAT
           4: "PIATTN_EHIP"}
 
 EXPORTS = ["piattn_fwd", "piattn_fwd_workspace_bytes", "piattn_decode", "piattn_decode_workspace_bytes",
-           "piattn_decode_auto_splits", "piattn_neighbors", "piattn_neighbors_cap",
+           "piattn_decode_auto_splits", "piattn_rolling_slots", "piattn_cache_append",
+           "piattn_decode_rolling", "piattn_neighbors", "piattn_neighbors_cap",
            "piattn_last_error", "piattn_version"]
 
 
@@ -40,6 +41,7 @@ class Pattern(ctypes.Structure):
 
 
 Strides = ctypes.c_int64 * 15
+Strides4 = ctypes.c_int64 * 12
 _lib = None
 
 
@@ -65,6 +67,13 @@ def lib():
         L.piattn_decode_workspace_bytes.restype = sz
         L.piattn_decode_auto_splits.argtypes = [i32, i32, i32, pat]
         L.piattn_decode_auto_splits.restype = i32
+        L.piattn_decode_rolling.argtypes = L.piattn_decode.argtypes
+        L.piattn_decode_rolling.restype = ctypes.c_int
+        L.piattn_rolling_slots.argtypes = [pat]
+        L.piattn_rolling_slots.restype = i32
+        L.piattn_cache_append.argtypes = [ctypes.c_int, i32, i32, i32, vp, vp, vp, vp, vp, i32,
+                                          ctypes.POINTER(Strides4), vp]
+        L.piattn_cache_append.restype = ctypes.c_int
         L.piattn_neighbors.argtypes = [i32, pat, i32, i32, i32, vp, vp, vp, vp]
         L.piattn_neighbors.restype = ctypes.c_int
         L.piattn_neighbors_cap.argtypes = [pat]
@@ -191,10 +200,41 @@ def decode_workspace_bytes(S, H, d, num_splits, pattern: Pattern) -> int:
     return int(lib().piattn_decode_workspace_bytes(S, H, d, num_splits, ctypes.byref(pattern)))
 
 
+def rolling_slots(window_k: int, period_pi: int, num_skips: int) -> int:
+    """Rows of a rolling decode cache for this pattern: max(k, M*pi) + 1."""
+    return int(lib().piattn_rolling_slots(ctypes.byref(make_pattern(window_k, period_pi, num_skips))))
+
+
+def cache_append(k_new, v_new, k_cache, v_cache, positions):
+    """Write k_new, v_new [S, H, d] to row positions[s] mod W of the rolling
+    caches [S, H, W, d] (positions: int32 [S] on the GPU; negative = skip)."""
+    code = _dtype_code(k_new)
+    _need_cuda(k_new, v_new, k_cache, v_cache, positions)
+    if k_new.dim() != 3 or v_new.shape != k_new.shape or k_cache.dim() != 4 or v_cache.shape != k_cache.shape:
+        raise ValueError("expect k_new, v_new [S, H, d] and caches [S, H, W, d]")
+    S, H, d = k_new.shape
+    if tuple(k_cache.shape[:2]) != (S, H) or k_cache.shape[3] != d:
+        raise ValueError("cache shape does not match the new rows")
+    if positions.dtype != torch.int32 or tuple(positions.shape) != (S,):
+        raise ValueError("positions must be int32 [S]")
+    for t in (k_new, v_new, k_cache, v_cache):
+        if t.dtype != k_new.dtype or t.stride(-1) != 1:
+            raise ValueError("same dtype and a contiguous head dimension expected")
+    st = [(k_new.stride(0), k_new.stride(1), 0), (v_new.stride(0), v_new.stride(1), 0),
+          tuple(k_cache.stride()[:3]), tuple(v_cache.stride()[:3])]
+    strides = Strides4(*[x for s in st for x in s])
+    rc = lib().piattn_cache_append(code, S, H, d, _ptr(k_new), _ptr(v_new), _ptr(k_cache), _ptr(v_cache),
+                                   _ptr(positions), k_cache.shape[2], ctypes.byref(strides),
+                                   ctypes.c_void_p(_stream(k_new.device)))
+    _check(rc)
+
+
 def decode(q, k_cache, v_cache, cache_lens, g, *, window_k: int, period_pi: int,
-           num_skips: int, scale: float = 0.0, num_splits: int = 0, workspace=None, out=None):
+           num_skips: int, scale: float = 0.0, num_splits: int = 0, workspace=None, out=None,
+           rolling: bool = False):
     """pi-Attention decode: q [S, H, d], caches [S, H, L, d] (strided, last dim
     contiguous), cache_lens int32 [S] (query position len-1), g [S, H].
+    rolling: the caches are rolling caches of L rows (position j in row j mod L).
     workspace: optional uint8 GPU tensor; allocated here when needed and absent."""
     code = _dtype_code(q)
     _need_cuda(q, k_cache, v_cache, cache_lens, g, out, workspace)
@@ -221,10 +261,10 @@ def decode(q, k_cache, v_cache, cache_lens, g, *, window_k: int, period_pi: int,
           tuple(v_cache.stride()[:3]), (out.stride(0), out.stride(1), 0),
           (g.stride(0), g.stride(1), 0)]
     strides = Strides(*[x for s in st for x in s])
-    rc = lib().piattn_decode(code, S, H, d, _ptr(q), _ptr(k_cache), _ptr(v_cache),
-                             _ptr(cache_lens), k_cache.shape[2], _ptr(g), _ptr(out),
-                             ctypes.byref(strides), ctypes.byref(pat), int(num_splits),
-                             _ptr(workspace), wbytes, ctypes.c_void_p(_stream(q.device)))
+    fn = lib().piattn_decode_rolling if rolling else lib().piattn_decode
+    rc = fn(code, S, H, d, _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(cache_lens), k_cache.shape[2],
+            _ptr(g), _ptr(out), ctypes.byref(strides), ctypes.byref(pat), int(num_splits),
+            _ptr(workspace), wbytes, ctypes.c_void_p(_stream(q.device)))
     _check(rc)
     return out
 

@@ -241,11 +241,22 @@ int32_t piattn_decode_auto_splits(int32_t S, int32_t H, int32_t d, const piattn_
     return decode_splits_for(S, H, p);
 }
 
-int piattn_decode(piattn_dtype dtype, int32_t S, int32_t H, int32_t d, const void* q,
-                  const void* k_cache, const void* v_cache, const int32_t* cache_lens,
-                  int32_t cache_capacity, const float* gate_logits, void* out,
-                  const int64_t strides[5][3], const piattn_pattern* pattern, int32_t num_splits,
-                  void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// Rows a rolling cache needs so that every key of the newest position is
+// still held: the window reaches back k positions, the skips M*pi (when the
+// pattern has skip keys outside the window).  -1 when that exceeds int32.
+static int64_t rolling_slots_for(const PiPattern& p) {
+    const int64_t back = p.M >= p.k / p.pi + 1 ? (int64_t)p.M * p.pi : 0;
+    const int64_t w = (back > p.k ? back : p.k) + 1;
+    return w < kMaxExtent ? w : -1;
+}
+
+static int decode_impl(piattn_dtype dtype, int32_t S, int32_t H, int32_t d, const void* q,
+                       const void* k_cache, const void* v_cache, const int32_t* cache_lens,
+                       int32_t cache_capacity, const float* gate_logits, void* out,
+                       const int64_t strides[5][3], const piattn_pattern* pattern, int32_t num_splits,
+                       void* workspace, size_t workspace_bytes, void* stream, bool rolling) {
     if (dtype != PIATTN_F32 && dtype != PIATTN_BF16)
         return fail(PIATTN_EINVAL, "dtype=%d is not PIATTN_F32 or PIATTN_BF16", (int)dtype);
     PiPattern p;
@@ -256,6 +267,12 @@ int piattn_decode(piattn_dtype dtype, int32_t S, int32_t H, int32_t d, const voi
         return fail(PIATTN_EINVAL, "S=%d H=%d out of range", S, H);
     if (cache_capacity < 1 || cache_capacity >= kMaxExtent - p.k)
         return fail(PIATTN_EINVAL, "cache_capacity=%d out of range", cache_capacity);
+    if (rolling) {
+        const int64_t need = rolling_slots_for(p);
+        if (need < 0 || cache_capacity < need)
+            return fail(PIATTN_EINVAL, "a rolling cache of %d rows is smaller than max(k, M*pi) + 1 = %lld",
+                        cache_capacity, (long long)need);
+    }
     if (d < 1) return fail(PIATTN_EINVAL, "d=%d must be positive", d);
     if (d != 32 && d != 64 && d != 128)
         return fail(PIATTN_EUNSUPPORTED, "d=%d unsupported (32, 64 or 128)", d);
@@ -306,12 +323,78 @@ int piattn_decode(piattn_dtype dtype, int32_t S, int32_t H, int32_t d, const voi
     a.H = H;
     a.d = d;
     a.cap = cache_capacity;
+    a.ring = rolling ? cache_capacity : 0;
     a.splits = splits;
     a.chunk = (int32_t)((umax + splits - 1) / splits);
     a.pat = p;
     a.scale_log2 = scale_log2(pattern, d);
     return launch_status(launch_decode(dtype == PIATTN_BF16 ? 1 : 0, a,
                                        static_cast<hipStream_t>(stream)));
+}
+
+extern "C" {
+
+int piattn_decode(piattn_dtype dtype, int32_t S, int32_t H, int32_t d, const void* q,
+                  const void* k_cache, const void* v_cache, const int32_t* cache_lens,
+                  int32_t cache_capacity, const float* gate_logits, void* out,
+                  const int64_t strides[5][3], const piattn_pattern* pattern, int32_t num_splits,
+                  void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl(dtype, S, H, d, q, k_cache, v_cache, cache_lens, cache_capacity, gate_logits, out,
+                       strides, pattern, num_splits, workspace, workspace_bytes, stream, false);
+}
+
+int piattn_decode_rolling(piattn_dtype dtype, int32_t S, int32_t H, int32_t d, const void* q,
+                          const void* k_cache, const void* v_cache, const int32_t* cache_lens,
+                          int32_t cache_slots, const float* gate_logits, void* out,
+                          const int64_t strides[5][3], const piattn_pattern* pattern, int32_t num_splits,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl(dtype, S, H, d, q, k_cache, v_cache, cache_lens, cache_slots, gate_logits, out,
+                       strides, pattern, num_splits, workspace, workspace_bytes, stream, true);
+}
+
+int32_t piattn_rolling_slots(const piattn_pattern* pattern) {
+    PiPattern p;
+    if (check_pattern(pattern, &p) != PIATTN_OK) return -1;
+    return (int32_t)rolling_slots_for(p);
+}
+
+int piattn_cache_append(piattn_dtype dtype, int32_t S, int32_t H, int32_t d, const void* k_new,
+                        const void* v_new, void* k_cache, void* v_cache, const int32_t* positions,
+                        int32_t cache_slots, const int64_t strides[4][3], void* stream) {
+    if (dtype != PIATTN_F32 && dtype != PIATTN_BF16)
+        return fail(PIATTN_EINVAL, "dtype=%d is not PIATTN_F32 or PIATTN_BF16", (int)dtype);
+    if (S < 1 || H < 1 || (int64_t)S * H > INT32_MAX)
+        return fail(PIATTN_EINVAL, "S=%d H=%d out of range", S, H);
+    if (d < 1) return fail(PIATTN_EINVAL, "d=%d must be positive", d);
+    if (d != 32 && d != 64 && d != 128)
+        return fail(PIATTN_EUNSUPPORTED, "d=%d unsupported (32, 64 or 128)", d);
+    if (cache_slots < 1) return fail(PIATTN_EINVAL, "cache_slots=%d must be positive", cache_slots);
+    if (!strides) return fail(PIATTN_EINVAL, "strides is NULL");
+    if (!positions || !aligned(positions, 4)) return fail(PIATTN_EINVAL, "positions is NULL or misaligned");
+    const int64_t esz = dtype == PIATTN_BF16 ? 2 : 4;
+    const void* ptrs[4] = {k_new, v_new, k_cache, v_cache};
+    const char* names[4] = {"k_new", "v_new", "k_cache", "v_cache"};
+    for (int t = 0; t < 4; ++t) {
+        if (!ptrs[t] || !aligned(ptrs[t], esz)) return fail(PIATTN_EINVAL, "%s is NULL or misaligned", names[t]);
+        for (int j = 0; j < 3; ++j)
+            if (strides[t][j] < 0) return fail(PIATTN_EINVAL, "%s stride[%d] is negative", names[t], j);
+    }
+    if (k_cache == v_cache) return fail(PIATTN_EINVAL, "k_cache and v_cache are the same buffer");
+    AppendArgs a;
+    a.kn = k_new;
+    a.vn = v_new;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.pos = positions;
+    a.skn = Str3{strides[0][0], strides[0][1], 0};
+    a.svn = Str3{strides[1][0], strides[1][1], 0};
+    a.skc = str3(strides[2]);
+    a.svc = str3(strides[3]);
+    a.S = S;
+    a.H = H;
+    a.d = d;
+    a.slots = cache_slots;
+    return launch_status(launch_cache_append(dtype == PIATTN_BF16 ? 1 : 0, a, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

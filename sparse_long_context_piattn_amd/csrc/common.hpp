@@ -29,6 +29,17 @@ struct FwdArgs {
     float scale_log2;    // logit scale * log2(e)
 };
 
+// Appends one token's key and value per (sequence, head) to a rolling cache.
+struct AppendArgs {
+    const void* kn;
+    const void* vn;
+    void* kc;
+    void* vc;
+    const int32_t* pos;  // position of the new token per sequence; < 0: skipped
+    Str3 skn, svn, skc, svc;
+    int32_t S, H, d, slots;
+};
+
 struct DecodeArgs {
     const void* q;
     const void* kc;
@@ -39,6 +50,7 @@ struct DecodeArgs {
     float* ws;           // partials [S*H][splits][d + 2] when splits > 1
     Str3 sq, sk, sv, so, sg;
     int32_t S, H, d, cap;
+    int32_t ring;        // 0: position j in cache row j; else rolling cache, row j mod ring (= cap)
     int32_t splits;
     int32_t chunk;       // union positions per split
     PiPattern pat;

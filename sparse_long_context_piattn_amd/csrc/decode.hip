@@ -26,7 +26,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     const int32_t split = blockIdx.y;
     const int32_t s = sh / a.H, h = sh % a.H;
     const int32_t len = a.lens[s];
-    const bool bad = len < 1 || len > a.cap;
+    const bool bad = len < 1 || (a.ring == 0 && len > a.cap);
 
     RowPartial st;
     st.m = -INFINITY;
@@ -49,7 +49,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         float pl, ps;
         gate_priors(a.g[(int64_t)s * a.sg.s + (int64_t)h * a.sg.h], sp.has_skip(), &pl, &ps);
         gather_row<T, D>(qrow, kb, vb, a.sk.t, a.sv.t, sp, i, a.pat.pi, w0, w1, pl, ps,
-                         a.scale_log2, st);
+                         a.scale_log2, st, a.ring);
         reduce_slots<D>(st);
     }
 
@@ -100,7 +100,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
     const int32_t s = sh / a.H, h = sh % a.H;
     const int c = threadIdx.x;
     const int32_t len = a.lens[s];
-    const bool bad = len < 1 || len > a.cap;
+    const bool bad = len < 1 || (a.ring == 0 && len > a.cap);
     const float* p = a.ws + (int64_t)sh * a.splits * (D + 2);
     float m = -INFINITY;
     for (int32_t sp = 0; sp < a.splits; ++sp) m = fmaxf(m, p[sp * (D + 2)]);
@@ -131,7 +131,41 @@ hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// One (sequence, head) row per workgroup of 64 threads: the new key and
+// value (d elements each) go to row pos mod slots of the rolling cache.
+template <typename T, int D>
+__global__ __launch_bounds__(64) void cache_append_kernel(AppendArgs a) {
+    const int32_t sh = blockIdx.x;
+    const int32_t s = sh / a.H, h = sh % a.H;
+    const int32_t pos = a.pos[s];
+    if (pos < 0) return;
+    const int64_t row = pos % a.slots;
+    const T* kn = static_cast<const T*>(a.kn) + (int64_t)s * a.skn.s + (int64_t)h * a.skn.h;
+    const T* vn = static_cast<const T*>(a.vn) + (int64_t)s * a.svn.s + (int64_t)h * a.svn.h;
+    T* kc = static_cast<T*>(a.kc) + (int64_t)s * a.skc.s + (int64_t)h * a.skc.h + row * a.skc.t;
+    T* vc = static_cast<T*>(a.vc) + (int64_t)s * a.svc.s + (int64_t)h * a.svc.h + row * a.svc.t;
+    for (int c = threadIdx.x; c < D; c += 64) {
+        kc[c] = kn[c];
+        vc[c] = vn[c];
+    }
+}
+
+template <typename T>
+hipError_t append_t(const AppendArgs& a, hipStream_t stream) {
+    switch (a.d) {
+        case 32: hipLaunchKernelGGL((cache_append_kernel<T, 32>), dim3(a.S * a.H), dim3(64), 0, stream, a); break;
+        case 64: hipLaunchKernelGGL((cache_append_kernel<T, 64>), dim3(a.S * a.H), dim3(64), 0, stream, a); break;
+        case 128: hipLaunchKernelGGL((cache_append_kernel<T, 128>), dim3(a.S * a.H), dim3(64), 0, stream, a); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_cache_append(int dtype, const AppendArgs& a, hipStream_t stream) {
+    return dtype == 0 ? append_t<float>(a, stream) : append_t<uint16_t>(a, stream);
+}
 
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t stream) {
     if (dtype == 0) {

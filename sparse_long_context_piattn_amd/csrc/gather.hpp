@@ -68,14 +68,15 @@ struct RowPartial {
 
 // Process union positions [u0, u1) of row i.  kbase/vbase point at token 0
 // of the row's (sequence, head); k_tok_stride / v_tok_stride are the token
-// strides of the key and value tensors.
+// strides of the key and value tensors.  ring > 0: key position j lives in
+// row j mod ring (a rolling cache); 0: in row j.
 template <typename T, int D>
 __device__ __forceinline__ void gather_row(const T* __restrict__ qrow, const T* __restrict__ kbase,
                                            const T* __restrict__ vbase, int64_t k_tok_stride,
                                            int64_t v_tok_stride,
                                            const RowSpan& sp, int32_t i, int32_t pi, int32_t u0,
                                            int32_t u1, float pl, float ps, float scale_log2,
-                                           RowPartial& st) {
+                                           RowPartial& st, int32_t ring = 0) {
     using G = GatherShape<D>;
     const int lane = threadIdx.x & 63;
     const int slot = lane / G::LPK;
@@ -89,6 +90,7 @@ __device__ __forceinline__ void gather_row(const T* __restrict__ qrow, const T* 
 #pragma unroll
     for (int j = 0; j < 8; ++j) st.acc[j] = 0.0f;
 
+    const int32_t ri = ring > 0 ? i % ring : 0;          // row of position i in a rolling cache
     for (int32_t base = u0; base < u1; base += G::NS) {
         const int32_t u = base + slot;
         const bool valid = u < u1;
@@ -96,7 +98,11 @@ __device__ __forceinline__ void gather_row(const T* __restrict__ qrow, const T* 
         float prior = 0.0f;
         if (valid) {
             bool loc;
-            const int32_t key = span_key(sp, i, pi, u, &loc);
+            int32_t key = span_key(sp, i, pi, u, &loc);
+            if (ring > 0) {                               // key >= i - ring + 1: row (i - delta) mod ring
+                const int32_t r = ri - (i - key);
+                key = r < 0 ? r + ring : r;
+            }
             Elem<T>::load8(kbase + (int64_t)key * k_tok_stride + c, kv);
             Elem<T>::load8(vbase + (int64_t)key * v_tok_stride + c, vv);
             prior = loc ? pl : ps;

@@ -169,3 +169,45 @@ def test_neighbors_empty_range_is_a_no_op():
     L = pa.lib()
     p = pa.make_pattern(8, 16, 4)
     assert L.piattn_neighbors(16, ctypes.byref(p), 3, 0, 13, None, None, None, None) == 0
+
+
+def test_rolling_slots_query():
+    L = pa.lib()
+    assert pa.rolling_slots(8, 16, 4) == 65                   # max(8, 4*16) + 1
+    assert pa.rolling_slots(256, 512, 63) == 63 * 512 + 1
+    assert pa.rolling_slots(64, 32, 2) == 65                  # M < k/pi + 1: no skip keys, k + 1
+    assert pa.rolling_slots(100, 16, 0) == 101
+    assert L.piattn_rolling_slots(ctypes.byref(pa.make_pattern(4, 0, 2))) == -1
+    assert L.piattn_rolling_slots(ctypes.byref(pa.make_pattern(4, 1 << 20, 1 << 12))) == -1   # >= 2^30
+
+
+def test_decode_rolling_rejects_a_short_cache():
+    L = pa.lib()
+    st = binding.Strides(*([2 * 128, 128, 0] + [2 * 100 * 128, 100 * 128, 128] * 2 +
+                           [2 * 128, 128, 0] + [2, 1, 0]))
+    p = pa.make_pattern(8, 16, 4)                             # needs 65 rows
+    for slots, expect in ((64, EINVAL), (65, None)):
+        rc = L.piattn_decode_rolling(1, 2, 2, 128, A, A2, A3, A, slots, A, OUT, ctypes.byref(st),
+                                     ctypes.byref(p), 4, None, 0, None)
+        if expect is not None:
+            assert rc == expect and "rolling" in L.piattn_last_error().decode()
+        else:
+            assert rc == EWORKSPACE                           # passes the size check, stops at the workspace
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(pos=None), EINVAL),
+    (dict(d=48), EUNSUPPORTED),
+    (dict(slots=0), EINVAL),
+    (dict(S=0), EINVAL),
+    (dict(kc=A2, vc=A2), EINVAL),
+    (dict(kn=None), EINVAL),
+])
+def test_cache_append_rejects_bad_arguments(kw, expect):
+    L = pa.lib()
+    args = dict(dtype=1, S=2, H=2, d=64, kn=A, vn=A3, kc=A2, vc=OUT, pos=A, slots=16)
+    args.update(kw)
+    st = binding.Strides4(*([128, 64, 0] * 2 + [2 * 16 * 64, 16 * 64, 64] * 2))
+    rc = L.piattn_cache_append(args["dtype"], args["S"], args["H"], args["d"], args["kn"], args["vn"],
+                               args["kc"], args["vc"], args["pos"], args["slots"], ctypes.byref(st), None)
+    assert rc == expect and L.piattn_last_error().decode()
