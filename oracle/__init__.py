@@ -60,6 +60,9 @@ def _load():
         lib.oracle_decode.restype = None
         lib.oracle_neighbor_table.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32, vp, vp, vp]
         lib.oracle_neighbor_table.restype = i32
+        lib.oracle_bwd.argtypes = [i32, vp, i32, i32, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32,
+                                   i32, dbl, vp, vp, vp, vp]
+        lib.oracle_bwd.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         _lib = lib
@@ -162,3 +165,28 @@ def decode(q, k_cache, v_cache, lens, g, kw: int, pi: int, M: int, scale: float,
     _load().oracle_decode(S, H, d, _ptr(q), _ptr(kc), _ptr(vc), dt, _ptr(cs), _ptr(lens),
                           _ptr(g), kw, pi, M, float(scale), _ptr(out), _ptr(lse), int(nthreads))
     return (out, lse) if want_lse else out
+
+
+def bwd(q, k, v, g, dout, cu_seqlens, kw: int, pi: int, M: int, bidir: bool, scale: float):
+    """Gradients of sum(dout * out) for the prefill over a packed batch.
+
+    q, k, v, dout: [T, H, d] (float64 / float32 / bf16-bits uint16); g: [T, H];
+    cu_seqlens: [nseq + 1].  Returns dq, dk, dv [T, H, d] and dg [T, H], fp64.
+    """
+    q, dt = _as_input(q)
+    k, dtk = _as_input(k)
+    v, dtv = _as_input(v)
+    dout, dtd = _as_input(dout)
+    assert dt == dtk == dtv and q.shape == k.shape == v.shape == dout.shape and q.ndim == 3
+    T, H, d = q.shape
+    g = np.ascontiguousarray(g, dtype=np.float64).reshape(T, H)
+    cu = np.ascontiguousarray(cu_seqlens, dtype=np.int64)
+    assert cu[0] == 0 and cu[-1] == T
+    dq = np.zeros((T, H, d), np.float64)
+    dk = np.zeros((T, H, d), np.float64)
+    dv = np.zeros((T, H, d), np.float64)
+    dg = np.zeros((T, H), np.float64)
+    _load().oracle_bwd(len(cu) - 1, _ptr(cu), H, d, _ptr(q), _ptr(k), _ptr(v), dt, _ptr(g),
+                       _ptr(dout), dtd, kw, pi, M, int(bool(bidir)), float(scale), _ptr(dq),
+                       _ptr(dk), _ptr(dv), _ptr(dg))
+    return dq, dk, dv, dg

@@ -274,6 +274,95 @@ void oracle_decode(int S, int H, int d, const void *q, const void *kc,
     }
 }
 
+/*
+ * Backward of the prefill over a packed batch (every row; single-threaded,
+ * since the key-side gradients are scattered).  dout [T, H, d] (element
+ * type dtd) is the gradient of the loss with respect to out; the results are
+ * the gradients with respect to q, k, v ([T, H, d] fp64, zeroed here) and
+ * the gate logits g ([T, H] fp64).  It is the chain rule through the one
+ * softmax of each row, with the row's logits recomputed:
+ *   P_a      = softmax(logit)_a over the row's neighbours j_a
+ *   dP_a     = <dout_i, v_{j_a}>,   D = sum_a P_a dP_a   (= <dout_i, out_i>)
+ *   dlogit_a = P_a (dP_a - D)
+ *   dq_i    += scale dlogit_a k_{j_a}
+ *   dk_{j_a}+= scale dlogit_a q_i
+ *   dv_{j_a}+= P_a dout_i
+ *   dg_i    += dlogit_a * d prior_a / d g_i: d log(sigmoid(g)) / dg =
+ *              1 - sigmoid(g) for a local key, d log(1 - sigmoid(g)) / dg =
+ *              -sigmoid(g) for a skip key, and no term when the row has no
+ *              skip key (it has no prior).
+ */
+void oracle_bwd(int nseq, const int64_t *cu, int H, int d, const void *q,
+                const void *kk, const void *vv, int dt, const double *g,
+                const void *dout, int dtd, int kw, int pi, int M, int bidir,
+                double scale, double *dq, double *dk, double *dv, double *dg)
+{
+    int64_t T = cu[nseq];
+    int cap = list_cap(kw, M);
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * cap);
+    int8_t *kind = (int8_t *)malloc((size_t)cap);
+    double *sc = (double *)malloc(sizeof(double) * cap);
+    double *dp = (double *)malloc(sizeof(double) * cap);
+    int s, h, i, a, c;
+
+    memset(dq, 0, sizeof(double) * (size_t)(T * H * d));
+    memset(dk, 0, sizeof(double) * (size_t)(T * H * d));
+    memset(dv, 0, sizeof(double) * (size_t)(T * H * d));
+    memset(dg, 0, sizeof(double) * (size_t)(T * H));
+    for (s = 0; s < nseq; ++s) {
+        int n = (int)(cu[s + 1] - cu[s]);
+        for (h = 0; h < H; ++h) {
+            int64_t base = (cu[s] * H + h) * (int64_t)d; /* token 0 of this (sequence, head) */
+            int64_t ts = (int64_t)H * d;                 /* token stride */
+            for (i = 0; i < n; ++i) {
+                int64_t qo = base + i * ts, go = (cu[s] + i) * H + h;
+                int cnt = oracle_neighbors(n, kw, pi, M, bidir, i, idx, kind);
+                int has_skip = 0;
+                double ga = g[go], mx = -INFINITY, z = 0.0, D = 0.0;
+                double alpha = 1.0 / (1.0 + exp(-ga));
+                for (a = 0; a < cnt; ++a)
+                    if (kind[a] == KIND_SKIP)
+                        has_skip = 1;
+                for (a = 0; a < cnt; ++a) {
+                    int64_t ko = base + idx[a] * ts;
+                    double dot = 0.0, dpa = 0.0;
+                    for (c = 0; c < d; ++c) {
+                        dot += load_elem(q, qo + c, dt) * load_elem(kk, ko + c, dt);
+                        dpa += load_elem(dout, qo + c, dtd) * load_elem(vv, ko + c, dt);
+                    }
+                    sc[a] = dot * scale;
+                    if (has_skip)
+                        sc[a] += (kind[a] == KIND_LOCAL) ? log_sigmoid(ga) : log_sigmoid(-ga);
+                    dp[a] = dpa;
+                    if (sc[a] > mx)
+                        mx = sc[a];
+                }
+                for (a = 0; a < cnt; ++a)
+                    z += exp(sc[a] - mx);
+                for (a = 0; a < cnt; ++a) {
+                    sc[a] = exp(sc[a] - mx) / z; /* now P_a */
+                    D += sc[a] * dp[a];
+                }
+                for (a = 0; a < cnt; ++a) {
+                    int64_t ko = base + idx[a] * ts;
+                    double ds = sc[a] * (dp[a] - D);
+                    for (c = 0; c < d; ++c) {
+                        dq[qo + c] += scale * ds * load_elem(kk, ko + c, dt);
+                        dk[ko + c] += scale * ds * load_elem(q, qo + c, dt);
+                        dv[ko + c] += sc[a] * load_elem(dout, qo + c, dtd);
+                    }
+                    if (has_skip)
+                        dg[go] += ds * ((kind[a] == KIND_LOCAL) ? (1.0 - alpha) : -alpha);
+                }
+            }
+        }
+    }
+    free(idx);
+    free(kind);
+    free(sc);
+    free(dp);
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP

@@ -24,6 +24,11 @@ MUTATIONS = {
     "softplus_sign": ("return -log1p(exp(-x));", "return -log1p(exp(x));"),
     "v_read_from_k": ("out[c] += w * load_elem(vv, vb + c, dt);",
                       "out[c] += w * load_elem(kk, vb + c, dt);"),
+    # the backward
+    "bwd_dk_scale_dropped": ("dk[ko + c] += scale * ds *", "dk[ko + c] += ds *"),
+    "bwd_skip_gate_sign": ("? (1.0 - alpha) : -alpha)", "? (1.0 - alpha) : alpha)"),
+    "bwd_dv_uses_dlogit": ("dv[ko + c] += sc[a] *", "dv[ko + c] += ds *"),
+    "bwd_D_dropped": ("double ds = sc[a] * (dp[a] - D);", "double ds = sc[a] * dp[a];"),
 }
 
 

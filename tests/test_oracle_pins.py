@@ -285,3 +285,67 @@ def test_bf16_inputs_read_exactly(oracle_lib):
     a = oracle.fwd(bits, bits, bits, g, [0, n], 2, 3, 2, False, 0.3)
     b = oracle.fwd(as64, as64, as64, g, [0, n], 2, 3, 2, False, 0.3)
     np.testing.assert_array_equal(a, b)
+
+
+# ---------------------------------------------------------------- backward
+# The backward oracle is pinned to central finite differences of the
+# forward oracle (itself pinned above): for L = sum(dout * out), every
+# element of q, k, v and g is moved by +-h and (L+ - L-) / 2h compared with
+# the analytic gradient.  The truncation error is O(h^2 * third derivative)
+# and the rounding error O(eps * |L| / h): with h = 1e-5 both stay below 1e-7.
+
+def _fd_case(seed, lens, H, d, kw, pi, M, bidir, scale, gstd=1.5):
+    T = sum(lens)
+    q, k, v = (_rand((T, H, d), seed + i) for i in range(3))
+    g = _rand((T, H), seed + 3, gstd)
+    dout = _rand((T, H, d), seed + 4)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    return q, k, v, g, dout, cu
+
+
+def _loss(q, k, v, g, dout, cu, kw, pi, M, bidir, scale):
+    out = oracle.fwd(q, k, v, g, cu, kw, pi, M, bidir, scale)
+    return float((out * dout.reshape(out.shape)).sum())
+
+
+@pytest.mark.parametrize("bidir", [False, True])
+@pytest.mark.parametrize("kw,pi,M", [(2, 3, 2), (0, 2, 3), (4, 3, 1), (3, 1, 2)])
+def test_backward_matches_finite_differences(oracle_lib, bidir, kw, pi, M):
+    lens = [9, 13]
+    q, k, v, g, dout, cu = _fd_case(7 * kw + pi + 11 * M + int(bidir), lens, 2, 3, kw, pi, M, bidir, 0.7)
+    args = (kw, pi, M, bidir, 0.7)
+    dq, dk, dv, dg = oracle.bwd(q, k, v, g, dout, cu, *args)
+    h = 1e-5
+    worst = 0.0
+    for name, x, gx in (("q", q, dq), ("k", k, dk), ("v", v, dv), ("g", g, dg)):
+        flat, gflat = x.reshape(-1), gx.reshape(-1)
+        for e in range(flat.size):
+            keep = flat[e]
+            flat[e] = keep + h
+            lp = _loss(q, k, v, g, dout, cu, *args)
+            flat[e] = keep - h
+            lm = _loss(q, k, v, g, dout, cu, *args)
+            flat[e] = keep
+            fd = (lp - lm) / (2 * h)
+            worst = max(worst, abs(fd - gflat[e]))
+            assert abs(fd - gflat[e]) <= 1e-6 * max(1.0, abs(fd)), (name, e, fd, gflat[e])
+    assert worst <= 1e-6
+
+
+def test_backward_gate_gradient_vanishes_without_skips(oracle_lib):
+    # M = 0: no row has skip keys, so no prior and no dependence on g
+    q, k, v, g, dout, cu = _fd_case(3, [12], 2, 4, 3, 4, 0, False, 0.5)
+    dq, dk, dv, dg = oracle.bwd(q, k, v, g, dout, cu, 3, 4, 0, False, 0.5)
+    assert not dg.any()
+    assert np.abs(dq).max() > 0 and np.abs(dv).max() > 0
+
+
+def test_backward_dv_columns_sum_to_dout(oracle_lib):
+    # each row's softmax weights sum to 1, so summed over all keys dv equals
+    # dout summed over all rows (per sequence and head)
+    lens = [10, 7]
+    q, k, v, g, dout, cu = _fd_case(5, lens, 3, 4, 2, 3, 2, True, 0.9)
+    dq, dk, dv, dg = oracle.bwd(q, k, v, g, dout, cu, 2, 3, 2, True, 0.9)
+    for s in range(len(lens)):
+        sl = slice(cu[s], cu[s + 1])
+        np.testing.assert_allclose(dv[sl].sum(axis=0), dout[sl].sum(axis=0), rtol=0, atol=1e-12)
