@@ -219,6 +219,54 @@ def bench_decode(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
+def bench_backward(args, w, dev, sets, outs, fwd_step, lengths, rows):
+    """Time piattn_bwd (gradients of q, k, v and the gate logits) on the
+    workload; the forward outputs it needs are computed first, untimed.
+    Algorithmic bytes per row: q, k, v, out, dout read and dq, dk, dv written
+    once (8 d e) plus the fp32 gate logit read and its gradient written."""
+    import torch
+
+    import sparse_long_context_piattn_amd as pa
+
+    nsets = len(sets)
+    for j in range(nsets):
+        fwd_step(j)
+    douts = []
+    for j, x in enumerate(sets):
+        gen = torch.Generator(device=dev).manual_seed(1000 + j)
+        douts.append(torch.randn(x["q"].shape, generator=gen, device=dev).to(x["q"].dtype))
+    e = 2 if w.dtype == "bf16" else 4
+    alg_bytes = rows * (8 * w.d * e + 8)
+    nb = pa.binding.lib().piattn_bwd_workspace_bytes(len(lengths) if lengths else w.B, w.H,
+                                                       max(lengths) if lengths else w.n)
+    ws = torch.empty(nb, dtype=torch.uint8, device=dev)
+
+    def step(j):
+        x = sets[j % nsets]
+        pa.bwd(x["q"], x["k"], x["v"], x["g"], outs[j % nsets], douts[j % nsets], window_k=w.k,
+               period_pi=w.pi, num_skips=w.M, bidirectional=w.bidir, cu_seqlens=x.get("cu_seqlens"),
+               max_seqlen=max(lengths) if lengths else None, workspace=ws)
+
+    ms_per_step = timed(step, args, dev)
+    sec = ms_per_step / 1e3
+    gbps = alg_bytes / sec / 1e9
+    log("backward: %.4f ms/step  %.3e rows/s  %.0f GB/s (%.1f%% of HBM peak)"
+        % (ms_per_step, rows / sec, gbps, 100 * gbps / HBM_PEAK_GBPS))
+    res = {"metric": "pi-attn backward (dq, dk, dv, d gate) query rows/s, 1 GPU", "value": round(rows / sec, 1),
+           "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "bf16" if w.dtype == "bf16" else "f32",
+           "data": "synthetic (seeded N(0,1) q/k/v/dout, N(0,1) gate logits)",
+           "config": {"workload": w.name, "pass": "backward", "B": w.B if not w.nseq else len(lengths),
+                      "H": w.H, "n": w.n if not w.nseq else max(lengths), "d": w.d, "k": w.k, "pi": w.pi,
+                      "M": w.M, "bidirectional": w.bidir},
+           "kernel_digest": kernel_digest(),
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+           "cpu_baseline": None}
+    print(json.dumps(res), flush=True)
+
+
 COPY_ELEMS = 256 << 20          # bf16 elements of the calibration copy (512 MiB each way)
 
 
@@ -317,6 +365,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
     ap.add_argument("--splits", type=int, default=0, help="decode key-range splits (0 = auto)")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward (piattn_bwd) instead of the forward (prefill workloads)")
     ap.add_argument("--rolling", action="store_true",
                     help="decode over a rolling cache of max(k, M pi) + 1 rows")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -367,6 +417,9 @@ def main():
         pa.fwd(x["q"], x["k"], x["v"], x["g"], window_k=w.k, period_pi=w.pi, num_skips=w.M,
                bidirectional=w.bidir, cu_seqlens=x.get("cu_seqlens"),
                max_seqlen=max(lengths) if lengths else None, out=outs[j % nsets], workspace=ws)
+
+    if args.backward:
+        return bench_backward(args, w, dev, sets, outs, step, lengths, rows)
 
     ms_per_step = timed(step, args, dev)
     if args.calibrate_copy:

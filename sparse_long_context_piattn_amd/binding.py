@@ -21,7 +21,8 @@ PIATTN_F32, PIATTN_BF16 = 0, 1
 STATUS = {0: "PIATTN_OK", 1: "PIATTN_EINVAL", 2: "PIATTN_EUNSUPPORTED", 3: "PIATTN_EWORKSPACE",
           4: "PIATTN_EHIP"}
 
-EXPORTS = ["piattn_fwd", "piattn_fwd_workspace_bytes", "piattn_decode", "piattn_decode_workspace_bytes",
+EXPORTS = ["piattn_fwd", "piattn_fwd_workspace_bytes", "piattn_bwd", "piattn_bwd_workspace_bytes",
+           "piattn_decode", "piattn_decode_workspace_bytes",
            "piattn_decode_auto_splits", "piattn_rolling_slots", "piattn_cache_append",
            "piattn_decode_rolling", "piattn_neighbors", "piattn_neighbors_cap",
            "piattn_last_error", "piattn_version"]
@@ -60,6 +61,11 @@ def lib():
         L.piattn_fwd.restype = ctypes.c_int
         L.piattn_fwd_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, pat]
         L.piattn_fwd_workspace_bytes.restype = sz
+        L.piattn_bwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                 ctypes.POINTER(Strides), vp, pat, vp, sz, vp]
+        L.piattn_bwd.restype = ctypes.c_int
+        L.piattn_bwd_workspace_bytes.argtypes = [i32, i32, i32]
+        L.piattn_bwd_workspace_bytes.restype = sz
         L.piattn_decode.argtypes = [ctypes.c_int, i32, i32, i32, vp, vp, vp, vp, i32, vp, vp,
                                     ctypes.POINTER(Strides), pat, i32, vp, sz, vp]
         L.piattn_decode.restype = ctypes.c_int
@@ -117,6 +123,47 @@ def _need_cuda(*ts):
             raise ValueError("tensors must live on the GPU")
 
 
+def _prefill_geometry(q, k, v, g, out, cu_seqlens, max_seqlen):
+    """(B, H, n, d, strides, cu pointer) of a prefill call, or None when the
+    varlen batch is empty.  Dense: q, k, v, out [B, H, n, d], g [B, H, n];
+    varlen: [T, H, d] and g [T, H] with cu_seqlens int32 [B + 1]."""
+    if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError("dense mode expects q [B, H, n, d]")
+        B, H, n, d = q.shape
+        if k.shape != q.shape or v.shape != q.shape or out.shape != q.shape:
+            raise ValueError("q, k, v, out shapes differ")
+        if tuple(g.shape) != (B, H, n):
+            raise ValueError("g must be [B, H, n]")
+        st4 = [tuple(t.stride()[:3]) for t in (q, k, v, out)]
+        gst = tuple(g.stride())
+        cu_ptr = None
+    else:
+        if q.dim() != 3:
+            raise ValueError("varlen mode expects q [T, H, d]")
+        T, H, d = q.shape
+        if k.shape != q.shape or v.shape != q.shape or out.shape != q.shape:
+            raise ValueError("q, k, v, out shapes differ")
+        if tuple(g.shape) != (T, H):
+            raise ValueError("g must be [T, H]")
+        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+            raise ValueError("cu_seqlens must be a 1-D int32 tensor")
+        B = cu_seqlens.numel() - 1
+        if max_seqlen is None:
+            cu_h = cu_seqlens.cpu()
+            max_seqlen = int((cu_h[1:] - cu_h[:-1]).max()) if B > 0 else 0
+        n = int(max_seqlen)
+        if n == 0:
+            return None
+        st4 = [(0, t.stride(1), t.stride(0)) for t in (q, k, v, out)]
+        gst = (0, g.stride(1), g.stride(0))
+        cu_ptr = _ptr(cu_seqlens)
+    for t in (q, k, v, out):
+        if t.stride(-1) != 1:
+            raise ValueError("the head dimension must be contiguous")
+    return B, H, n, d, Strides(*[x for s in st4 for x in s], *gst), cu_ptr
+
+
 def fwd_workspace_bytes(dtype_code: int, B: int, H: int, n: int, d: int, pattern: Pattern) -> int:
     return int(lib().piattn_fwd_workspace_bytes(dtype_code, B, H, n, d, ctypes.byref(pattern)))
 
@@ -144,45 +191,12 @@ def fwd(q, k, v, g, *, window_k: int, period_pi: int, num_skips: int, bidirectio
         out = torch.empty_like(q)
     if q.numel() == 0 or (cu_seqlens is not None and cu_seqlens.numel() <= 1):
         return out  # nothing to attend
-    if cu_seqlens is None:
-        if q.dim() != 4:
-            raise ValueError("dense mode expects q [B, H, n, d]")
-        B, H, n, d = q.shape
-        if k.shape != q.shape or v.shape != q.shape or out.shape != q.shape:
-            raise ValueError("q, k, v, out shapes differ")
-        if tuple(g.shape) != (B, H, n):
-            raise ValueError("g must be [B, H, n]")
-        st4 = [tuple(t.stride()[:3]) for t in (q, k, v, out)]
-        gst = tuple(g.stride())
-        if lse is not None and (tuple(lse.shape) != (B, H, n) or lse.stride() != g.stride()):
-            raise ValueError("lse must have g's shape and strides")
-        cu_ptr = None
-    else:
-        if q.dim() != 3:
-            raise ValueError("varlen mode expects q [T, H, d]")
-        T, H, d = q.shape
-        if k.shape != q.shape or v.shape != q.shape or out.shape != q.shape:
-            raise ValueError("q, k, v, out shapes differ")
-        if tuple(g.shape) != (T, H):
-            raise ValueError("g must be [T, H]")
-        if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
-            raise ValueError("cu_seqlens must be a 1-D int32 tensor")
-        B = cu_seqlens.numel() - 1
-        if max_seqlen is None:
-            cu_h = cu_seqlens.cpu()
-            max_seqlen = int((cu_h[1:] - cu_h[:-1]).max()) if B > 0 else 0
-        n = int(max_seqlen)
-        if n == 0:
-            return out
-        st4 = [(0, t.stride(1), t.stride(0)) for t in (q, k, v, out)]
-        gst = (0, g.stride(1), g.stride(0))
-        if lse is not None and (tuple(lse.shape) != (T, H) or lse.stride() != g.stride()):
-            raise ValueError("lse must have g's shape and strides")
-        cu_ptr = _ptr(cu_seqlens)
-    for t in (q, k, v, out):
-        if t.stride(-1) != 1:
-            raise ValueError("the head dimension must be contiguous")
-    strides = Strides(*[x for s in st4 for x in s], *gst)
+    geo = _prefill_geometry(q, k, v, g, out, cu_seqlens, max_seqlen)
+    if geo is None:
+        return out
+    B, H, n, d, strides, cu_ptr = geo
+    if lse is not None and (lse.shape != g.shape or lse.stride() != g.stride()):
+        raise ValueError("lse must have g's shape and strides")
     pat = make_pattern(window_k, period_pi, num_skips, bidirectional, scale)
     need = fwd_workspace_bytes(code, B, H, n, d, pat)
     if workspace is None and need:
@@ -194,6 +208,44 @@ def fwd(q, k, v, g, *, window_k: int, period_pi: int, num_skips: int, bidirectio
                           _ptr(workspace), wbytes, ctypes.c_void_p(_stream(q.device)))
     _check(rc)
     return out
+
+
+def bwd(q, k, v, g, out, dout, *, window_k: int, period_pi: int, num_skips: int, bidirectional=False,
+        scale: float = 0.0, cu_seqlens=None, max_seqlen: int | None = None, workspace=None):
+    """Backward of fwd: the gradients (dq, dk, dv, dg) of a loss whose gradient
+    with respect to fwd's output `out` is `dout`.  dq, dk, dv have the shapes
+    and strides of q, k, v (allocated like them); dg is fp32 like g.  dout
+    must have out's strides."""
+    code = _dtype_code(q)
+    _need_cuda(q, k, v, g, out, dout, cu_seqlens, workspace)
+    for t in (k, v, out, dout):
+        if t.dtype != q.dtype:
+            raise TypeError("q, k, v, out, dout must share a dtype")
+    if g.dtype != torch.float32:
+        raise TypeError("gate logits must be float32")
+    if dout.shape != out.shape or dout.stride() != out.stride():
+        raise ValueError("dout must have out's shape and strides")
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dg = torch.empty_like(g)
+    if q.numel() == 0:
+        return dq, dk, dv, dg
+    if not (dq.stride() == q.stride() and dk.stride() == k.stride() and dv.stride() == v.stride()
+            and dg.stride() == g.stride()):
+        raise ValueError("q, k, v and g must be dense (gradients take their strides)")
+    geo = _prefill_geometry(q, k, v, g, out, cu_seqlens, max_seqlen)
+    if geo is None:
+        return dq, dk, dv, dg
+    B, H, n, d, strides, cu_ptr = geo
+    pat = make_pattern(window_k, period_pi, num_skips, bidirectional, scale)
+    need = int(lib().piattn_bwd_workspace_bytes(B, H, n))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    rc = lib().piattn_bwd(code, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out), _ptr(dout),
+                          _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), ctypes.byref(strides), cu_ptr,
+                          ctypes.byref(pat), _ptr(workspace), wbytes, ctypes.c_void_p(_stream(q.device)))
+    _check(rc)
+    return dq, dk, dv, dg
 
 
 def decode_workspace_bytes(S, H, d, num_splits, pattern: Pattern) -> int:

@@ -49,10 +49,9 @@ int check_pattern(const piattn_pattern* p, PiPattern* out) {
     return PIATTN_OK;
 }
 
-float scale_log2(const piattn_pattern* p, int d) {
-    const float s = p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)d);
-    return s * 1.4426950408889634f;
-}
+float scale_nat(const piattn_pattern* p, int d) { return p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)d); }
+
+float scale_log2(const piattn_pattern* p, int d) { return scale_nat(p, d) * 1.4426950408889634f; }
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -142,14 +141,17 @@ size_t piattn_fwd_workspace_bytes(piattn_dtype dtype, int32_t B, int32_t H, int3
     return fwd_split_workspace(dtype, B, H, n, d, p);
 }
 
-int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, const void* q,
-               const void* k, const void* v, const float* gate_logits, void* out, float* lse_out,
-               const int64_t strides[5][3], const int32_t* cu_seqlens,
-               const piattn_pattern* pattern, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+// Validates the arguments piattn_fwd and piattn_bwd share and fills a.
+static int fwd_args(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, const void* q,
+                    const void* k, const void* v, const float* gate_logits, void* out, float* lse_out,
+                    const int64_t strides[5][3], const int32_t* cu_seqlens, const piattn_pattern* pattern,
+                    FwdArgs& a, PiPattern& p) {
+    int rc;
     if (dtype != PIATTN_F32 && dtype != PIATTN_BF16)
         return fail(PIATTN_EINVAL, "dtype=%d is not PIATTN_F32 or PIATTN_BF16", (int)dtype);
-    PiPattern p;
-    int rc = check_pattern(pattern, &p);
+    rc = check_pattern(pattern, &p);
     if (rc) return rc;
     if (B < 1 || B > 65535) return fail(PIATTN_EINVAL, "B=%d out of range [1, 65535]", B);
     if (H < 1 || H > 65535) return fail(PIATTN_EINVAL, "H=%d out of range [1, 65535]", H);
@@ -174,7 +176,6 @@ int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
     if (!dense && !aligned(cu_seqlens, 4))
         return fail(PIATTN_EINVAL, "cu_seqlens must be 4-byte aligned");
 
-    FwdArgs a;
     a.q = q;
     a.k = k;
     a.v = v;
@@ -193,6 +194,20 @@ int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
     a.d = d;
     a.pat = p;
     a.scale_log2 = scale_log2(pattern, d);
+    return PIATTN_OK;
+}
+
+extern "C" {
+
+int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, const void* q,
+               const void* k, const void* v, const float* gate_logits, void* out, float* lse_out,
+               const int64_t strides[5][3], const int32_t* cu_seqlens,
+               const piattn_pattern* pattern, void* workspace, size_t workspace_bytes, void* stream) {
+    FwdArgs a;
+    PiPattern p;
+    const int rc = fwd_args(dtype, B, H, n, d, q, k, v, gate_logits, out, lse_out, strides, cu_seqlens,
+                            pattern, a, p);
+    if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int dt = dtype == PIATTN_BF16 ? 1 : 0;
     // Kernel choice.  PIATTN_FWD_KERNEL = split | resid | gather forces
@@ -219,6 +234,49 @@ int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
     if (fwd_split_supported(dt, a)) return split();
     if (fwd_resid_supported(dt, a)) return launch_status(launch_fwd_resid(a, st));
     return launch_status(launch_fwd_gather(dt, a, st));
+}
+
+size_t piattn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t n) {
+    if (B < 1 || H < 1 || n < 1) return 0;
+    return (size_t)B * H * n * 2 * sizeof(float);
+}
+
+int piattn_bwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, const void* q, const void* k,
+               const void* v, const float* gate_logits, const void* out, const void* dout, void* dq, void* dk,
+               void* dv, float* dgate, const int64_t strides[5][3], const int32_t* cu_seqlens,
+               const piattn_pattern* pattern, void* workspace, size_t workspace_bytes, void* stream) {
+    BwdArgs ba;
+    PiPattern p;
+    int rc = fwd_args(dtype, B, H, n, d, q, k, v, gate_logits, const_cast<void*>(out), nullptr, strides,
+                      cu_seqlens, pattern, ba.f, p);
+    if (rc) return rc;
+    const int64_t mult = dtype == PIATTN_BF16 ? 8 : 4;
+    const bool dense = cu_seqlens == nullptr;
+    if ((rc = check_tensor("dout", dout, strides[3], mult, dense))) return rc;
+    if ((rc = check_tensor("dq", dq, strides[0], mult, dense))) return rc;
+    if ((rc = check_tensor("dk", dk, strides[1], mult, dense))) return rc;
+    if ((rc = check_tensor("dv", dv, strides[2], mult, dense))) return rc;
+    if (!dgate || !aligned(dgate, 4)) return fail(PIATTN_EINVAL, "dgate is NULL or misaligned");
+    const void* ins[5] = {q, k, v, out, dout};
+    void* outs[3] = {dq, dk, dv};
+    for (void* o : outs)
+        for (const void* in : ins)
+            if (o == in) return fail(PIATTN_EINVAL, "a gradient aliases an input");
+    if (dq == dk || dq == dv || dk == dv) return fail(PIATTN_EINVAL, "gradients alias each other");
+    if (static_cast<const void*>(dgate) == gate_logits) return fail(PIATTN_EINVAL, "dgate aliases gate_logits");
+    const size_t need = piattn_bwd_workspace_bytes(B, H, n);
+    if (!workspace) return fail(PIATTN_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+        return fail(PIATTN_EWORKSPACE, "workspace of %zu bytes is smaller than %zu", workspace_bytes, need);
+    if (!aligned(workspace, 256)) return fail(PIATTN_EINVAL, "workspace is not 256-byte aligned");
+    ba.dout = dout;
+    ba.dq = dq;
+    ba.dk = dk;
+    ba.dv = dv;
+    ba.dg = dgate;
+    ba.rowstat = static_cast<float*>(workspace);
+    ba.scale = scale_nat(pattern, d);
+    return launch_status(launch_bwd(dtype == PIATTN_BF16 ? 1 : 0, ba, static_cast<hipStream_t>(stream)));
 }
 
 size_t piattn_decode_workspace_bytes(int32_t S, int32_t H, int32_t d, int32_t num_splits,

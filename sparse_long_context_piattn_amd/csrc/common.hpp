@@ -29,6 +29,20 @@ struct FwdArgs {
     float scale_log2;    // logit scale * log2(e)
 };
 
+// Backward of the prefill: the forward's arguments (o = its output), plus the
+// incoming gradient and the gradients written.  dq, dk, dv use the strides of
+// q, k, v; dout those of o; dg those of g.
+struct BwdArgs {
+    FwdArgs f;
+    const void* dout;
+    void* dq;
+    void* dk;
+    void* dv;
+    float* dg;
+    float* rowstat;      // workspace: per row (log2-sum-exp, D), [B][H][n][2]
+    float scale;         // logit scale (natural units)
+};
+
 // Appends one token's key and value per (sequence, head) to a rolling cache.
 struct AppendArgs {
     const void* kn;
