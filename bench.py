@@ -219,24 +219,29 @@ def bench_decode(args, w, dev):
     print(json.dumps(res), flush=True)
 
 
-def bench_backward(args, w, dev, sets, outs, fwd_step, lengths, rows):
+def bench_backward(args, w, dev, sets, outs, lengths, rows):
     """Time piattn_bwd (gradients of q, k, v and the gate logits) on the
-    workload; the forward outputs it needs are computed first, untimed.
-    Algorithmic bytes per row: q, k, v, out, dout read and dq, dk, dv written
-    once (8 d e) plus the fp32 gate logit read and its gradient written."""
+    workload; the forward outputs and log-sum-exp it takes are computed
+    first, untimed.  Algorithmic bytes per row: q, k, v, out, dout read and
+    dq, dk, dv written once (8 d e), the fp32 gate logit and lse read and the
+    gate gradient written (12)."""
     import torch
 
     import sparse_long_context_piattn_amd as pa
 
     nsets = len(sets)
-    for j in range(nsets):
-        fwd_step(j)
+    lses = []
+    for j, x in enumerate(sets):
+        lses.append(torch.empty_like(x["g"]))
+        pa.fwd(x["q"], x["k"], x["v"], x["g"], window_k=w.k, period_pi=w.pi, num_skips=w.M,
+               bidirectional=w.bidir, cu_seqlens=x.get("cu_seqlens"),
+               max_seqlen=max(lengths) if lengths else None, out=outs[j], lse=lses[j])
     douts = []
     for j, x in enumerate(sets):
         gen = torch.Generator(device=dev).manual_seed(1000 + j)
         douts.append(torch.randn(x["q"].shape, generator=gen, device=dev).to(x["q"].dtype))
     e = 2 if w.dtype == "bf16" else 4
-    alg_bytes = rows * (8 * w.d * e + 8)
+    alg_bytes = rows * (8 * w.d * e + 12)
     nb = pa.binding.lib().piattn_bwd_workspace_bytes(len(lengths) if lengths else w.B, w.H,
                                                        max(lengths) if lengths else w.n)
     ws = torch.empty(nb, dtype=torch.uint8, device=dev)
@@ -245,7 +250,7 @@ def bench_backward(args, w, dev, sets, outs, fwd_step, lengths, rows):
         x = sets[j % nsets]
         pa.bwd(x["q"], x["k"], x["v"], x["g"], outs[j % nsets], douts[j % nsets], window_k=w.k,
                period_pi=w.pi, num_skips=w.M, bidirectional=w.bidir, cu_seqlens=x.get("cu_seqlens"),
-               max_seqlen=max(lengths) if lengths else None, workspace=ws)
+               max_seqlen=max(lengths) if lengths else None, lse=lses[j % nsets], workspace=ws)
 
     ms_per_step = timed(step, args, dev)
     sec = ms_per_step / 1e3
@@ -419,7 +424,7 @@ def main():
                max_seqlen=max(lengths) if lengths else None, out=outs[j % nsets], workspace=ws)
 
     if args.backward:
-        return bench_backward(args, w, dev, sets, outs, step, lengths, rows)
+        return bench_backward(args, w, dev, sets, outs, lengths, rows)
 
     ms_per_step = timed(step, args, dev)
     if args.calibrate_copy:

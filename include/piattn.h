@@ -126,33 +126,42 @@ size_t piattn_fwd_workspace_bytes(piattn_dtype dtype, int32_t B, int32_t H,
                                   const piattn_pattern *pattern);
 
 /*
- * piattn_bwd -- backward of piattn_fwd: given the forward's inputs, its
- * output `out` and the gradient `dout` of a loss with respect to out, writes
- * the gradients with respect to q, k, v (dq, dk, dv; element type of q) and
- * the gate logits (dgate, fp32).  Per row i with keys j (one softmax P_ij
- * over L(i) u S(i)): dS_ij = P_ij (<dout_i, v_j> - <dout_i, out_i>),
+ * piattn_bwd -- backward of piattn_fwd (the pages train pi-Attention
+ * models: gist.science section 4 "Experimental Results", item
+ * "Computational Efficiency", training speed; its section 2 "Execution &
+ * Scheduling" overlaps micro-batches in training).  Given the forward's
+ * inputs, its output `out`, optionally its log-sum-exp `lse`, and the
+ * gradient `dout` of a loss with respect to out, writes the gradients with
+ * respect to q, k, v (dq, dk, dv; element type of q) and the gate logits
+ * (dgate, fp32).  Per row i with keys j (one softmax P_ij over L(i) u S(i)):
+ * dS_ij = P_ij (<dout_i, v_j> - <dout_i, out_i>),
  * dq_i = scale sum_j dS_ij k_j, dk_j = scale sum_i dS_ij q_i,
  * dv_j = sum_i P_ij dout_i, dgate_i = (1 - alpha_i) sum_{j in L} dS_ij -
- * alpha_i sum_{j in S} dS_ij (0 on rows without skip keys).  The row's
- * softmax is recomputed in fp32; no forward state besides out is needed.
+ * alpha_i sum_{j in S} dS_ij (0 on rows without skip keys).
+ *
+ * lse: the forward's lse_out (natural log, addressed like the gate logits),
+ * or NULL.  Given lse, PIATTN_BF16 with d in {64, 128} runs on MFMA (P from
+ * the saved lse; a skip pass then a window pass, the skip part of dq, dk, dv
+ * held as bf16 in the gradient rows in between).  Otherwise, or with NULL,
+ * each row's softmax is recomputed in fp32 on the gather path.
  *
  * Shapes, modes and requirements as for piattn_fwd; dq, dk, dv use the
  * strides of q, k, v (strides[0..2]), dout those of out (strides[3]) and
  * dgate those of the gate logits (strides[4]).  No gradient may alias an
  * input or another gradient.  workspace: device scratch of at least
- * piattn_bwd_workspace_bytes(B, H, n) bytes (8 per row), 256-byte aligned.
+ * piattn_bwd_workspace_bytes(B, H, n) bytes (16 per row), 256-byte aligned.
  * Returns PIATTN_OK, PIATTN_EINVAL, PIATTN_EUNSUPPORTED, PIATTN_EWORKSPACE
  * or PIATTN_EHIP.
  */
 int piattn_bwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d,
                const void *q, const void *k, const void *v,
-               const float *gate_logits, const void *out, const void *dout,
-               void *dq, void *dk, void *dv, float *dgate,
+               const float *gate_logits, const void *out, const float *lse,
+               const void *dout, void *dq, void *dk, void *dv, float *dgate,
                const int64_t strides[5][3], const int32_t *cu_seqlens,
                const piattn_pattern *pattern, void *workspace,
                size_t workspace_bytes, void *stream);
 
-/* Workspace bytes piattn_bwd needs: 8 * B * H * n (0 for invalid sizes). */
+/* Workspace bytes piattn_bwd needs: 16 * B * H * n (0 for invalid sizes). */
 size_t piattn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t n);
 
 /*

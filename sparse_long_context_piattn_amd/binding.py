@@ -61,7 +61,7 @@ def lib():
         L.piattn_fwd.restype = ctypes.c_int
         L.piattn_fwd_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, pat]
         L.piattn_fwd_workspace_bytes.restype = sz
-        L.piattn_bwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+        L.piattn_bwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                  ctypes.POINTER(Strides), vp, pat, vp, sz, vp]
         L.piattn_bwd.restype = ctypes.c_int
         L.piattn_bwd_workspace_bytes.argtypes = [i32, i32, i32]
@@ -211,13 +211,17 @@ def fwd(q, k, v, g, *, window_k: int, period_pi: int, num_skips: int, bidirectio
 
 
 def bwd(q, k, v, g, out, dout, *, window_k: int, period_pi: int, num_skips: int, bidirectional=False,
-        scale: float = 0.0, cu_seqlens=None, max_seqlen: int | None = None, workspace=None):
+        scale: float = 0.0, cu_seqlens=None, max_seqlen: int | None = None, lse=None, workspace=None):
     """Backward of fwd: the gradients (dq, dk, dv, dg) of a loss whose gradient
     with respect to fwd's output `out` is `dout`.  dq, dk, dv have the shapes
     and strides of q, k, v (allocated like them); dg is fp32 like g.  dout
-    must have out's strides."""
+    must have out's strides.  lse: the log-sum-exp fwd wrote (fp32, g's shape
+    and strides), or None; bf16 with d 64 / 128 runs on the MFMA kernels when
+    it is given, everything else on the gather kernels (which recompute it)."""
     code = _dtype_code(q)
-    _need_cuda(q, k, v, g, out, dout, cu_seqlens, workspace)
+    _need_cuda(q, k, v, g, out, dout, cu_seqlens, workspace, lse)
+    if lse is not None and (lse.dtype != torch.float32 or lse.shape != g.shape or lse.stride() != g.stride()):
+        raise ValueError("lse must be float32 with g's shape and strides")
     for t in (k, v, out, dout):
         if t.dtype != q.dtype:
             raise TypeError("q, k, v, out, dout must share a dtype")
@@ -241,7 +245,7 @@ def bwd(q, k, v, g, out, dout, *, window_k: int, period_pi: int, num_skips: int,
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = workspace.numel() * workspace.element_size()
-    rc = lib().piattn_bwd(code, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out), _ptr(dout),
+    rc = lib().piattn_bwd(code, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out), _ptr(lse), _ptr(dout),
                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg), ctypes.byref(strides), cu_ptr,
                           ctypes.byref(pat), _ptr(workspace), wbytes, ctypes.c_void_p(_stream(q.device)))
     _check(rc)

@@ -238,11 +238,12 @@ int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
 
 size_t piattn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t n) {
     if (B < 1 || H < 1 || n < 1) return 0;
-    return (size_t)B * H * n * 2 * sizeof(float);
+    return (size_t)B * H * n * 4 * sizeof(float);
 }
 
 int piattn_bwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, const void* q, const void* k,
-               const void* v, const float* gate_logits, const void* out, const void* dout, void* dq, void* dk,
+               const void* v, const float* gate_logits, const void* out, const float* lse, const void* dout,
+               void* dq, void* dk,
                void* dv, float* dgate, const int64_t strides[5][3], const int32_t* cu_seqlens,
                const piattn_pattern* pattern, void* workspace, size_t workspace_bytes, void* stream) {
     BwdArgs ba;
@@ -264,6 +265,9 @@ int piattn_bwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
             if (o == in) return fail(PIATTN_EINVAL, "a gradient aliases an input");
     if (dq == dk || dq == dv || dk == dv) return fail(PIATTN_EINVAL, "gradients alias each other");
     if (static_cast<const void*>(dgate) == gate_logits) return fail(PIATTN_EINVAL, "dgate aliases gate_logits");
+    if (lse && !aligned(lse, 4)) return fail(PIATTN_EINVAL, "lse must be 4-byte aligned");
+    if (lse && static_cast<const void*>(lse) == static_cast<const void*>(dgate))
+        return fail(PIATTN_EINVAL, "dgate aliases lse");
     const size_t need = piattn_bwd_workspace_bytes(B, H, n);
     if (!workspace) return fail(PIATTN_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
     if (workspace_bytes < need)
@@ -275,8 +279,25 @@ int piattn_bwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
     ba.dv = dv;
     ba.dg = dgate;
     ba.rowstat = static_cast<float*>(workspace);
+    ba.lse_in = lse;
     ba.scale = scale_nat(pattern, d);
-    return launch_status(launch_bwd(dtype == PIATTN_BF16 ? 1 : 0, ba, static_cast<hipStream_t>(stream)));
+    const int dt = dtype == PIATTN_BF16 ? 1 : 0;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // Kernel choice: the MFMA band kernels when they take the call (bf16,
+    // d 64 / 128, lse given), else the gather kernels.  PIATTN_BWD_KERNEL =
+    // band | gather forces one (testing and measurement; EUNSUPPORTED if it
+    // cannot take the call).
+    const char* force = getenv("PIATTN_BWD_KERNEL");
+    const bool band_ok = bwd_band_supported(dt, ba);
+    if (force && *force && strcmp(force, "auto") != 0) {
+        if (strcmp(force, "band") == 0) {
+            if (!band_ok) return fail(PIATTN_EUNSUPPORTED, "PIATTN_BWD_KERNEL=band cannot take this call");
+            return launch_status(launch_bwd_band(ba, st));
+        }
+        if (strcmp(force, "gather") == 0) return launch_status(launch_bwd(dt, ba, st));
+        return fail(PIATTN_EINVAL, "PIATTN_BWD_KERNEL=%s is not band, gather or auto", force);
+    }
+    return launch_status(band_ok ? launch_bwd_band(ba, st) : launch_bwd(dt, ba, st));
 }
 
 size_t piattn_decode_workspace_bytes(int32_t S, int32_t H, int32_t d, int32_t num_splits,

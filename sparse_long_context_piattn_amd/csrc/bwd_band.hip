@@ -1,0 +1,505 @@
+// bwd_band.hip -- backward of the prefill on bf16 MFMA for head dim 64 or
+// 128 (gfx950): a row-record kernel, then two passes of one banded kernel,
+// the skip keys in residue layout and then the window in sequence layout.
+//
+// With the forward's log-sum-exp lse_i (natural log, from piattn_fwd's
+// lse_out) the softmax of row i is P_ij = exp2(s_ij + c_i), where
+// s_ij = scale log2(e) <q_i, k_j> and c_i = prior - lse_i log2(e).  The
+// prior is log2(alpha_i) on window keys and log2(1 - alpha_i) on skip keys,
+// and 0 on rows without skip keys (pi-Attention "Dynamic Adaptive Fusion").
+// With D_i = <dout_i, out_i>:
+//   dS_ij = P_ij (<dout_i, v_j> - D_i),
+//   dq_i = scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i,
+//   dv_j = sum_i P_ij dout_i.
+// Every one of these sums splits exactly into a window part and a skip
+// part that share only lse_i and D_i, so the two parts run separately.
+//
+// bwd_record_kernel: each row's record {D_i, c_i (window), c_i (skip)}.
+//
+// bwd_band_kernel: a view is the rows of one sequence at positions
+// base + p step, p = 0 .. L-1: the whole sequence (step 1) for the window,
+// one residue class (base a < pi, step pi) for the skips, whose keys
+// i -/+ m pi, m in [floor(k/pi)+1, M], are then the view rows p -/+ m.
+// Both parts are a band: query p sees key p' when p - p' lies in
+// [dlo, dhi] (and, for bidirectional skips, |p - p'| >= floor(k/pi)+1).
+// A workgroup owns the 64 rows of view tile t, as queries and as keys:
+//   phase A  the key tiles of t's band stream through two LDS slots; each
+//            wave takes 16 query rows: S^T = K Q^T and dP^T = V dO^T on
+//            v_mfma_f32_16x16x32_bf16, P and dS in fp32, dq^T += K^T dS^T;
+//   phase B  the query tiles whose band holds t stream through the same
+//            slots (Q, dO and the rows' records); each wave takes 16 key
+//            rows: S = Q K^T, dP = dO V^T, dv^T += dO^T P, dk^T += Q^T dS.
+// A block pair is computed in both phases (the MFMA work is small next to
+// the memory traffic), so no partial sum crosses workgroups.  The skip pass
+// stores its dq, dk, dv as bf16 partials in the gradient rows and each row's
+// skip sum of dS in its record; the window pass adds the partials and forms
+// the gate gradient (1 - alpha) sum_L dS - alpha sum_S dS.
+#include "kernels.hpp"
+#include "mfma_util.hpp"
+
+namespace {
+
+constexpr int BT = 64;   // rows per tile, query side and key side
+
+// Per-row record in the workspace.
+struct alignas(16) RowRec {
+    float D;    // <dout_i, out_i>
+    float cw;   // window keys: prior - lse2
+    float cs;   // skip keys: prior - lse2
+    float ss;   // sum of dS over the skip keys (written by the skip pass)
+};
+
+struct SeqLoc {
+    int64_t tok0;
+    int64_t bq;
+    int32_t n;
+};
+
+__device__ __forceinline__ SeqLoc seq_loc(const FwdArgs& a, int32_t b) {
+    SeqLoc r;
+    r.n = a.n;
+    r.tok0 = 0;
+    if (a.cu) {
+        r.tok0 = a.cu[b];
+        r.n = a.cu[b + 1] - a.cu[b];
+    }
+    r.bq = a.cu ? 0 : (int64_t)b;
+    return r;
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// One record per row: D_i = <dout_i, out_i> over D/8 lanes (16 bytes each),
+// and c_i = prior - lse_i log2(e) for both key kinds.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_record_kernel(BwdArgs ba) {
+    constexpr int LPK = D / 8, NS = 64 / LPK;
+    const FwdArgs& a = ba.f;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int slot = lane / LPK, c = (lane % LPK) * 8;
+    const int32_t h = blockIdx.y, b = blockIdx.z;
+    const SeqLoc sl = seq_loc(a, b);
+    const int32_t i0 = (blockIdx.x * 4 + wave) * NS + slot;
+    const bool valid = i0 < sl.n;
+    const int32_t i = valid ? i0 : sl.n - 1;
+    if (sl.n < 1) return;
+    const int64_t tok = sl.tok0 + i;
+    const int64_t orow = sl.bq * a.so.s + h * a.so.h + tok * a.so.t + c;
+    const uint4 o = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.o) + orow);
+    const uint4 g = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(ba.dout) + orow);
+    float dp = 0.0f;
+    dp = fmaf(bf16_lo(o.x), bf16_lo(g.x), dp);
+    dp = fmaf(bf16_hi(o.x), bf16_hi(g.x), dp);
+    dp = fmaf(bf16_lo(o.y), bf16_lo(g.y), dp);
+    dp = fmaf(bf16_hi(o.y), bf16_hi(g.y), dp);
+    dp = fmaf(bf16_lo(o.z), bf16_lo(g.z), dp);
+    dp = fmaf(bf16_hi(o.z), bf16_hi(g.z), dp);
+    dp = fmaf(bf16_lo(o.w), bf16_lo(g.w), dp);
+    dp = fmaf(bf16_hi(o.w), bf16_hi(g.w), dp);
+#pragma unroll
+    for (int off = 1; off < LPK; off <<= 1) dp += __shfl_xor(dp, off, 64);
+    if (valid && (lane % LPK) == 0) {
+        const int64_t goff = sl.bq * a.sg.s + h * a.sg.h + tok * a.sg.t;
+        float pl, ps;
+        gate_priors(a.g[goff], row_span(i, sl.n, a.pat).has_skip(), &pl, &ps);
+        const float lse2 = ba.lse_in[goff] * PIATTN_LOG2E;
+        RowRec r;
+        r.D = dp;
+        r.cw = pl - lse2;
+        r.cs = ps - lse2;
+        r.ss = 0.0f;
+        reinterpret_cast<RowRec*>(ba.rowstat)[((int64_t)b * a.H + h) * a.n + i] = r;
+    }
+}
+
+template <int D, bool SKIP, bool BIDIR>
+__global__ __launch_bounds__(256, D == 64 ? 4 : 2) void bwd_band_kernel(BwdArgs ba, int32_t step, int32_t nres,
+                                                                         int32_t tiles, int32_t total,
+                                                                         int32_t merge) {
+    constexpr int DC = D / 32, DB = D / 16, CH = D / 8, RPI = 64 / CH;
+    constexpr int LPH = 32 / RPI;                       // 1 KB loads per wave per stage: half a tile
+    __shared__ __attribute__((aligned(16))) uint16_t x0s[BT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t x1s[BT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t y0s[BT * D];
+    __shared__ __attribute__((aligned(16))) uint16_t y1s[BT * D];
+    __shared__ __attribute__((aligned(16))) float c0s[BT];
+    __shared__ __attribute__((aligned(16))) float c1s[BT];
+    __shared__ __attribute__((aligned(16))) float d0s[BT];
+    __shared__ __attribute__((aligned(16))) float d1s[BT];
+
+    const FwdArgs& a = ba.f;
+    const int32_t logical = xcd_logical(blockIdx.x, total);
+    const int32_t t = logical % tiles;
+    int32_t rest = logical / tiles;
+    const int32_t res = rest % nres;
+    rest /= nres;
+    const int32_t h = rest % a.H, b = rest / a.H;
+    const SeqLoc sq = seq_loc(a, b);
+    if (res >= sq.n) return;                            // workgroup-uniform
+    const int32_t L = (sq.n - 1 - res) / step + 1;
+    const int32_t p0 = t * BT;
+    if (p0 >= L) return;
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, x = lane & 15, g = lane >> 4;
+    const int32_t kw = a.pat.k, pi = a.pat.pi, M = a.pat.M, mlo = kw / pi + 1;
+    const int32_t dlo = SKIP ? (BIDIR ? -M : mlo) : (BIDIR ? -kw : 0);
+    const int32_t dhi = SKIP ? M : kw;
+
+    // view row 0 of each tensor, and the view's row strides (elements)
+    const int64_t r0tok = sq.tok0 + res;
+    const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + sq.bq * a.sq.s + h * a.sq.h + r0tok * a.sq.t;
+    const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + sq.bq * a.sk.s + h * a.sk.h + r0tok * a.sk.t;
+    const uint16_t* Vb = static_cast<const uint16_t*>(a.v) + sq.bq * a.sv.s + h * a.sv.h + r0tok * a.sv.t;
+    const uint16_t* Ob = static_cast<const uint16_t*>(ba.dout) + sq.bq * a.so.s + h * a.so.h + r0tok * a.so.t;
+    uint16_t* dQb = static_cast<uint16_t*>(ba.dq) + sq.bq * a.sq.s + h * a.sq.h + r0tok * a.sq.t;
+    uint16_t* dKb = static_cast<uint16_t*>(ba.dk) + sq.bq * a.sk.s + h * a.sk.h + r0tok * a.sk.t;
+    uint16_t* dVb = static_cast<uint16_t*>(ba.dv) + sq.bq * a.sv.s + h * a.sv.h + r0tok * a.sv.t;
+    const int64_t qst = (int64_t)step * a.sq.t, kst = (int64_t)step * a.sk.t;
+    const int64_t vst = (int64_t)step * a.sv.t, ost = (int64_t)step * a.so.t;
+    RowRec* Rb = reinterpret_cast<RowRec*>(ba.rowstat) + ((int64_t)b * a.H + h) * a.n + res;
+
+    // the key tiles of tile t's band (phase A) and the query tiles whose
+    // band holds tile t (phase B)
+    const int32_t alo = imax32(0, p0 - dhi), ahi = imin32(L - 1, p0 + BT - 1 - dlo);
+    const int32_t jlo = alo / BT, NA = ahi >= alo ? ahi / BT - jlo + 1 : 0;
+    const int32_t blo = imax32(0, p0 + dlo), bhi = imin32(L - 1, p0 + BT - 1 + dhi);
+    const int32_t ilo = blo / BT, NB = bhi >= blo ? bhi / BT - ilo + 1 : 0;
+    const int32_t N = NA + NB;
+
+    // ---- staging: rows s0 .. s0+RPI-1 of the view into slot rows r0 ..;
+    // lane row r0 + lane/CH, physical chunk lane%CH = logical chunk
+    // (lane%CH) ^ (row%8); rows past the view load its last row
+    auto stage_rows = [&](const uint16_t* src, int64_t rst, int32_t s0, int r0, uint16_t* dst)
+        __attribute__((always_inline)) {
+        const int rl = r0 + lane / CH;
+        const int lc = ((lane % CH) ^ (rl & 7)) << 3;
+        const bool inside = s0 + RPI - 1 < L;
+        const uint16_t* ub = inside ? src + (int64_t)s0 * rst : src;
+        const int64_t row = inside ? (int64_t)(lane / CH) : (int64_t)imin32(s0 + lane / CH, L - 1);
+        dma16(ub, (uint32_t)(row * rst + lc) * 2u, lds_addr(dst + r0 * D));
+    };
+    // stage s < NA: key tile jlo+s (K to x, V to y); then query tile
+    // ilo+s-NA (Q to x, dO to y, the rows' c and D to cs, ds).  Waves 0-1
+    // load the x tensor, waves 2-3 the y tensor; each wave's two sources
+    // are fixed here, as values.
+    const bool second = wave >= 2;
+    const uint16_t* const srcA = second ? Vb : Kb;
+    const uint16_t* const srcB = second ? Ob : Qb;
+    const int64_t rstA = second ? vst : kst;
+    const int64_t rstB = second ? ost : qst;
+    auto issue = [&](int32_t s, uint16_t* X, uint16_t* Y, float* C, float* Dd) __attribute__((always_inline)) {
+        const bool pa = s < NA;
+        const int32_t tb = (pa ? jlo + s : ilo + s - NA) * BT;
+        const uint16_t* src = srcB;
+        int64_t rst = rstB;
+        if (pa) {
+            src = srcA;
+            rst = rstA;
+        }
+        uint16_t* dst = second ? Y : X;
+#pragma unroll
+        for (int j = 0; j < LPH; ++j) {
+            const int r0 = (wave & 1) * 32 + j * RPI;
+            stage_rows(src, rst, tb + r0, r0, dst);
+        }
+        if (!pa && (wave & 1) == 0) {
+            const int32_t p = imin32(tb + lane, L - 1);
+            const uint32_t field = wave == 0 ? (SKIP ? 8u : 4u) : 0u;
+            dma4(Rb, (uint32_t)(p * step) * 16u + field, lds_addr(wave == 0 ? C : Dd));
+        }
+    };
+
+    if (N > 0) issue(0, x0s, y0s, c0s, d0s);
+
+    // ---- the lane's own row (query in phase A, key in phase B)
+    const int32_t pw = p0 + 16 * wave;                  // the wave's first row
+    const int32_t pme = pw + x;
+    const bool mine = pme < L;
+    const int32_t pc = mine ? pme : L - 1;
+    bf16x8_t qf[DC], of[DC];
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+        qf[c] = *reinterpret_cast<const bf16x8_t*>(Qb + pc * qst + 32 * c + 8 * g);
+        of[c] = *reinterpret_cast<const bf16x8_t*>(Ob + pc * ost + 32 * c + 8 * g);
+    }
+    const RowRec own = Rb[(int64_t)pc * step];
+    const float cq = SKIP ? own.cs : own.cw;
+
+    const float sl2 = a.scale_log2;
+    const int tr_row = 4 * g + (x >> 2);
+    const int tr_col = 4 * (x & 3);
+    const bool wave_live = pw < L;                      // wave-uniform
+
+    // whether view rows (query pq, key pk) form a pair of this part
+    auto pair_ok = [&](int32_t pq, int32_t pk) __attribute__((always_inline)) {
+        const int32_t dd = pq - pk;
+        bool ok = dd >= dlo && dd <= dhi && pq < L && pk < L;
+        if (SKIP && BIDIR) ok = ok && (dd >= mlo || dd <= -mlo);
+        return ok;
+    };
+    auto pack4 = [](float a0, float a1, float a2, float a3) __attribute__((always_inline)) {
+        return __builtin_bit_cast(s16x4_t, make_uint2(cvt_pk_bf16(a0, a1), cvt_pk_bf16(a2, a3)));
+    };
+    auto cat8 = [](s16x4_t lo, s16x4_t hi) __attribute__((always_inline)) {
+        return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    // transposed operand of a 16-row block pair: A[m = column][k = rows]
+    auto tr_pair = [&](const uint16_t* S, int u, int bb) __attribute__((always_inline)) {
+        const s16x4_t lo = ld_tr16(S + swr<D>(16 * u + tr_row, 2 * bb + (tr_col >> 3)) + (tr_col & 7));
+        const s16x4_t hi = ld_tr16(S + swr<D>(16 * u + 16 + tr_row, 2 * bb + (tr_col >> 3)) + (tr_col & 7));
+        return cat8(lo, hi);
+    };
+
+    // ---- phase A: dq of the wave's 16 query rows
+    f32x4_t dqa[DB];
+#pragma unroll
+    for (int bb = 0; bb < DB; ++bb) dqa[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float ssum = 0.0f;                                  // sum of dS over this lane's keys of row pme
+    const int32_t kmin = pw - dhi, kmax = imin32(pw + 15, L - 1) - dlo;   // the wave's key range
+    auto computeA = [&](int32_t kb0, const uint16_t* Ks, const uint16_t* Vs) __attribute__((always_inline)) {
+        if (!wave_live) return;
+#pragma unroll
+        for (int u = 0; u < 4; u += 2) {
+            s16x4_t db[2];
+            bool act[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int32_t k0 = kb0 + 16 * (u + e);
+                act[e] = k0 <= imin32(kmax, L - 1) && k0 + 15 >= kmin;
+                db[e] = s16x4_t{0, 0, 0, 0};
+                if (act[e]) {
+                    f32x4_t s4 = {0.f, 0.f, 0.f, 0.f}, p4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < DC; ++c) {
+                        const bf16x8_t kk =
+                            *reinterpret_cast<const bf16x8_t*>(Ks + swr<D>(16 * (u + e) + x, 4 * c + g));
+                        s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qf[c], s4, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int c = 0; c < DC; ++c) {
+                        const bf16x8_t vv =
+                            *reinterpret_cast<const bf16x8_t*>(Vs + swr<D>(16 * (u + e) + x, 4 * c + g));
+                        p4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vv, of[c], p4, 0, 0, 0);
+                    }
+                    float dsv[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const bool ok = pair_ok(pme, k0 + 4 * g + r);
+                        const float p = exp2_fast(fmaf(s4[r], sl2, cq));
+                        dsv[r] = ok ? p * (p4[r] - own.D) : 0.0f;
+                        ssum += dsv[r];
+                    }
+                    db[e] = pack4(dsv[0], dsv[1], dsv[2], dsv[3]);
+                }
+            }
+            if (!act[0] && !act[1]) continue;
+            const bf16x8_t dd = cat8(db[0], db[1]);
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb)
+                dqa[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_pair(Ks, u, bb), dd, dqa[bb], 0, 0, 0);
+        }
+    };
+    // dq rows out (the skip pass stores partials, the window pass adds them)
+    // and the row sums of dS: the skip pass records its sum, the window
+    // pass forms the gate gradient
+    auto finishA = [&]() __attribute__((always_inline)) {
+        const float srow = sum4(ssum);
+        if (!mine) return;
+        uint16_t* dst = dQb + pme * qst;
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) {
+            float v0 = dqa[bb][0] * ba.scale, v1 = dqa[bb][1] * ba.scale;
+            float v2 = dqa[bb][2] * ba.scale, v3 = dqa[bb][3] * ba.scale;
+            uint2* pd = reinterpret_cast<uint2*>(dst + 16 * bb + 4 * g);
+            if (!SKIP && merge) {
+                const uint2 pr = *pd;
+                v0 += bf16_lo(pr.x);
+                v1 += bf16_hi(pr.x);
+                v2 += bf16_lo(pr.y);
+                v3 += bf16_hi(pr.y);
+            }
+            *pd = make_uint2(cvt_pk_bf16(v0, v1), cvt_pk_bf16(v2, v3));
+        }
+        if (g == 0) {
+            if (SKIP) {
+                Rb[(int64_t)pme * step].ss = srow;
+            } else {
+                const int64_t goff = sq.bq * a.sg.s + h * a.sg.h + (sq.tok0 + pme) * a.sg.t;
+                const bool hs = merge && row_span(pme, sq.n, a.pat).has_skip();
+                const float alpha = 1.0f / (1.0f + __expf(-a.g[goff]));
+                ba.dg[goff] = hs ? (1.0f - alpha) * srow - alpha * own.ss : 0.0f;
+            }
+        }
+    };
+
+    // ---- phase B: dk, dv of the wave's 16 key rows
+    f32x4_t dka[DB], dva[DB];
+    bf16x8_t kf[DC], vf[DC];
+    const int32_t qmin = pw + dlo, qmax = imin32(pw + 15, L - 1) + dhi;   // the wave's query range
+    auto computeB = [&](int32_t qb0, const uint16_t* Qs, const uint16_t* Os, const float* C, const float* Dd)
+        __attribute__((always_inline)) {
+        if (!wave_live) return;
+#pragma unroll
+        for (int v = 0; v < 4; v += 2) {
+            s16x4_t pb[2], db[2];
+            bool act[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int32_t q0 = qb0 + 16 * (v + e);
+                act[e] = q0 <= imin32(qmax, L - 1) && q0 + 15 >= qmin;
+                pb[e] = db[e] = s16x4_t{0, 0, 0, 0};
+                if (act[e]) {
+                    f32x4_t s4 = {0.f, 0.f, 0.f, 0.f}, p4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int c = 0; c < DC; ++c) {
+                        const bf16x8_t qq =
+                            *reinterpret_cast<const bf16x8_t*>(Qs + swr<D>(16 * (v + e) + x, 4 * c + g));
+                        s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qq, kf[c], s4, 0, 0, 0);
+                    }
+#pragma unroll
+                    for (int c = 0; c < DC; ++c) {
+                        const bf16x8_t oo =
+                            *reinterpret_cast<const bf16x8_t*>(Os + swr<D>(16 * (v + e) + x, 4 * c + g));
+                        p4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(oo, vf[c], p4, 0, 0, 0);
+                    }
+                    const f32x4_t c4 = *reinterpret_cast<const f32x4_t*>(C + 16 * (v + e) + 4 * g);
+                    const f32x4_t d4 = *reinterpret_cast<const f32x4_t*>(Dd + 16 * (v + e) + 4 * g);
+                    float pv[4], dsv[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const bool ok = pair_ok(q0 + 4 * g + r, pme);
+                        const float p = exp2_fast(fmaf(s4[r], sl2, c4[r]));
+                        pv[r] = ok ? p : 0.0f;
+                        dsv[r] = ok ? p * (p4[r] - d4[r]) : 0.0f;
+                    }
+                    pb[e] = pack4(pv[0], pv[1], pv[2], pv[3]);
+                    db[e] = pack4(dsv[0], dsv[1], dsv[2], dsv[3]);
+                }
+            }
+            if (!act[0] && !act[1]) continue;
+            const bf16x8_t pp = cat8(pb[0], pb[1]);
+            const bf16x8_t dd = cat8(db[0], db[1]);
+#pragma unroll
+            for (int bb = 0; bb < DB; ++bb) {
+                dva[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_pair(Os, v, bb), pp, dva[bb], 0, 0, 0);
+                dka[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_pair(Qs, v, bb), dd, dka[bb], 0, 0, 0);
+            }
+        }
+    };
+    auto finishB = [&]() __attribute__((always_inline)) {
+        if (!mine) return;
+        uint16_t* kd = dKb + pme * kst;
+        uint16_t* vd = dVb + pme * vst;
+#pragma unroll
+        for (int bb = 0; bb < DB; ++bb) {
+            float k0 = dka[bb][0] * ba.scale, k1 = dka[bb][1] * ba.scale;
+            float k2 = dka[bb][2] * ba.scale, k3 = dka[bb][3] * ba.scale;
+            float v0 = dva[bb][0], v1 = dva[bb][1], v2 = dva[bb][2], v3 = dva[bb][3];
+            uint2* pk = reinterpret_cast<uint2*>(kd + 16 * bb + 4 * g);
+            uint2* pv = reinterpret_cast<uint2*>(vd + 16 * bb + 4 * g);
+            if (!SKIP && merge) {
+                const uint2 ok = *pk, ov = *pv;
+                k0 += bf16_lo(ok.x);
+                k1 += bf16_hi(ok.x);
+                k2 += bf16_lo(ok.y);
+                k3 += bf16_hi(ok.y);
+                v0 += bf16_lo(ov.x);
+                v1 += bf16_hi(ov.x);
+                v2 += bf16_lo(ov.y);
+                v3 += bf16_hi(ov.y);
+            }
+            *pk = make_uint2(cvt_pk_bf16(k0, k1), cvt_pk_bf16(k2, k3));
+            *pv = make_uint2(cvt_pk_bf16(v0, v1), cvt_pk_bf16(v2, v3));
+        }
+    };
+
+    // step s: this wave's loads of stage s landed (wait), every wave's
+    // landed and stage s-1 fully read (barrier); issue stage s+1 into the
+    // other slot, compute stage s.  Phase A and phase B run as separate
+    // loops so that q, dout and dq of phase A are dead in phase B.
+    auto waitissue = [&](int32_t s, uint16_t* Xn, uint16_t* Yn, float* Cn, float* Dn) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+        lds_barrier();
+        if (s + 1 < N) issue(s + 1, Xn, Yn, Cn, Dn);
+    };
+    for (int32_t s = 0; s < NA; ++s) {
+        if (s & 1) {
+            waitissue(s, x0s, y0s, c0s, d0s);
+            computeA((jlo + s) * BT, x1s, y1s);
+        } else {
+            waitissue(s, x1s, y1s, c1s, d1s);
+            computeA((jlo + s) * BT, x0s, y0s);
+        }
+    }
+    finishA();
+
+#pragma unroll
+    for (int c = 0; c < DC; ++c) {
+        kf[c] = *reinterpret_cast<const bf16x8_t*>(Kb + pc * kst + 32 * c + 8 * g);
+        vf[c] = *reinterpret_cast<const bf16x8_t*>(Vb + pc * vst + 32 * c + 8 * g);
+    }
+#pragma unroll
+    for (int bb = 0; bb < DB; ++bb) dka[bb] = dva[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int32_t s = NA; s < N; ++s) {
+        if (s & 1) {
+            waitissue(s, x0s, y0s, c0s, d0s);
+            computeB((ilo + s - NA) * BT, x1s, y1s, c1s, d1s);
+        } else {
+            waitissue(s, x1s, y1s, c1s, d1s);
+            computeB((ilo + s - NA) * BT, x0s, y0s, c0s, d0s);
+        }
+    }
+    finishB();
+}
+
+template <int D, bool BIDIR>
+hipError_t launch_t(const BwdArgs& ba, hipStream_t stream) {
+    const FwdArgs& a = ba.f;
+    constexpr int NS = 64 / (D / 8);
+    const dim3 rgrid((a.n + 4 * NS - 1) / (4 * NS), a.H, a.B);
+    hipLaunchKernelGGL((bwd_record_kernel<D>), rgrid, dim3(256), 0, stream, ba);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int32_t mlo = a.pat.k / a.pat.pi + 1;
+    const bool skips = a.pat.M >= mlo;
+    if (skips) {
+        const int32_t nres = imin32(a.pat.pi, a.n);
+        const int32_t lmax = (a.n - 1) / a.pat.pi + 1;
+        const int32_t tiles = (lmax + BT - 1) / BT;
+        const int64_t total = (int64_t)tiles * nres * a.H * a.B;
+        if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL((bwd_band_kernel<D, true, BIDIR>), dim3((uint32_t)total), dim3(256), 0, stream, ba,
+                           a.pat.pi, nres, tiles, (int32_t)total, 0);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const int32_t tiles = (a.n + BT - 1) / BT;
+    const int64_t total = (int64_t)tiles * a.H * a.B;
+    if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((bwd_band_kernel<D, false, BIDIR>), dim3((uint32_t)total), dim3(256), 0, stream, ba, 1, 1,
+                       tiles, (int32_t)total, skips ? 1 : 0);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+bool bwd_band_supported(int dtype, const BwdArgs& ba) {
+    const FwdArgs& a = ba.f;
+    if (dtype != 1 || (a.d != 64 && a.d != 128) || !ba.lse_in) return false;
+    // 32-bit byte offsets from a view's first row: any row of the sequence
+    // (elements of the token-strided tensors, records of 16 bytes)
+    int64_t ts = a.sq.t;
+    const int64_t s4[3] = {a.sk.t, a.sv.t, a.so.t};
+    for (int64_t s : s4) ts = s > ts ? s : ts;
+    const int64_t rows = (int64_t)a.n + BT;
+    return rows * ts * 2 + a.d * 2 < ((int64_t)1 << 31) && rows * 16 < ((int64_t)1 << 31) &&
+           (int64_t)a.n + 2LL * a.pat.k + 2LL * a.pat.M + 2 * BT < ((int64_t)1 << 30);
+}
+
+hipError_t launch_bwd_band(const BwdArgs& ba, hipStream_t stream) {
+    if (ba.f.d == 64) return ba.f.pat.bidir ? launch_t<64, true>(ba, stream) : launch_t<64, false>(ba, stream);
+    return ba.f.pat.bidir ? launch_t<128, true>(ba, stream) : launch_t<128, false>(ba, stream);
+}

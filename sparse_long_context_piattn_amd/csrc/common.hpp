@@ -39,7 +39,8 @@ struct BwdArgs {
     void* dk;
     void* dv;
     float* dg;
-    float* rowstat;      // workspace: per row (log2-sum-exp, D), [B][H][n][2]
+    float* rowstat;      // workspace: 16 bytes per row, [B][H][n]
+    const float* lse_in; // the forward's log-sum-exp (natural log, layout of g), or null
     float scale;         // logit scale (natural units)
 };
 

@@ -50,44 +50,16 @@ struct Geo {
     static constexpr int RPI = 64 / CH;  // rows covered by one 64-lane 16-byte load
 };
 
-// Element offset of 16-byte chunk c of row r of a row-major [rows][D] tile
-// whose chunks are XOR-swizzled by r % 8.
-template <int D>
-__device__ __forceinline__ int swr(int r, int c) { return r * D + ((c ^ (r & 7)) << 3); }
-
 // Same, swizzled by (r / 2) % 8: the 16 rows of a K-operand read then fall
 // on distinct banks when a row is 128 bytes.
 template <int D>
 __device__ __forceinline__ int swu(int r, int c) { return r * D + ((c ^ ((r >> 1) & 7)) << 3); }
-
-// 4-byte LDS-direct load of each active lane (lane l writes lds + 4 l).
-__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("global_load_lds_dword %0, %1" : : "v"(voff), "s"(uniform_ptr(sbase)),
-                 "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
-}
 
 // Whether row (residue a, period t) with pr periods in its residue has any
 // skip key.
 template <bool BIDIR>
 __device__ __forceinline__ bool row_has_skip(int32_t t, int32_t pr, int32_t mlo, int32_t M) {
     return M >= mlo && (t >= mlo || (BIDIR && t + mlo < pr));
-}
-
-// Tile order.  Workgroup hw runs on XCD hw % 8 as that XCD's (hw / 8)-th.
-// Logical tiles are dealt to the XCDs in runs of XG consecutive tiles, run
-// r to XCD r % 8: neighbouring tiles (which share halo rows) share an L2,
-// and the runs of long and short sequences spread over all XCDs.  With
-// runs of 32 the window pass's halo rows come from L2 (its HBM reads fall
-// to q, k, v, the partial and the records once each); with runs of 16 about
-// 70% of them were fetched again.
-constexpr int32_t XG = 32;
-__device__ __forceinline__ int32_t xcd_logical(int32_t hw, int32_t total) {
-    const int32_t xcd = hw % 8, loc = hw / 8;
-    const int32_t logical = ((loc / XG) * 8 + xcd) * XG + loc % XG;
-    // the last, partial round of runs: fall back to the plain order so that
-    // every logical tile below total is produced exactly once
-    const int32_t full = total / (8 * XG) * (8 * XG);
-    return hw < full ? logical : hw;
 }
 
 // Skip partial of one row, handed from the skip pass to the window pass.

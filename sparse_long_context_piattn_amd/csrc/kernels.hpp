@@ -18,8 +18,13 @@ bool fwd_split_supported(int dtype, const FwdArgs& a);
 hipError_t launch_fwd_split(const FwdArgs& a, float* ws, hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_cache_append(int dtype, const AppendArgs& a, hipStream_t stream);
-// Backward of the prefill (gather path, any supported dtype and d).
+// Backward of the prefill (gather path, any supported dtype and d; the
+// rows' log-sum-exp recomputed).
 hipError_t launch_bwd(int dtype, const BwdArgs& a, hipStream_t stream);
+// Backward on MFMA (bf16, d 64/128, the forward's log-sum-exp given): skip
+// pass in residue layout, then the window pass.
+bool bwd_band_supported(int dtype, const BwdArgs& a);
+hipError_t launch_bwd_band(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_neighbors(int32_t n, const PiPattern& p, int32_t q_begin, int32_t q_count,
                             int32_t cap, int32_t* idx, int8_t* kind, int32_t* count,
                             hipStream_t stream);

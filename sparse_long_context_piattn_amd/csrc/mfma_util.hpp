@@ -96,6 +96,13 @@ constexpr int vm_wait_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4)
 // caller waits with vm_wait_imm before reading the data, and no compiler-
 // visible load may be consumed while they are in flight unless an explicit
 // wait covers them.  sbase must be wave-uniform.
+//
+// The compiler's hazard recognizer does not look inside the asm, so the
+// block supplies the wait states the ISA requires before the load: a VMEM
+// instruction that reads an SGPR written by a VALU instruction
+// (v_readfirstlane, or v_readlane restoring a spilled SGPR) needs 5, and an
+// LDS-DMA load after an SALU write of M0 needs 1.  s_nop 4 gives 5; without
+// it the load can use the SGPR's previous value as its base address.
 __device__ __forceinline__ const void* uniform_ptr(const void* p) {
     const uint64_t v = reinterpret_cast<uint64_t>(p);
     const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
@@ -103,6 +110,35 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
     return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
 }
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("global_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(uniform_ptr(sbase)),
+    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(uniform_ptr(sbase)),
                  "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+// 4-byte LDS-direct load of each active lane (lane l writes lds + 4 l);
+// wait states as for dma16.
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+    asm volatile("s_nop 4\n\tglobal_load_lds_dword %0, %1" : : "v"(voff), "s"(uniform_ptr(sbase)),
+                 "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+// Element offset of 16-byte chunk c of row r of a row-major [rows][D] tile
+// whose chunks are XOR-swizzled by r % 8.
+template <int D>
+__device__ __forceinline__ int swr(int r, int c) { return r * D + ((c ^ (r & 7)) << 3); }
+
+// Tile order.  Workgroup hw runs on XCD hw % 8 as that XCD's (hw / 8)-th.
+// Logical tiles are dealt to the XCDs in runs of XG consecutive tiles, run
+// r to XCD r % 8: neighbouring tiles (which share halo rows) share an L2,
+// and the runs of long and short sequences spread over all XCDs.  With
+// runs of 32 the window pass's halo rows come from L2 (its HBM reads fall
+// to q, k, v, the partial and the records once each); with runs of 16 about
+// 70% of them were fetched again.
+constexpr int32_t XG = 32;
+__device__ __forceinline__ int32_t xcd_logical(int32_t hw, int32_t total) {
+    const int32_t xcd = hw % 8, loc = hw / 8;
+    const int32_t logical = ((loc / XG) * 8 + xcd) * XG + loc % XG;
+    // the last, partial round of runs: fall back to the plain order so that
+    // every logical tile below total is produced exactly once
+    const int32_t full = total / (8 * XG) * (8 * XG);
+    return hw < full ? logical : hw;
 }

@@ -211,3 +211,44 @@ def test_cache_append_rejects_bad_arguments(kw, expect):
     rc = L.piattn_cache_append(args["dtype"], args["S"], args["H"], args["d"], args["kn"], args["vn"],
                                args["kc"], args["vc"], args["pos"], args["slots"], ctypes.byref(st), None)
     assert rc == expect and L.piattn_last_error().decode()
+
+
+DOUT = ctypes.c_void_p(5 << 20)
+DQ, DK, DV = ctypes.c_void_p(6 << 20), ctypes.c_void_p(7 << 20), ctypes.c_void_p(8 << 20)
+DG = ctypes.c_void_p(9 << 20)
+LSE = ctypes.c_void_p(10 << 20)
+WS = ctypes.c_void_p(11 << 20)
+
+
+def _bwd(dtype=1, B=1, H=1, n=64, d=64, lse=LSE, dout=DOUT, dq=DQ, dk=DK, dv=DV, dg=DG, ws=WS,
+         wsb=1 << 20, pat=None):
+    L = pa.lib()
+    p = pat if pat is not None else pa.make_pattern(4, 16, 2)
+    rc = L.piattn_bwd(dtype, B, H, n, d, A, A2, A3, A, OUT, lse, dout, dq, dk, dv, dg,
+                      ctypes.byref(_strides()), None, ctypes.byref(p), ws, wsb, None)
+    return rc, L.piattn_last_error().decode()
+
+
+def test_bwd_workspace_query():
+    L = pa.lib()
+    assert L.piattn_bwd_workspace_bytes(2, 3, 100) == 16 * 2 * 3 * 100
+    assert L.piattn_bwd_workspace_bytes(0, 3, 100) == 0
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dq=A), EINVAL),                                  # gradient aliases an input
+    (dict(dk=DQ), EINVAL),                                 # gradients alias each other
+    (dict(dg=ctypes.c_void_p((9 << 20) + 2)), EINVAL),     # dgate misaligned
+    (dict(lse=ctypes.c_void_p((10 << 20) + 2)), EINVAL),   # lse misaligned
+    (dict(lse=DG), EINVAL),                                # dgate aliases lse
+    (dict(dout=ctypes.c_void_p((5 << 20) + 2)), EINVAL),   # dout misaligned
+    (dict(ws=None), EWORKSPACE),
+    (dict(wsb=16 * 64 - 1), EWORKSPACE),
+    (dict(ws=ctypes.c_void_p((11 << 20) + 16)), EINVAL),  # workspace not 256-byte aligned
+    (dict(d=96), EUNSUPPORTED),
+    (dict(pat=pa.make_pattern(4, 0, 2)), EINVAL),
+])
+def test_bwd_rejects_bad_arguments(kw, expect):
+    rc, msg = _bwd(**kw)
+    assert rc == expect, msg
+    assert msg
