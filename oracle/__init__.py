@@ -63,6 +63,20 @@ def _load():
         lib.oracle_bwd.argtypes = [i32, vp, i32, i32, vp, vp, vp, i32, vp, vp, i32, i32, i32, i32,
                                    i32, dbl, vp, vp, vp, vp]
         lib.oracle_bwd.restype = None
+        lib.oracle_neighbors_levels.argtypes = [i32, i32, i32, vp, vp, i32, i32, vp, vp]
+        lib.oracle_neighbors_levels.restype = i32
+        lib.oracle_neighbor_table_levels.argtypes = [i32, i32, i32, vp, vp, i32, i32, i32, i32, vp, vp,
+                                                     vp]
+        lib.oracle_neighbor_table_levels.restype = i32
+        lib.oracle_fwd_levels.argtypes = [i32, vp, i32, i32, vp, vp, vp, i32, vp, i32, i32, vp, vp,
+                                          i32, dbl, i64, vp, vp, vp, i32]
+        lib.oracle_fwd_levels.restype = None
+        lib.oracle_decode_levels.argtypes = [i32, i32, i32, vp, vp, vp, i32, vp, vp, vp, i32, i32, vp,
+                                             vp, dbl, vp, vp, i32]
+        lib.oracle_decode_levels.restype = None
+        lib.oracle_bwd_levels.argtypes = [i32, vp, i32, i32, vp, vp, vp, i32, vp, vp, i32, i32, i32,
+                                          vp, vp, i32, dbl, vp, vp, vp, vp]
+        lib.oracle_bwd_levels.restype = None
         lib.oracle_max_threads.argtypes = []
         lib.oracle_max_threads.restype = i32
         _lib = lib
@@ -89,34 +103,49 @@ def _as_input(x):
     raise TypeError("oracle inputs must be float64, float32 or uint16 (bf16 bits), got %s" % x.dtype)
 
 
-def neighbors(n: int, k: int, pi: int, M: int, bidir: bool, i: int):
-    """Ascending neighbour keys of query i and their kinds (1 local, 2 skip)."""
-    cap = 2 * k + 1 + 2 * M
+def _levels(pi: int, M: int, levels):
+    """Level arrays (periods, counts): the base level (pi, M), then the extra
+    levels of a skip schedule, each an (pi_r, M_r) pair."""
+    lv = [(int(pi), int(M))] + [(int(a), int(b)) for a, b in (levels or ())]
+    lpi = np.array([a for a, _ in lv], np.int32)
+    lM = np.array([b for _, b in lv], np.int32)
+    return len(lv), lpi, lM
+
+
+def neighbors(n: int, k: int, pi: int, M: int, bidir: bool, i: int, levels=None):
+    """Ascending neighbour keys of query i and their kinds (1 local, 2 skip).
+    levels: extra (pi_r, M_r) levels of a skip schedule (union of skip sets)."""
+    nlev, lpi, lM = _levels(pi, M, levels)
+    cap = 2 * k + 1 + 2 * int(lM.sum())
     idx = np.zeros(max(cap, 1), np.int32)
     kind = np.zeros(max(cap, 1), np.int8)
-    c = _load().oracle_neighbors(n, k, pi, M, int(bool(bidir)), i, _ptr(idx), _ptr(kind))
+    c = _load().oracle_neighbors_levels(n, k, nlev, _ptr(lpi), _ptr(lM), int(bool(bidir)), i,
+                                        _ptr(idx), _ptr(kind))
     return idx[:c].copy(), kind[:c].copy()
 
 
 def neighbor_table(n: int, k: int, pi: int, M: int, bidir: bool, q_begin: int = 0,
-                   q_count: int | None = None, cap: int | None = None):
+                   q_count: int | None = None, cap: int | None = None, levels=None):
     """[q_count, cap] int32 keys (-1 padded), int8 kinds (0 padded), int32 counts."""
+    nlev, lpi, lM = _levels(pi, M, levels)
     if q_count is None:
         q_count = n - q_begin
     if cap is None:
-        cap = (2 * k + 1 + 2 * M) if bidir else (k + 1 + M)
+        msum = int(lM.sum())
+        cap = (2 * k + 1 + 2 * msum) if bidir else (k + 1 + msum)
     idx = np.empty((q_count, cap), np.int32)
     kind = np.empty((q_count, cap), np.int8)
     cnt = np.empty(q_count, np.int32)
-    rc = _load().oracle_neighbor_table(n, k, pi, M, int(bool(bidir)), q_begin, q_count, cap,
-                                       _ptr(idx), _ptr(kind), _ptr(cnt))
+    rc = _load().oracle_neighbor_table_levels(n, k, nlev, _ptr(lpi), _ptr(lM), int(bool(bidir)),
+                                              q_begin, q_count, cap, _ptr(idx), _ptr(kind),
+                                              _ptr(cnt))
     if rc != 0:
         raise ValueError("a neighbour list does not fit in cap=%d" % cap)
     return idx, kind, cnt
 
 
 def fwd(q, k, v, g, cu_seqlens, kw: int, pi: int, M: int, bidir: bool, scale: float,
-        rows=None, nthreads: int = 0, want_lse: bool = False):
+        rows=None, nthreads: int = 0, want_lse: bool = False, levels=None):
     """Prefill over a packed batch.
 
     q, k, v: [T, H, d] (float64 / float32 / bf16-bits uint16); g: [T, H] gate
@@ -138,14 +167,15 @@ def fwd(q, k, v, g, cu_seqlens, kw: int, pi: int, M: int, bidir: bool, scale: fl
         nrows, rp = rows_arr.size, _ptr(rows_arr)
     out = np.zeros((nrows, d), np.float64)
     lse = np.zeros(nrows, np.float64)
-    _load().oracle_fwd(len(cu) - 1, _ptr(cu), H, d, _ptr(q), _ptr(k), _ptr(v), dt, _ptr(g),
-                       kw, pi, M, int(bool(bidir)), float(scale), nrows, rp, _ptr(out),
-                       _ptr(lse), int(nthreads))
+    nlev, lpi, lM = _levels(pi, M, levels)
+    _load().oracle_fwd_levels(len(cu) - 1, _ptr(cu), H, d, _ptr(q), _ptr(k), _ptr(v), dt, _ptr(g),
+                              kw, nlev, _ptr(lpi), _ptr(lM), int(bool(bidir)), float(scale), nrows,
+                              rp, _ptr(out), _ptr(lse), int(nthreads))
     return (out, lse) if want_lse else out
 
 
 def decode(q, k_cache, v_cache, lens, g, kw: int, pi: int, M: int, scale: float,
-           nthreads: int = 0, want_lse: bool = False):
+           nthreads: int = 0, want_lse: bool = False, levels=None):
     """One query per (sequence, head) at position lens[s]-1.
 
     q: [S, H, d]; k_cache, v_cache: [S, H, L, d]; lens: [S]; g: [S, H].
@@ -162,12 +192,15 @@ def decode(q, k_cache, v_cache, lens, g, kw: int, pi: int, M: int, scale: float,
     g = np.ascontiguousarray(g, dtype=np.float64).reshape(S, H)
     out = np.zeros((S, H, d), np.float64)
     lse = np.zeros((S, H), np.float64)
-    _load().oracle_decode(S, H, d, _ptr(q), _ptr(kc), _ptr(vc), dt, _ptr(cs), _ptr(lens),
-                          _ptr(g), kw, pi, M, float(scale), _ptr(out), _ptr(lse), int(nthreads))
+    nlev, lpi, lM = _levels(pi, M, levels)
+    _load().oracle_decode_levels(S, H, d, _ptr(q), _ptr(kc), _ptr(vc), dt, _ptr(cs), _ptr(lens),
+                                 _ptr(g), kw, nlev, _ptr(lpi), _ptr(lM), float(scale), _ptr(out),
+                                 _ptr(lse), int(nthreads))
     return (out, lse) if want_lse else out
 
 
-def bwd(q, k, v, g, dout, cu_seqlens, kw: int, pi: int, M: int, bidir: bool, scale: float):
+def bwd(q, k, v, g, dout, cu_seqlens, kw: int, pi: int, M: int, bidir: bool, scale: float,
+        levels=None):
     """Gradients of sum(dout * out) for the prefill over a packed batch.
 
     q, k, v, dout: [T, H, d] (float64 / float32 / bf16-bits uint16); g: [T, H];
@@ -186,7 +219,8 @@ def bwd(q, k, v, g, dout, cu_seqlens, kw: int, pi: int, M: int, bidir: bool, sca
     dk = np.zeros((T, H, d), np.float64)
     dv = np.zeros((T, H, d), np.float64)
     dg = np.zeros((T, H), np.float64)
-    _load().oracle_bwd(len(cu) - 1, _ptr(cu), H, d, _ptr(q), _ptr(k), _ptr(v), dt, _ptr(g),
-                       _ptr(dout), dtd, kw, pi, M, int(bool(bidir)), float(scale), _ptr(dq),
-                       _ptr(dk), _ptr(dv), _ptr(dg))
+    nlev, lpi, lM = _levels(pi, M, levels)
+    _load().oracle_bwd_levels(len(cu) - 1, _ptr(cu), H, d, _ptr(q), _ptr(k), _ptr(v), dt, _ptr(g),
+                              _ptr(dout), dtd, kw, nlev, _ptr(lpi), _ptr(lM), int(bool(bidir)),
+                              float(scale), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dg))
     return dq, dk, dv, dg

@@ -18,8 +18,10 @@ from __future__ import annotations
 import numpy as np
 
 
-def masks(n: int, k: int, pi: int, M: int, bidir: bool):
-    """(local, skip) boolean [n, n] masks; row = query i, column = key j."""
+def masks(n: int, k: int, pi: int, M: int, bidir: bool, levels=None):
+    """(local, skip) boolean [n, n] masks; row = query i, column = key j.
+    levels: extra (pi_r, M_r) levels of a skip schedule; the skip mask is the
+    elementwise OR of each level's mask."""
     pos = np.arange(n)
     off = pos[:, None] - pos[None, :]          # i - j
     if bidir:
@@ -29,19 +31,21 @@ def masks(n: int, k: int, pi: int, M: int, bidir: bool):
         local = (off >= 0) & (off <= k)
         cand = off > 0
     dist = np.abs(off)
-    skip = cand & (dist % pi == 0) & (dist <= M * pi) & ~local
+    skip = np.zeros((n, n), bool)
+    for p_r, m_r in [(pi, M)] + list(levels or ()):
+        skip |= cand & (dist % p_r == 0) & (dist <= m_r * p_r) & ~local
     return local, skip
 
 
 def attention(q, k, v, g, kw: int, pi: int, M: int, bidir: bool, scale: float,
-              want_lse: bool = False):
+              want_lse: bool = False, levels=None):
     """One (sequence, head): q, k, v [n, d] float64, g [n] gate logits."""
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     g = np.asarray(g, np.float64)
     n = q.shape[0]
-    local, skip = masks(n, kw, pi, M, bidir)
+    local, skip = masks(n, kw, pi, M, bidir, levels)
     with np.errstate(divide="ignore"):
         alpha = 1.0 / (1.0 + np.exp(-g))
         log_a = np.log(alpha)

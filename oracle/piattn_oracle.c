@@ -21,6 +21,12 @@
  *     (when S(i) is empty the prior is a constant shift and is left out)
  *     o_i = sum_j softmax(logit)_j v_j      one softmax over L(i) u S(i)
  *
+ * Skip schedules (the hierarchical skip schedules the Dutch summary names as
+ * future work, section 5 "Betekenis en Conclusie"): a list of levels
+ * (pi_r, M_r); S(i) is the union over the levels of the single-period skip
+ * sets, each key once, all with the skip prior.  One level is the pattern
+ * above.
+ *
  * The set definitions are written as membership tests; the sets are built
  * by testing candidates and then sorted ascending.  Inputs are read exactly
  * (bf16 bits are widened to fp32 and then to fp64) and all arithmetic is
@@ -77,15 +83,38 @@ static int is_skip(int n, int k, int pi, int M, int bidir, int i, int j)
     return dist / pi >= 1 && dist / pi <= M;
 }
 
-/*
- * Neighbour list of query i (ascending key index, kind 1 = local, 2 = skip).
- * idx/kind must hold at least (2k + 1) + 2M entries.  Returns the count.
- */
-int oracle_neighbors(int n, int k, int pi, int M, int bidir, int i,
-                     int32_t *idx, int8_t *kind)
+/* Membership test for the skip set of a schedule: a skip of some level. */
+static int is_skip_levels(int n, int k, int nlev, const int *lpi, const int *lM,
+                          int bidir, int i, int j)
 {
-    int cnt = 0, a, b, m;
-    /* candidates: the window offsets and the multiples of pi */
+    int r;
+    for (r = 0; r < nlev; ++r)
+        if (is_skip(n, k, lpi[r], lM[r], bidir, i, j))
+            return 1;
+    return 0;
+}
+
+static int in_list(const int32_t *idx, int cnt, int32_t j)
+{
+    int a;
+    for (a = 0; a < cnt; ++a)
+        if (idx[a] == j)
+            return 1;
+    return 0;
+}
+
+/*
+ * Neighbour list of query i under a schedule of nlev levels (ascending key
+ * index, kind 1 = local, 2 = skip; a key reached by several levels appears
+ * once).  idx/kind must hold at least (2k + 1) + 2 sum(M_r) entries.
+ * Returns the count.
+ */
+int oracle_neighbors_levels(int n, int k, int nlev, const int *lpi,
+                            const int *lM, int bidir, int i, int32_t *idx,
+                            int8_t *kind)
+{
+    int cnt = 0, a, b, m, r;
+    /* candidates: the window offsets and the multiples of each period */
     for (a = -k; a <= k; ++a) {
         int j = i + a;
         if (is_local(n, k, bidir, i, j)) {
@@ -94,18 +123,22 @@ int oracle_neighbors(int n, int k, int pi, int M, int bidir, int i,
             ++cnt;
         }
     }
-    for (m = 1; m <= M; ++m) {
-        int64_t jb = (int64_t)i - (int64_t)m * pi;
-        int64_t jf = (int64_t)i + (int64_t)m * pi;
-        if (jb >= 0 && is_skip(n, k, pi, M, bidir, i, (int)jb)) {
-            idx[cnt] = (int32_t)jb;
-            kind[cnt] = KIND_SKIP;
-            ++cnt;
-        }
-        if (bidir && jf < n && is_skip(n, k, pi, M, bidir, i, (int)jf)) {
-            idx[cnt] = (int32_t)jf;
-            kind[cnt] = KIND_SKIP;
-            ++cnt;
+    for (r = 0; r < nlev; ++r) {
+        for (m = 1; m <= lM[r]; ++m) {
+            int64_t jb = (int64_t)i - (int64_t)m * lpi[r];
+            int64_t jf = (int64_t)i + (int64_t)m * lpi[r];
+            if (jb >= 0 && is_skip_levels(n, k, nlev, lpi, lM, bidir, i, (int)jb) &&
+                !in_list(idx, cnt, (int32_t)jb)) {
+                idx[cnt] = (int32_t)jb;
+                kind[cnt] = KIND_SKIP;
+                ++cnt;
+            }
+            if (bidir && jf < n && is_skip_levels(n, k, nlev, lpi, lM, bidir, i, (int)jf) &&
+                !in_list(idx, cnt, (int32_t)jf)) {
+                idx[cnt] = (int32_t)jf;
+                kind[cnt] = KIND_SKIP;
+                ++cnt;
+            }
         }
     }
     /* insertion sort by key index (lists are short) */
@@ -124,6 +157,13 @@ int oracle_neighbors(int n, int k, int pi, int M, int bidir, int i,
     return cnt;
 }
 
+/* The single-period pattern: one level (pi, M).  Capacity (2k + 1) + 2M. */
+int oracle_neighbors(int n, int k, int pi, int M, int bidir, int i,
+                     int32_t *idx, int8_t *kind)
+{
+    return oracle_neighbors_levels(n, k, 1, &pi, &M, bidir, i, idx, kind);
+}
+
 /* log(sigmoid(x)) without overflow; log(1 - sigmoid(x)) = log(sigmoid(-x)). */
 static double log_sigmoid(double x)
 {
@@ -139,11 +179,11 @@ static double log_sigmoid(double x)
 static void attend_row(int n, int i, int d, const void *q, int64_t q_off,
                        const void *kk, const void *vv, int64_t kv_base,
                        int64_t kv_tok_stride, int dt, double g, int kw,
-                       int pi, int M, int bidir, double scale,
-                       int32_t *idx, int8_t *kind, double *sc, double *out,
-                       double *lse)
+                       int nlev, const int *lpi, const int *lM, int bidir,
+                       double scale, int32_t *idx, int8_t *kind, double *sc,
+                       double *out, double *lse)
 {
-    int cnt = oracle_neighbors(n, kw, pi, M, bidir, i, idx, kind);
+    int cnt = oracle_neighbors_levels(n, kw, nlev, lpi, lM, bidir, i, idx, kind);
     int has_skip = 0, a, c;
     double prior_local = log_sigmoid(g), prior_skip = log_sigmoid(-g);
     double mx = -INFINITY, z = 0.0;
@@ -177,7 +217,13 @@ static void attend_row(int n, int i, int d, const void *q, int64_t q_off,
         *lse = mx + log(z);
 }
 
-static int list_cap(int k, int M) { return 2 * k + 1 + 2 * M; }
+static int list_cap(int k, int nlev, const int *lM)
+{
+    int r, c = 2 * k + 1;
+    for (r = 0; r < nlev; ++r)
+        c += 2 * lM[r];
+    return c;
+}
 
 /*
  * Forward (prefill) over a packed batch.
@@ -186,14 +232,16 @@ static int list_cap(int k, int M) { return 2 * k + 1 + 2 * M; }
  *   rows: nrows flat row ids (token * H + head), or NULL for all T*H rows.
  *   out: [nrows, d] fp64; lse: [nrows] fp64 or NULL.
  */
-void oracle_fwd(int nseq, const int64_t *cu, int H, int d, const void *q,
-                const void *kk, const void *vv, int dt, const double *g,
-                int kw, int pi, int M, int bidir, double scale, int64_t nrows,
-                const int64_t *rows, double *out, double *lse, int nthreads)
+void oracle_fwd_levels(int nseq, const int64_t *cu, int H, int d,
+                       const void *q, const void *kk, const void *vv, int dt,
+                       const double *g, int kw, int nlev, const int *lpi,
+                       const int *lM, int bidir, double scale, int64_t nrows,
+                       const int64_t *rows, double *out, double *lse,
+                       int nthreads)
 {
     int64_t total = cu[nseq] * (int64_t)H;
     int64_t count = rows ? nrows : total;
-    int cap = list_cap(kw, M);
+    int cap = list_cap(kw, nlev, lM);
 #ifdef _OPENMP
     if (nthreads > 0)
         omp_set_num_threads(nthreads);
@@ -224,13 +272,22 @@ void oracle_fwd(int nseq, const int64_t *cu, int H, int d, const void *q,
             i = (int)(tok - cu[s]);
             attend_row(n, i, d, q, (tok * H + h) * (int64_t)d, kk, vv,
                        (cu[s] * H + h) * (int64_t)d, (int64_t)H * d, dt,
-                       g[tok * H + h], kw, pi, M, bidir, scale, idx, kind, sc,
-                       out + r * (int64_t)d, lse ? lse + r : NULL);
+                       g[tok * H + h], kw, nlev, lpi, lM, bidir, scale, idx,
+                       kind, sc, out + r * (int64_t)d, lse ? lse + r : NULL);
         }
         free(idx);
         free(kind);
         free(sc);
     }
+}
+
+void oracle_fwd(int nseq, const int64_t *cu, int H, int d, const void *q,
+                const void *kk, const void *vv, int dt, const double *g,
+                int kw, int pi, int M, int bidir, double scale, int64_t nrows,
+                const int64_t *rows, double *out, double *lse, int nthreads)
+{
+    oracle_fwd_levels(nseq, cu, H, d, q, kk, vv, dt, g, kw, 1, &pi, &M, bidir,
+                      scale, nrows, rows, out, lse, nthreads);
 }
 
 /*
@@ -240,12 +297,13 @@ void oracle_fwd(int nseq, const int64_t *cu, int H, int d, const void *q,
  *   (elements, last dim contiguous); lens: [S]; g: [S, H] fp64.
  *   out: [S, H, d] fp64; lse: [S, H] or NULL.
  */
-void oracle_decode(int S, int H, int d, const void *q, const void *kc,
-                   const void *vc, int dt, const int64_t *cs,
-                   const int32_t *lens, const double *g, int kw, int pi, int M,
-                   double scale, double *out, double *lse, int nthreads)
+void oracle_decode_levels(int S, int H, int d, const void *q, const void *kc,
+                          const void *vc, int dt, const int64_t *cs,
+                          const int32_t *lens, const double *g, int kw,
+                          int nlev, const int *lpi, const int *lM, double scale,
+                          double *out, double *lse, int nthreads)
 {
-    int cap = list_cap(kw, M);
+    int cap = list_cap(kw, nlev, lM);
     int64_t total = (int64_t)S * H;
 #ifdef _OPENMP
     if (nthreads > 0)
@@ -265,13 +323,22 @@ void oracle_decode(int S, int H, int d, const void *q, const void *kc,
             int n = lens[s];
             attend_row(n, n - 1, d, q, r * (int64_t)d, kc, vc,
                        (int64_t)s * cs[0] + (int64_t)h * cs[1], cs[2], dt,
-                       g[r], kw, pi, M, 0, scale, idx, kind, sc,
+                       g[r], kw, nlev, lpi, lM, 0, scale, idx, kind, sc,
                        out + r * (int64_t)d, lse ? lse + r : NULL);
         }
         free(idx);
         free(kind);
         free(sc);
     }
+}
+
+void oracle_decode(int S, int H, int d, const void *q, const void *kc,
+                   const void *vc, int dt, const int64_t *cs,
+                   const int32_t *lens, const double *g, int kw, int pi, int M,
+                   double scale, double *out, double *lse, int nthreads)
+{
+    oracle_decode_levels(S, H, d, q, kc, vc, dt, cs, lens, g, kw, 1, &pi, &M,
+                         scale, out, lse, nthreads);
 }
 
 /*
@@ -292,13 +359,15 @@ void oracle_decode(int S, int H, int d, const void *q, const void *kc,
  *              -sigmoid(g) for a skip key, and no term when the row has no
  *              skip key (it has no prior).
  */
-void oracle_bwd(int nseq, const int64_t *cu, int H, int d, const void *q,
-                const void *kk, const void *vv, int dt, const double *g,
-                const void *dout, int dtd, int kw, int pi, int M, int bidir,
-                double scale, double *dq, double *dk, double *dv, double *dg)
+void oracle_bwd_levels(int nseq, const int64_t *cu, int H, int d,
+                       const void *q, const void *kk, const void *vv, int dt,
+                       const double *g, const void *dout, int dtd, int kw,
+                       int nlev, const int *lpi, const int *lM, int bidir,
+                       double scale, double *dq, double *dk, double *dv,
+                       double *dg)
 {
     int64_t T = cu[nseq];
-    int cap = list_cap(kw, M);
+    int cap = list_cap(kw, nlev, lM);
     int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * cap);
     int8_t *kind = (int8_t *)malloc((size_t)cap);
     double *sc = (double *)malloc(sizeof(double) * cap);
@@ -316,7 +385,7 @@ void oracle_bwd(int nseq, const int64_t *cu, int H, int d, const void *q,
             int64_t ts = (int64_t)H * d;                 /* token stride */
             for (i = 0; i < n; ++i) {
                 int64_t qo = base + i * ts, go = (cu[s] + i) * H + h;
-                int cnt = oracle_neighbors(n, kw, pi, M, bidir, i, idx, kind);
+                int cnt = oracle_neighbors_levels(n, kw, nlev, lpi, lM, bidir, i, idx, kind);
                 int has_skip = 0;
                 double ga = g[go], mx = -INFINITY, z = 0.0, D = 0.0;
                 double alpha = 1.0 / (1.0 + exp(-ga));
@@ -363,6 +432,15 @@ void oracle_bwd(int nseq, const int64_t *cu, int H, int d, const void *q,
     free(dp);
 }
 
+void oracle_bwd(int nseq, const int64_t *cu, int H, int d, const void *q,
+                const void *kk, const void *vv, int dt, const double *g,
+                const void *dout, int dtd, int kw, int pi, int M, int bidir,
+                double scale, double *dq, double *dk, double *dv, double *dg)
+{
+    oracle_bwd_levels(nseq, cu, H, d, q, kk, vv, dt, g, dout, dtd, kw, 1, &pi,
+                      &M, bidir, scale, dq, dk, dv, dg);
+}
+
 int oracle_max_threads(void)
 {
 #ifdef _OPENMP
@@ -377,12 +455,13 @@ int oracle_max_threads(void)
  * idx [q_count, cap] (-1 padding), kind [q_count, cap] (0 padding),
  * count [q_count].  Returns 0, or -1 if some list does not fit in cap.
  */
-int oracle_neighbor_table(int n, int k, int pi, int M, int bidir, int q_begin,
-                          int q_count, int cap, int32_t *idx, int8_t *kind,
-                          int32_t *count)
+int oracle_neighbor_table_levels(int n, int k, int nlev, const int *lpi,
+                                 const int *lM, int bidir, int q_begin,
+                                 int q_count, int cap, int32_t *idx,
+                                 int8_t *kind, int32_t *count)
 {
     int bad = 0;
-    int full = list_cap(k, M);
+    int full = list_cap(k, nlev, lM);
 #pragma omp parallel
     {
         int32_t *ti = (int32_t *)malloc(sizeof(int32_t) * full);
@@ -390,7 +469,7 @@ int oracle_neighbor_table(int n, int k, int pi, int M, int bidir, int q_begin,
         int r;
 #pragma omp for schedule(static)
         for (r = 0; r < q_count; ++r) {
-            int c = oracle_neighbors(n, k, pi, M, bidir, q_begin + r, ti, tk);
+            int c = oracle_neighbors_levels(n, k, nlev, lpi, lM, bidir, q_begin + r, ti, tk);
             int a;
             if (c > cap) {
 #pragma omp atomic write
@@ -407,4 +486,12 @@ int oracle_neighbor_table(int n, int k, int pi, int M, int bidir, int q_begin,
         free(tk);
     }
     return bad ? -1 : 0;
+}
+
+int oracle_neighbor_table(int n, int k, int pi, int M, int bidir, int q_begin,
+                          int q_count, int cap, int32_t *idx, int8_t *kind,
+                          int32_t *count)
+{
+    return oracle_neighbor_table_levels(n, k, 1, &pi, &M, bidir, q_begin,
+                                        q_count, cap, idx, kind, count);
 }

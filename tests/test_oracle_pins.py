@@ -349,3 +349,105 @@ def test_backward_dv_columns_sum_to_dout(oracle_lib):
     for s in range(len(lens)):
         sl = slice(cu[s], cu[s + 1])
         np.testing.assert_allclose(dv[sl].sum(axis=0), dout[sl].sum(axis=0), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- skip schedules
+# A schedule is a list of levels (pi_r, M_r) whose skip sets are unioned (the
+# hierarchical skip schedules the Dutch gist.science summary names as future
+# work, section 5 "Betekenis en Conclusie").  Pins: the dense-mask oracle
+# (an elementwise OR of per-level masks, written independently), closed-form
+# pair counts from the set of distinct distances, and the fact that levels
+# whose distances another level already has change nothing.
+
+def _distances(kw, levels):
+    return sorted({m * p for p, M in levels for m in range(1, M + 1) if m * p > kw})
+
+
+@pytest.mark.parametrize("bidir", [False, True])
+@pytest.mark.parametrize("n,kw,levels", [
+    (200, 3, [(8, 2), (4, 3), (16, 2)]),
+    (300, 5, [(16, 4), (32, 4), (64, 4)]),
+    (150, 2, [(3, 9), (5, 6)]),
+    (97, 20, [(8, 1), (7, 5), (50, 2)]),
+])
+def test_schedule_closed_form_counts(oracle_lib, n, kw, levels, bidir):
+    (pi, M), extra = levels[0], levels[1:]
+    idx, kind, cnt = oracle.neighbor_table(n, kw, pi, M, bidir, levels=extra)
+    skips = int((kind == 2).sum())
+    per_dir = sum(max(0, n - dd) for dd in _distances(kw, levels))
+    assert skips == (2 if bidir else 1) * per_dir
+    # every list is strictly ascending (no key twice)
+    for r in range(n):
+        row = idx[r, :cnt[r]]
+        assert np.all(np.diff(row) > 0)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_schedule_c_oracle_matches_dense(oracle_lib, seed):
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(1, 70))
+    d = int(rng.choice([4, 8]))
+    kw = int(rng.integers(0, 10))
+    nlev = int(rng.integers(1, 4))
+    levels = [(int(rng.integers(1, 14)), int(rng.integers(0, 7))) for _ in range(nlev)]
+    bidir = bool(seed % 2)
+    q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
+    g = rng.standard_normal(n) * 3
+    (pi, M), extra = levels[0], levels[1:]
+    out, lse = oracle.fwd(q[:, None], k[:, None], v[:, None], g[:, None], [0, n], kw, pi, M, bidir, 0.3,
+                          want_lse=True, levels=extra)
+    ref, rlse = dense.attention(q, k, v, g, kw, pi, M, bidir, 0.3, want_lse=True, levels=extra)
+    np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rlse, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("bidir", [False, True])
+def test_schedule_redundant_levels_change_nothing(oracle_lib, bidir):
+    # (2 pi, M/2) and (pi, 1) add only distances (pi, M) already has
+    n, d, kw, pi, M = 120, 8, 3, 5, 6
+    q, k, v = (_rand((n, 2, d), s) for s in (61, 62, 63))
+    g = _rand((n, 2), 64, 2.0)
+    cu = [0, n]
+    one = oracle.fwd(q, k, v, g, cu, kw, pi, M, bidir, 0.4)
+    many = oracle.fwd(q, k, v, g, cu, kw, pi, M, bidir, 0.4, levels=[(2 * pi, M // 2), (pi, 1)])
+    assert np.array_equal(one, many)
+    dout = _rand((n, 2, d), 65)
+    a = oracle.bwd(q, k, v, g, dout, cu, kw, pi, M, bidir, 0.4)
+    b = oracle.bwd(q, k, v, g, dout, cu, kw, pi, M, bidir, 0.4, levels=[(2 * pi, M // 2)])
+    assert all(np.array_equal(x, y) for x, y in zip(a, b))
+
+
+def test_schedule_decode_equals_last_prefill_row(oracle_lib):
+    n, d, kw = 90, 8, 4
+    levels = [(6, 3), (12, 3), (24, 3)]
+    q, k, v = (_rand((n, 1, d), s) for s in (71, 72, 73))
+    g = _rand((n, 1), 74)
+    out = oracle.fwd(q, k, v, g, [0, n], kw, 6, 3, False, 0.5, levels=levels[1:])
+    dec = oracle.decode(q[n - 1:n], k.transpose(1, 0, 2)[None], v.transpose(1, 0, 2)[None], [n],
+                        g[n - 1:n], kw, 6, 3, 0.5, levels=levels[1:])
+    np.testing.assert_allclose(dec[0], out[n - 1:n], rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("bidir", [False, True])
+def test_schedule_backward_matches_finite_differences(oracle_lib, bidir):
+    lens = [11, 14]
+    levels = [(2, 2), (3, 2), (6, 2)]
+    q, k, v, g, dout, cu = _fd_case(91 + int(bidir), lens, 2, 3, 1, 2, 2, bidir, 0.6)
+
+    def loss():
+        out = oracle.fwd(q, k, v, g, cu, 1, 2, 2, bidir, 0.6, levels=levels[1:])
+        return float((out * dout.reshape(out.shape)).sum())
+
+    dq, dk, dv, dg = oracle.bwd(q, k, v, g, dout, cu, 1, 2, 2, bidir, 0.6, levels=levels[1:])
+    h = 1e-5
+    for name, x, gx in (("q", q, dq), ("k", k, dk), ("v", v, dv), ("g", g, dg)):
+        flat, gflat = x.reshape(-1), gx.reshape(-1)
+        for e in range(flat.size):
+            keep = flat[e]
+            flat[e] = keep + h
+            lp = loss()
+            flat[e] = keep - h
+            lm = loss()
+            flat[e] = keep
+            fd = (lp - lm) / (2 * h)
+            assert abs(fd - gflat[e]) <= 1e-6 * max(1.0, abs(fd)), (name, e, fd, gflat[e])
