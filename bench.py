@@ -59,18 +59,17 @@ def pair_counts(w, lengths=None):
     range arithmetic (vectorised over rows)."""
     import numpy as np
 
+    # the distinct skip distances beyond the window (one level, or the union
+    # of a schedule's levels); distance dd is a skip of the rows i >= dd
+    # (and, bidirectional, of the rows i + dd <= n - 1)
+    dist = sorted({m * p for p, M in [(w.pi, w.M)] + list(w.levels) for m in range(1, M + 1) if m * p > w.k})
+
     def one(n):
         i = np.arange(n, dtype=np.int64)
         lo = np.maximum(0, i - w.k)
         hi = np.minimum(n - 1, i + w.k) if w.bidir else i
-        mlo = w.k // w.pi + 1
-        mb = np.minimum(w.M, i // w.pi)
-        nb = np.maximum(0, mb - mlo + 1)
-        nf = 0
-        if w.bidir:
-            mf = np.minimum(w.M, (n - 1 - i) // w.pi)
-            nf = np.maximum(0, mf - mlo + 1)
-        return int((hi - lo + 1).sum()), int((nb + nf).sum())
+        sk = sum(max(0, n - dd) for dd in dist) * (2 if w.bidir else 1)
+        return int((hi - lo + 1).sum()), int(sk)
 
     if w.nseq:
         tot = [one(n) for n in lengths]
@@ -129,7 +128,7 @@ def cpu_baseline(w, x, budget_s: float):
     while True:
         rows = np.sort(rng.integers(0, total_rows, count))
         t0 = time.perf_counter()
-        oracle.fwd(q, k, v, g, cu, w.k, w.pi, w.M, w.bidir, w.scale, rows=rows)
+        oracle.fwd(q, k, v, g, cu, w.k, w.pi, w.M, w.bidir, w.scale, rows=rows, levels=w.levels)
         elapsed = time.perf_counter() - t0
         if elapsed >= budget_s * 0.5 or count >= total_rows:
             break
@@ -140,7 +139,7 @@ def cpu_baseline(w, x, budget_s: float):
         passes = max(1, min(200, int(budget_s * 0.5 / max(elapsed, 1e-3))))
         t0 = time.perf_counter()
         for _ in range(passes):
-            oracle.fwd(q, k, v, g, cu, w.k, w.pi, w.M, w.bidir, w.scale, rows=rows)
+            oracle.fwd(q, k, v, g, cu, w.k, w.pi, w.M, w.bidir, w.scale, rows=rows, levels=w.levels)
         elapsed = time.perf_counter() - t0
     what = ("%d uniformly sampled query rows" % count if count < total_rows
             else "all query rows, %d pass%s," % (passes, "es" if passes > 1 else ""))
@@ -234,7 +233,7 @@ def bench_backward(args, w, dev, sets, outs, lengths, rows):
     for j, x in enumerate(sets):
         lses.append(torch.empty_like(x["g"]))
         pa.fwd(x["q"], x["k"], x["v"], x["g"], window_k=w.k, period_pi=w.pi, num_skips=w.M,
-               bidirectional=w.bidir, cu_seqlens=x.get("cu_seqlens"),
+               levels=w.levels, bidirectional=w.bidir, cu_seqlens=x.get("cu_seqlens"),
                max_seqlen=max(lengths) if lengths else None, out=outs[j], lse=lses[j])
     douts = []
     for j, x in enumerate(sets):
@@ -249,7 +248,8 @@ def bench_backward(args, w, dev, sets, outs, lengths, rows):
     def step(j):
         x = sets[j % nsets]
         pa.bwd(x["q"], x["k"], x["v"], x["g"], outs[j % nsets], douts[j % nsets], window_k=w.k,
-               period_pi=w.pi, num_skips=w.M, bidirectional=w.bidir, cu_seqlens=x.get("cu_seqlens"),
+               period_pi=w.pi, num_skips=w.M, levels=w.levels, bidirectional=w.bidir,
+               cu_seqlens=x.get("cu_seqlens"),
                max_seqlen=max(lengths) if lengths else None, lse=lses[j % nsets], workspace=ws)
 
     ms_per_step = timed(step, args, dev)
@@ -264,7 +264,7 @@ def bench_backward(args, w, dev, sets, outs, lengths, rows):
            "data": "synthetic (seeded N(0,1) q/k/v/dout, N(0,1) gate logits)",
            "config": {"workload": w.name, "pass": "backward", "B": w.B if not w.nseq else len(lengths),
                       "H": w.H, "n": w.n if not w.nseq else max(lengths), "d": w.d, "k": w.k, "pi": w.pi,
-                      "M": w.M, "bidirectional": w.bidir},
+                      "M": w.M, "bidirectional": w.bidir, **({"levels": [list(l) for l in w.levels]} if w.levels else {})},
            "kernel_digest": kernel_digest(),
            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
@@ -414,13 +414,13 @@ def main():
     # one workspace for every step (the steps are ordered on one stream)
     nb = pa.fwd_workspace_bytes(1 if w.dtype == "bf16" else 0, len(lengths) if lengths else w.B, w.H,
                                 max(lengths) if lengths else w.n, w.d,
-                                pa.make_pattern(w.k, w.pi, w.M, w.bidir, w.scale))
+                                pa.make_pattern(w.k, w.pi, w.M, w.bidir, w.scale, w.levels))
     ws = torch.empty(nb, dtype=torch.uint8, device=dev) if nb else None
 
     def step(j):
         x = sets[j % nsets]
         pa.fwd(x["q"], x["k"], x["v"], x["g"], window_k=w.k, period_pi=w.pi, num_skips=w.M,
-               bidirectional=w.bidir, cu_seqlens=x.get("cu_seqlens"),
+               levels=w.levels, bidirectional=w.bidir, cu_seqlens=x.get("cu_seqlens"),
                max_seqlen=max(lengths) if lengths else None, out=outs[j % nsets], workspace=ws)
 
     if args.backward:
@@ -451,6 +451,8 @@ def main():
            "n": w.n if not w.nseq else max(lengths), "d": w.d, "k": w.k, "pi": w.pi, "M": w.M,
            "bidirectional": w.bidir, "global_batch": w.B, "seq_len": w.n,
            "parallelism": "single GPU", "input_sets": nsets}
+    if w.levels:
+        cfg["levels"] = [list(l) for l in w.levels]
     res = {"metric": METRIC, "value": round(qps, 1), "unit": "queries/s", "n_gpus": 1,
            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16"

@@ -64,13 +64,28 @@ enum {
  *   num_skips_M   M >= 0: skips per direction
  *   bidirectional 0 = causal, 1 = two-sided window and skips
  *   scale         logit scale; <= 0 selects 1/sqrt(d)
+ *   num_levels    0..PIATTN_MAX_LEVELS: extra skip levels (a skip schedule,
+ *                 the hierarchical schedules the Dutch gist.science summary
+ *                 names as future work, section 5 "Betekenis en Conclusie");
+ *                 level r adds the skips i -/+ m*level_pi[r], 1 <= m <=
+ *                 level_M[r].  The skip set is the union over (period_pi,
+ *                 num_skips_M) and the extra levels, each key once, every
+ *                 skip key with the log(1 - alpha) prior.  With extra levels
+ *                 the distinct skip distances beyond the window must be
+ *                 multiples m*g, m < 128, of g = gcd of the periods of the
+ *                 levels with M > 0 (else PIATTN_EUNSUPPORTED).
+ * A zero-initialised tail (num_levels = 0) is the single-period pattern.
  */
+#define PIATTN_MAX_LEVELS 7
 typedef struct {
     int32_t window_k;
     int32_t period_pi;
     int32_t num_skips_M;
     int32_t bidirectional;
     float scale;
+    int32_t num_levels;
+    int32_t level_pi[PIATTN_MAX_LEVELS];
+    int32_t level_M[PIATTN_MAX_LEVELS];
 } piattn_pattern;
 
 /*

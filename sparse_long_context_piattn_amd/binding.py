@@ -34,11 +34,16 @@ class PiattnError(RuntimeError):
         self.code = code
 
 
+MAX_LEVELS = 7
+
+
 class Pattern(ctypes.Structure):
-    """piattn_pattern: window half-width k, period pi, skips M, direction, scale."""
+    """piattn_pattern: window half-width k, period pi, skips M, direction,
+    scale, and the extra levels (pi_r, M_r) of a skip schedule."""
     _fields_ = [("window_k", ctypes.c_int32), ("period_pi", ctypes.c_int32),
                 ("num_skips_M", ctypes.c_int32), ("bidirectional", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("num_levels", ctypes.c_int32),
+                ("level_pi", ctypes.c_int32 * MAX_LEVELS), ("level_M", ctypes.c_int32 * MAX_LEVELS)]
 
 
 Strides = ctypes.c_int64 * 15
@@ -97,8 +102,17 @@ def _check(rc: int):
         raise PiattnError(rc, lib().piattn_last_error().decode())
 
 
-def make_pattern(k: int, pi: int, M: int, bidir: bool = False, scale: float = 0.0) -> Pattern:
-    return Pattern(int(k), int(pi), int(M), int(bool(bidir)), float(scale))
+def make_pattern(k: int, pi: int, M: int, bidir: bool = False, scale: float = 0.0, levels=()) -> Pattern:
+    """levels: extra (pi_r, M_r) skip levels; the skip set is the union over
+    (pi, M) and these (a skip schedule)."""
+    levels = [(int(a), int(b)) for a, b in (levels or ())]
+    if len(levels) > MAX_LEVELS:
+        raise ValueError("at most %d extra levels" % MAX_LEVELS)
+    p = Pattern(int(k), int(pi), int(M), int(bool(bidir)), float(scale), len(levels))
+    for r, (a, b) in enumerate(levels):
+        p.level_pi[r] = a
+        p.level_M[r] = b
+    return p
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -170,7 +184,7 @@ def fwd_workspace_bytes(dtype_code: int, B: int, H: int, n: int, d: int, pattern
 
 def fwd(q, k, v, g, *, window_k: int, period_pi: int, num_skips: int, bidirectional=False,
         scale: float = 0.0, cu_seqlens=None, max_seqlen: int | None = None, out=None,
-        lse=None, workspace=None):
+        lse=None, workspace=None, levels=()):
     """pi-Attention prefill.
 
     Dense: q, k, v [B, H, n, d] (any strides, last dim contiguous), g [B, H, n].
@@ -197,7 +211,7 @@ def fwd(q, k, v, g, *, window_k: int, period_pi: int, num_skips: int, bidirectio
     B, H, n, d, strides, cu_ptr = geo
     if lse is not None and (lse.shape != g.shape or lse.stride() != g.stride()):
         raise ValueError("lse must have g's shape and strides")
-    pat = make_pattern(window_k, period_pi, num_skips, bidirectional, scale)
+    pat = make_pattern(window_k, period_pi, num_skips, bidirectional, scale, levels)
     need = fwd_workspace_bytes(code, B, H, n, d, pat)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -211,7 +225,8 @@ def fwd(q, k, v, g, *, window_k: int, period_pi: int, num_skips: int, bidirectio
 
 
 def bwd(q, k, v, g, out, dout, *, window_k: int, period_pi: int, num_skips: int, bidirectional=False,
-        scale: float = 0.0, cu_seqlens=None, max_seqlen: int | None = None, lse=None, workspace=None):
+        scale: float = 0.0, cu_seqlens=None, max_seqlen: int | None = None, lse=None, workspace=None,
+        levels=()):
     """Backward of fwd: the gradients (dq, dk, dv, dg) of a loss whose gradient
     with respect to fwd's output `out` is `dout`.  dq, dk, dv have the shapes
     and strides of q, k, v (allocated like them); dg is fp32 like g.  dout
@@ -240,7 +255,7 @@ def bwd(q, k, v, g, out, dout, *, window_k: int, period_pi: int, num_skips: int,
     if geo is None:
         return dq, dk, dv, dg
     B, H, n, d, strides, cu_ptr = geo
-    pat = make_pattern(window_k, period_pi, num_skips, bidirectional, scale)
+    pat = make_pattern(window_k, period_pi, num_skips, bidirectional, scale, levels)
     need = int(lib().piattn_bwd_workspace_bytes(B, H, n))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -256,9 +271,10 @@ def decode_workspace_bytes(S, H, d, num_splits, pattern: Pattern) -> int:
     return int(lib().piattn_decode_workspace_bytes(S, H, d, num_splits, ctypes.byref(pattern)))
 
 
-def rolling_slots(window_k: int, period_pi: int, num_skips: int) -> int:
-    """Rows of a rolling decode cache for this pattern: max(k, M*pi) + 1."""
-    return int(lib().piattn_rolling_slots(ctypes.byref(make_pattern(window_k, period_pi, num_skips))))
+def rolling_slots(window_k: int, period_pi: int, num_skips: int, levels=()) -> int:
+    """Rows of a rolling decode cache for this pattern: max(k, longest skip) + 1."""
+    pat = make_pattern(window_k, period_pi, num_skips, levels=levels)
+    return int(lib().piattn_rolling_slots(ctypes.byref(pat)))
 
 
 def cache_append(k_new, v_new, k_cache, v_cache, positions):
@@ -287,7 +303,7 @@ def cache_append(k_new, v_new, k_cache, v_cache, positions):
 
 def decode(q, k_cache, v_cache, cache_lens, g, *, window_k: int, period_pi: int,
            num_skips: int, scale: float = 0.0, num_splits: int = 0, workspace=None, out=None,
-           rolling: bool = False):
+           rolling: bool = False, levels=()):
     """pi-Attention decode: q [S, H, d], caches [S, H, L, d] (strided, last dim
     contiguous), cache_lens int32 [S] (query position len-1), g [S, H].
     rolling: the caches are rolling caches of L rows (position j in row j mod L).
@@ -305,7 +321,7 @@ def decode(q, k_cache, v_cache, cache_lens, g, *, window_k: int, period_pi: int,
         raise ValueError("g must be float32 [S, H]")
     if out is None:
         out = torch.empty_like(q)
-    pat = make_pattern(window_k, period_pi, num_skips, False, scale)
+    pat = make_pattern(window_k, period_pi, num_skips, False, scale, levels)
     need = decode_workspace_bytes(S, H, d, num_splits, pat)
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -325,16 +341,16 @@ def decode(q, k_cache, v_cache, cache_lens, g, *, window_k: int, period_pi: int,
     return out
 
 
-def neighbors_cap(window_k, period_pi, num_skips, bidirectional=False) -> int:
-    pat = make_pattern(window_k, period_pi, num_skips, bidirectional)
+def neighbors_cap(window_k, period_pi, num_skips, bidirectional=False, levels=()) -> int:
+    pat = make_pattern(window_k, period_pi, num_skips, bidirectional, levels=levels)
     return int(lib().piattn_neighbors_cap(ctypes.byref(pat)))
 
 
 def neighbors(n: int, *, window_k: int, period_pi: int, num_skips: int, bidirectional=False,
               q_begin: int = 0, q_count: int | None = None, cap: int | None = None,
-              device="cuda"):
+              device="cuda", levels=()):
     """Debug dump: (idx int32 [q_count, cap], kind int8, count int32) on the GPU."""
-    pat = make_pattern(window_k, period_pi, num_skips, bidirectional)
+    pat = make_pattern(window_k, period_pi, num_skips, bidirectional, levels=levels)
     if q_count is None:
         q_count = n - q_begin
     if cap is None:

@@ -42,11 +42,81 @@ int check_pattern(const piattn_pattern* p, PiPattern* out) {
     if (p->bidirectional != 0 && p->bidirectional != 1)
         return fail(PIATTN_EINVAL, "bidirectional=%d must be 0 or 1", p->bidirectional);
     if (!isfinite(p->scale)) return fail(PIATTN_EINVAL, "scale is not finite");
+    if (p->num_levels < 0 || p->num_levels > PIATTN_MAX_LEVELS)
+        return fail(PIATTN_EINVAL, "num_levels=%d out of range [0, %d]", p->num_levels, PIATTN_MAX_LEVELS);
+    for (int r = 0; r < p->num_levels; ++r) {
+        if (p->level_pi[r] < 1 || p->level_pi[r] >= kMaxExtent)
+            return fail(PIATTN_EINVAL, "level_pi[%d]=%d out of range [1, 2^30)", r, p->level_pi[r]);
+        if (p->level_M[r] < 0 || p->level_M[r] >= kMaxExtent)
+            return fail(PIATTN_EINVAL, "level_M[%d]=%d out of range [0, 2^30)", r, p->level_M[r]);
+    }
+    *out = PiPattern{};
     out->k = p->window_k;
     out->pi = p->period_pi;
     out->M = p->num_skips_M;
     out->bidir = p->bidirectional;
+    out->mlo = p->window_k / p->period_pi + 1;
+    if (p->num_levels == 0) return PIATTN_OK;
+    // A schedule: the union of the levels' skip distances beyond the window,
+    // as multiples of g = gcd of the periods (of the levels with M > 0).
+    int32_t lp[PIATTN_MAX_LEVELS + 1], lm[PIATTN_MAX_LEVELS + 1];
+    lp[0] = p->period_pi;
+    lm[0] = p->num_skips_M;
+    for (int r = 0; r < p->num_levels; ++r) {
+        lp[r + 1] = p->level_pi[r];
+        lm[r + 1] = p->level_M[r];
+    }
+    const int nl = p->num_levels + 1;
+    int64_t g = 0;
+    for (int r = 0; r < nl; ++r) {
+        if (lm[r] == 0) continue;
+        int64_t a = g, b = lp[r];
+        while (b) {
+            const int64_t t = a % b;
+            a = b;
+            b = t;
+        }
+        g = a;
+    }
+    if (g == 0) {                                       // no level has skips
+        out->M = 0;
+        return PIATTN_OK;
+    }
+    uint32_t mask[4] = {0, 0, 0, 0};
+    for (int r = 0; r < nl; ++r) {
+        const int64_t step = lp[r] / g;                 // multiples of g per multiple of lp[r]
+        for (int64_t m = 1; m <= lm[r]; ++m) {
+            const int64_t mm = m * step;                 // distance mm * g
+            if (mm * g <= p->window_k) continue;        // inside the window
+            if (mm >= kMaskBits)
+                return fail(PIATTN_EUNSUPPORTED,
+                            "skip schedule reaches distance %lld = %lld * gcd %lld (at most 127 multiples of the "
+                            "periods' gcd)", (long long)(mm * g), (long long)mm, (long long)g);
+            mask[mm >> 5] |= 1u << (mm & 31);
+        }
+    }
+    int32_t lo = -1, hi = 0, cnt = 0;
+    for (int32_t m = 0; m < kMaskBits; ++m)
+        if ((mask[m >> 5] >> (m & 31)) & 1u) {
+            if (lo < 0) lo = m;
+            hi = m;
+            ++cnt;
+        }
+    out->pi = (int32_t)g;
+    out->M = hi;
+    out->mlo = lo < 0 ? out->k / out->pi + 1 : lo;
+    if (lo >= 0 && cnt != hi - lo + 1) {                // not one contiguous range of multiples
+        out->masked = 1;
+        for (int w = 0; w < 4; ++w) out->mask[w] = mask[w];
+    }
     return PIATTN_OK;
+}
+
+// Skip keys per direction at most: multiples in the mask, else M.
+int64_t skip_cap(const PiPattern& p) {
+    if (!p.masked) return p.M;
+    return __builtin_popcount(p.mask[0]) + __builtin_popcount(p.mask[1]) + __builtin_popcount(p.mask[2]) +
+           __builtin_popcount(p.mask[3]);
 }
 
 float scale_nat(const piattn_pattern* p, int d) { return p->scale > 0.0f ? p->scale : 1.0f / sqrtf((float)d); }
@@ -101,7 +171,8 @@ const char* piattn_version(void) { return "libpiattn 0.1 (gfx950)"; }
 int32_t piattn_neighbors_cap(const piattn_pattern* pattern) {
     PiPattern p;
     if (check_pattern(pattern, &p) != PIATTN_OK) return -1;
-    const int64_t cap = p.bidir ? 2LL * p.k + 1 + 2LL * p.M : (int64_t)p.k + 1 + p.M;
+    const int64_t sk = skip_cap(p);
+    const int64_t cap = p.bidir ? 2LL * p.k + 1 + 2 * sk : (int64_t)p.k + 1 + sk;
     return cap > INT32_MAX ? -1 : (int32_t)cap;
 }
 
@@ -114,7 +185,8 @@ int piattn_neighbors(int32_t n, const piattn_pattern* pattern, int32_t q_begin, 
     if (q_begin < 0 || q_count < 0 || (int64_t)q_begin + q_count > n)
         return fail(PIATTN_EINVAL, "query range [%d, %d+%d) not inside [0, %d)", q_begin, q_begin,
                     q_count, n);
-    const int64_t need = p.bidir ? 2LL * p.k + 1 + 2LL * p.M : (int64_t)p.k + 1 + p.M;
+    const int64_t sk = skip_cap(p);
+    const int64_t need = p.bidir ? 2LL * p.k + 1 + 2 * sk : (int64_t)p.k + 1 + sk;
     const int64_t need_n = need < n ? need : n;  // a list never exceeds n keys
     if (cap < need_n)
         return fail(PIATTN_EINVAL, "cap=%d is smaller than the longest list (%lld)", cap,
@@ -130,7 +202,7 @@ int piattn_neighbors(int32_t n, const piattn_pattern* pattern, int32_t q_begin, 
 // bf16 at d = 64 / 128 with a non-empty skip set can take that path.
 static size_t fwd_split_workspace(int dtype, int32_t B, int32_t H, int32_t n, int32_t d, const PiPattern& p) {
     if (dtype != PIATTN_BF16 || (d != 64 && d != 128)) return 0;
-    if (p.M < p.k / p.pi + 1) return 0;
+    if (p.M < p.mlo) return 0;
     return (size_t)B * H * n * 2 * sizeof(float);
 }
 
@@ -326,7 +398,7 @@ int32_t piattn_decode_auto_splits(int32_t S, int32_t H, int32_t d, const piattn_
 // still held: the window reaches back k positions, the skips M*pi (when the
 // pattern has skip keys outside the window).  -1 when that exceeds int32.
 static int64_t rolling_slots_for(const PiPattern& p) {
-    const int64_t back = p.M >= p.k / p.pi + 1 ? (int64_t)p.M * p.pi : 0;
+    const int64_t back = p.M >= p.mlo ? (int64_t)p.M * p.pi : 0;
     const int64_t w = (back > p.k ? back : p.k) + 1;
     return w < kMaxExtent ? w : -1;
 }

@@ -100,7 +100,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs ba) {
         float s = -INFINITY;
         if (u < U) {
             bool loc;
-            const int32_t key = span_key(sp, i, a.pat.pi, u, &loc);
+            const int32_t key = span_key(sp, i, a.pat, u, &loc);
             float k8[8];
             Elem<T>::load8(kb + (int64_t)key * a.sk.t + c, k8);
             float dot = 0.0f;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs ba) {
         const int32_t u = base + slot;
         if (u < U) {
             bool loc;
-            const int32_t key = span_key(sp, i, a.pat.pi, u, &loc);
+            const int32_t key = span_key(sp, i, a.pat, u, &loc);
             float k8[8], v8[8];
             Elem<T>::load8(kb + (int64_t)key * a.sk.t + c, k8);
             Elem<T>::load8(vb + (int64_t)key * a.sv.t + c, v8);
@@ -164,37 +164,33 @@ __global__ __launch_bounds__(256) void bwd_dq_kernel(BwdArgs ba) {
 
 // The queries whose union holds key j, as union positions u in [0, total):
 // the window rows [wlo, whi], then (bidirectional) the rows j - m pi, then
-// the rows j + m pi, m from mlo.
+// the rows j + m pi, m running over the pattern's skip multiples.
 struct KeySpan {
     int32_t wlo, whi;   // window rows
-    int32_t mlo;
-    int32_t mb;         // rows j - m pi, m in [mlo, mb] (bidirectional only)
-    int32_t mf;         // rows j + m pi, m in [mlo, mf]
+    int32_t nb;         // rows j - m pi (bidirectional only)
+    int32_t nf;         // rows j + m pi
     __device__ int32_t n_win() const { return whi - wlo + 1; }
-    __device__ int32_t n_back() const { return mb >= mlo ? mb - mlo + 1 : 0; }
-    __device__ int32_t n_fwd() const { return mf >= mlo ? mf - mlo + 1 : 0; }
-    __device__ int32_t total() const { return n_win() + n_back() + n_fwd(); }
-    __device__ int32_t row(int32_t j, int32_t pi, int32_t u, bool* loc) const {
+    __device__ int32_t total() const { return n_win() + nb + nf; }
+    __device__ int32_t row(int32_t j, const PiPattern& p, int32_t u, bool* loc) const {
         if (u < n_win()) {
             *loc = true;
             return wlo + u;
         }
         u -= n_win();
         *loc = false;
-        if (u < n_back()) return j - (mlo + u) * pi;
-        return j + (mlo + u - n_back()) * pi;
+        if (u < nb) return j - skip_multiple(p, u) * p.pi;
+        return j + skip_multiple(p, u - nb) * p.pi;
     }
 };
 
 // Key j is in L(i) iff |i - j| <= k (and i >= j when causal); it is in S(i)
-// iff i - j = +-m pi with 1 <= m <= M and |i - j| > k, i.e. m >= k/pi + 1.
+// iff i - j = +-m pi for a skip multiple m of the pattern (all beyond k).
 __device__ __forceinline__ KeySpan key_span(int32_t j, int32_t n, const PiPattern& p) {
     KeySpan r;
     r.wlo = p.bidir ? imax32(0, j - p.k) : j;
     r.whi = imin32(n - 1, j + p.k);
-    r.mlo = p.k / p.pi + 1;
-    r.mb = p.bidir ? imin32(p.M, j / p.pi) : 0;
-    r.mf = imin32(p.M, (n - 1 - j) / p.pi);
+    r.nb = p.bidir ? skips_upto(p, j / p.pi) : 0;
+    r.nf = skips_upto(p, (n - 1 - j) / p.pi);
     return r;
 }
 
@@ -229,7 +225,7 @@ __global__ __launch_bounds__(256) void bwd_dkv_kernel(BwdArgs ba) {
         const int32_t u = base + slot;
         if (u < U) {
             bool loc;
-            const int32_t i = ks.row(j, a.pat.pi, u, &loc);
+            const int32_t i = ks.row(j, a.pat, u, &loc);
             float q8[8], do8[8];
             Elem<T>::load8(qb + (int64_t)i * a.sq.t + c, q8);
             Elem<T>::load8(dob + (int64_t)i * a.so.t + c, do8);

@@ -113,7 +113,10 @@ __global__ __launch_bounds__(256) void bwd_record_kernel(BwdArgs ba) {
     }
 }
 
-template <int D, bool SKIP, bool BIDIR>
+// MASKED: the skip multiples are a schedule's mask (skip pass only); a
+// separate instantiation keeps the mask test out of the other kernels'
+// register budget.
+template <int D, bool SKIP, bool BIDIR, bool MASKED>
 __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void bwd_band_kernel(BwdArgs ba, int32_t step, int32_t nres,
                                                                          int32_t tiles, int32_t total,
                                                                          int32_t merge) {
@@ -144,7 +147,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void bwd_band_kernel(BwdArgs 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, x = lane & 15, g = lane >> 4;
-    const int32_t kw = a.pat.k, pi = a.pat.pi, M = a.pat.M, mlo = kw / pi + 1;
+    const int32_t kw = a.pat.k, M = a.pat.M, mlo = a.pat.mlo;
     const int32_t dlo = SKIP ? (BIDIR ? -M : mlo) : (BIDIR ? -kw : 0);
     const int32_t dhi = SKIP ? M : kw;
 
@@ -238,6 +241,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void bwd_band_kernel(BwdArgs 
         const int32_t dd = pq - pk;
         bool ok = dd >= dlo && dd <= dhi && pq < L && pk < L;
         if (SKIP && BIDIR) ok = ok && (dd >= mlo || dd <= -mlo);
+        if (MASKED) ok = ok && mask_has(a.pat, BIDIR ? abs(dd) : dd);
         return ok;
     };
     auto pack4 = [](float a0, float a1, float a2, float a3) __attribute__((always_inline)) {
@@ -463,23 +467,23 @@ hipError_t launch_t(const BwdArgs& ba, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_record_kernel<D>), rgrid, dim3(256), 0, stream, ba);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int32_t mlo = a.pat.k / a.pat.pi + 1;
-    const bool skips = a.pat.M >= mlo;
+    const bool skips = a.pat.M >= a.pat.mlo;
     if (skips) {
         const int32_t nres = imin32(a.pat.pi, a.n);
         const int32_t lmax = (a.n - 1) / a.pat.pi + 1;
         const int32_t tiles = (lmax + BT - 1) / BT;
         const int64_t total = (int64_t)tiles * nres * a.H * a.B;
         if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL((bwd_band_kernel<D, true, BIDIR>), dim3((uint32_t)total), dim3(256), 0, stream, ba,
-                           a.pat.pi, nres, tiles, (int32_t)total, 0);
+        auto kern = a.pat.masked ? bwd_band_kernel<D, true, BIDIR, true> : bwd_band_kernel<D, true, BIDIR, false>;
+        hipLaunchKernelGGL(kern, dim3((uint32_t)total), dim3(256), 0, stream, ba, a.pat.pi, nres, tiles,
+                           (int32_t)total, 0);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int32_t tiles = (a.n + BT - 1) / BT;
     const int64_t total = (int64_t)tiles * a.H * a.B;
     if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_band_kernel<D, false, BIDIR>), dim3((uint32_t)total), dim3(256), 0, stream, ba, 1, 1,
+    hipLaunchKernelGGL((bwd_band_kernel<D, false, BIDIR, false>), dim3((uint32_t)total), dim3(256), 0, stream, ba, 1, 1,
                        tiles, (int32_t)total, skips ? 1 : 0);
     return hipGetLastError();
 }

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void fwd_gather_kernel(FwdArgs a) {
     gate_priors(a.g[goff], sp.has_skip(), &pl, &ps);
 
     RowPartial st;
-    gather_row<T, D>(qrow, kb, vb, a.sk.t, a.sv.t, sp, i, a.pat.pi, 0, sp.total(), pl, ps,
+    gather_row<T, D>(qrow, kb, vb, a.sk.t, a.sv.t, sp, i, a.pat, 0, sp.total(), pl, ps,
                      a.scale_log2, st);
     reduce_slots<D>(st);
 

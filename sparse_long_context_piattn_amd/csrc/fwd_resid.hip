@@ -676,6 +676,8 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
 
 bool fwd_resid_supported(int dtype, const FwdArgs& a) {
     if (dtype != 1 || a.d != 64 || a.pat.pi % AT != 0) return false;
+    // the contiguous skip range [floor(k/pi)+1, M] only (no skip schedules)
+    if (a.pat.masked || a.pat.mlo != a.pat.k / a.pat.pi + 1) return false;
     int64_t ts = a.sk.t > a.sv.t ? a.sk.t : a.sv.t;
     ts = ts > a.sq.t ? ts : a.sq.t;
     if ((int64_t)a.n * ts + D >= ((int64_t)1 << 31)) return false;   // 32-bit row offsets

@@ -55,6 +55,13 @@ struct Geo {
 template <int D>
 __device__ __forceinline__ int swu(int r, int c) { return r * D + ((c ^ ((r >> 1) & 7)) << 3); }
 
+// Whether key period kp is a skip key of query period tq under a skip
+// schedule's mask of multiples (masked patterns only).
+template <bool BIDIR>
+__device__ __forceinline__ bool in_schedule(const PiPattern& p, int32_t tq, int32_t kp) {
+    return mask_has(p, BIDIR ? abs(tq - kp) : tq - kp);
+}
+
 // Whether row (residue a, period t) with pr periods in its residue has any
 // skip key.
 template <bool BIDIR>
@@ -159,7 +166,7 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_kernel(FwdArgs a, float* lse
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, x = lane & 15, g = lane >> 4;
-    const int32_t pi = a.pat.pi, kw = a.pat.k, M = a.pat.M, mlo = kw / pi + 1;
+    const int32_t pi = a.pat.pi, M = a.pat.M, mlo = a.pat.mlo;
     const int32_t res = rg * SW + wave;
     if (res >= pi || res >= n) return;                // no barriers in this kernel
     const int32_t pr = (n - 1 - res) / pi + 1;        // periods of this residue
@@ -263,6 +270,7 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_kernel(FwdArgs a, float* lse
         for (int r = 0; r < 4; ++r) {
             bool ok = (uint32_t)(e0 + r) <= sspan;
             if (BIDIR) ok = ok && (uint32_t)(h0 + r) > (uint32_t)(2 * mlo - 2);
+            if (a.pat.masked) ok = ok && in_schedule<BIDIR>(a.pat, stq, kp0 + r);
             sc[r] = ok ? s4[r] : -INFINITY;
         }
         const float mx = max4(fmax_ieee(fmax_ieee(sc[0], sc[1]), fmax_ieee(sc[2], sc[3]))) * sl2;
@@ -365,7 +373,7 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, x = lane & 15, g = lane >> 4;
-    const int32_t pi = a.pat.pi, kw = a.pat.k, M = a.pat.M, mlo = kw / pi + 1;
+    const int32_t pi = a.pat.pi, M = a.pat.M, mlo = a.pat.mlo;
     const int32_t res = rg * SW + wave;
     if (res >= pi || res >= n) return;                  // no barriers in this kernel
     const int32_t pr = (n - 1 - res) / pi + 1;
@@ -474,6 +482,7 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
             for (int r = 0; r < 4; ++r) {
                 bool ok = (uint32_t)(e0 + r) <= sspan;
                 if (BIDIR) ok = ok && (uint32_t)(h0 + r) > (uint32_t)(2 * mlo - 2);
+                if (a.pat.masked) ok = ok && in_schedule<BIDIR>(a.pat, tq, kp0 + r);
                 sc[i][r] = ok ? s4[r] : -INFINITY;
             }
             mxl = fmax_ieee(mxl, fmax_ieee(fmax_ieee(sc[i][0], sc[i][1]), fmax_ieee(sc[i][2], sc[i][3])));
@@ -571,7 +580,7 @@ __global__ __launch_bounds__(WinShape<D>::WW * 64, WinShape<D>::EU) void fwd_win
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63, x = lane & 15, g = lane >> 4;
-    const int32_t pi = a.pat.pi, kw = a.pat.k, M = a.pat.M, mlo = kw / pi + 1;
+    const int32_t pi = a.pat.pi, kw = a.pat.k, M = a.pat.M, mlo = a.pat.mlo;
 
     const int64_t bq = a.cu ? 0 : (int64_t)b;
     const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + bq * a.sq.s + h * a.sq.h + tok0 * a.sq.t;
@@ -823,8 +832,7 @@ __global__ __launch_bounds__(WinShape<D>::WW * 64, WinShape<D>::EU) void fwd_win
 // null when the pattern has no skip keys.
 template <int D, bool BIDIR>
 hipError_t launch_t(const FwdArgs& a, float* lse_s, hipStream_t stream) {
-    const int32_t mlo = a.pat.k / a.pat.pi + 1;
-    const bool skips = a.pat.M >= mlo;
+    const bool skips = a.pat.M >= a.pat.mlo;
     if (skips) {
         if (!lse_s) return hipErrorInvalidValue;
         const int32_t rgroups = (imin32(a.pat.pi, a.n) + SW - 1) / SW;

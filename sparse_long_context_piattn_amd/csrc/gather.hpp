@@ -74,7 +74,7 @@ template <typename T, int D>
 __device__ __forceinline__ void gather_row(const T* __restrict__ qrow, const T* __restrict__ kbase,
                                            const T* __restrict__ vbase, int64_t k_tok_stride,
                                            int64_t v_tok_stride,
-                                           const RowSpan& sp, int32_t i, int32_t pi, int32_t u0,
+                                           const RowSpan& sp, int32_t i, const PiPattern& pat, int32_t u0,
                                            int32_t u1, float pl, float ps, float scale_log2,
                                            RowPartial& st, int32_t ring = 0) {
     using G = GatherShape<D>;
@@ -98,7 +98,7 @@ __device__ __forceinline__ void gather_row(const T* __restrict__ qrow, const T* 
         float prior = 0.0f;
         if (valid) {
             bool loc;
-            int32_t key = span_key(sp, i, pi, u, &loc);
+            int32_t key = span_key(sp, i, pat, u, &loc);
             if (ring > 0) {                               // key >= i - ring + 1: row (i - delta) mod ring
                 const int32_t r = ri - (i - key);
                 key = r < 0 ? r + ring : r;

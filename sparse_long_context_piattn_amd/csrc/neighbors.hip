@@ -19,7 +19,7 @@ __global__ __launch_bounds__(256) void neighbors_kernel(int32_t n, PiPattern p, 
     for (int32_t u = 0; u < cap; ++u) {
         if (u < tot) {
             bool loc;
-            ir[u] = span_key(sp, i, p.pi, u, &loc);
+            ir[u] = span_key(sp, i, p, u, &loc);
             kr[u] = loc ? 1 : 2;
         } else {
             ir[u] = -1;

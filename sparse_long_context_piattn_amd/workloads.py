@@ -6,7 +6,8 @@ fed from it.  Every tensor is drawn from a seeded ``torch.Generator``.
 
 The five workloads are the shapes the pi-Attention write-ups motivate: a tiny
 fp32 case, an 8K-token causal prefill, a 128K-token causal prefill, a 32K-cache
-decode batch and a bidirectional variable-length encoder batch.  The pages'
+decode batch and a bidirectional variable-length encoder batch; a sixth is the
+8K prefill under a hierarchical skip schedule.  The pages'
 own evaluation data (WikiText-103, PG-19, LRA, MSCOCO, Flickr30K) is not used:
 these synthetic tensors stand in for it.
 """
@@ -37,6 +38,7 @@ class Workload:
     qkv_std: float = 1.0
     g_std: float = 1.0
     seed: int = 0
+    levels: tuple = ()   # extra skip levels (pi_r, M_r) of a skip schedule
     extra: dict = field(default_factory=dict)
 
     @property
@@ -59,6 +61,11 @@ WORKLOADS = {
                            pi=512, M=63, seed=1004),
     "bidir_varlen": Workload("bidir_varlen", "fwd", "bf16", H=16, d=64, k=32, pi=64, M=32,
                              bidir=True, nseq=8, len_lo=4096, len_hi=32768, seed=1005),
+    # prefill_8k with a hierarchical (doubling-period) skip schedule: the
+    # skips of (128, 16), (256, 16) and (512, 16) unioned -- 32 distinct
+    # distances, multiples 1..16, 18..32 step 2 and 36..64 step 4 of 128
+    "prefill_8k_sched": Workload("prefill_8k_sched", "fwd", "bf16", B=4, H=16, n=8192, d=64, k=64,
+                                 pi=128, M=16, levels=((256, 16), (512, 16)), seed=1006),
 }
 
 

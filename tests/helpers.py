@@ -45,7 +45,7 @@ def oracle_dense_fwd(x, w, rows=None, want_lse=False, bidir=None):
     gg = g.detach().cpu().permute(0, 2, 1).reshape(B * n, H).double().numpy()
     res = oracle.fwd(packed(q), packed(k), packed(v), gg, np.arange(B + 1) * n, w.k, w.pi, w.M,
                      w.bidir if bidir is None else bidir, w.scale, rows=rows,
-                     want_lse=want_lse)
+                     want_lse=want_lse, levels=w.levels)
     if rows is not None:
         return res
     if want_lse:

@@ -252,3 +252,25 @@ def test_bwd_rejects_bad_arguments(kw, expect):
     rc, msg = _bwd(**kw)
     assert rc == expect, msg
     assert msg
+
+
+def test_schedule_caps_and_validation():
+    L = pa.lib()
+    cap = lambda **kw: L.piattn_neighbors_cap(ctypes.byref(pa.make_pattern(**kw)))
+    # distances {4, 8, 12, 16, 32}: gcd 4, multiples {1, 2, 3, 4, 8} (not contiguous)
+    assert cap(k=3, pi=8, M=2, levels=[(4, 3), (16, 2)]) == 4 + 5
+    assert cap(k=3, pi=8, M=2, bidir=True, levels=[(4, 3), (16, 2)]) == 7 + 10
+    # distances {8, 16}: multiples {1, 2} of 8, the single-period pattern (8, 2)
+    assert cap(k=3, pi=8, M=2, levels=[(16, 1)]) == cap(k=3, pi=8, M=2)
+    # levels with M = 0 add nothing
+    assert cap(k=3, pi=8, M=2, levels=[(5, 0)]) == cap(k=3, pi=8, M=2)
+    p = pa.make_pattern(3, 8, 2, levels=[(4, 3)])
+    p.num_levels = 8
+    assert L.piattn_neighbors_cap(ctypes.byref(p)) == -1
+    for bad in ([(0, 3)], [(4, -1)]):
+        assert cap(k=3, pi=8, M=2, levels=bad) == -1
+    # gcd 1 with distances up to 200: beyond 127 multiples -> EUNSUPPORTED
+    rc, msg = _fwd(pat=pa.make_pattern(3, 5, 4, levels=[(2, 100)]))
+    assert rc == EUNSUPPORTED and "gcd" in msg, msg
+    # the same levels with the far multiples inside the window are fine
+    assert cap(k=300, pi=5, M=4, levels=[(2, 100)]) == 301
