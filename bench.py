@@ -272,6 +272,94 @@ def bench_backward(args, w, dev, sets, outs, lengths, rows):
     print(json.dumps(res), flush=True)
 
 
+def bench_layer(args, w, dev):
+    """gate logits -> attention -> output projection on the workload's shape
+    (dense bf16 workloads; model width Dm = H d, random weights).  One step
+    runs the three calls; each stage is also timed alone with HIP events on
+    the launch stream.  The roofline is the output projection's (a GEMM on
+    bf16 MFMA: 2 M Dm Dm flops)."""
+    import torch
+
+    import sparse_long_context_piattn_amd as pa
+    from sparse_long_context_piattn_amd import workloads as wl
+
+    if w.nseq or w.kind != "fwd" or w.dtype != "bf16":
+        raise SystemExit("--layer takes a dense bf16 prefill workload")
+    B, H, n, d = w.B, w.H, w.n, w.d
+    Dm = H * d
+    gen = torch.Generator(device=dev).manual_seed(w.seed)
+    rnd = lambda shape, std: (torch.randn(shape, generator=gen, device=dev) * std).to(torch.bfloat16)
+    xs = wl.make_fwd_inputs(w, device=dev)
+    x = rnd((B, n, Dm), 1.0)
+    wg = rnd((H, Dm), Dm ** -0.5)
+    wo = rnd((Dm, Dm), Dm ** -0.5)
+    g = torch.empty((B, H, n), dtype=torch.float32, device=dev)
+    o = torch.empty_like(xs["q"])
+    y = torch.empty((B, n, Dm), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(max(1, pa.fwd_workspace_bytes(1, B, H, n, d, pa.make_pattern(w.k, w.pi, w.M, w.bidir, 0.0,
+                                                                                 w.levels))),
+                     dtype=torch.uint8, device=dev)
+    stages = {
+        "gate": lambda: pa.gate_logits(x, wg, out=g),
+        "attention": lambda: pa.fwd(xs["q"], xs["k"], xs["v"], g, window_k=w.k, period_pi=w.pi, num_skips=w.M,
+                                    levels=w.levels, bidirectional=w.bidir, out=o, workspace=ws),
+        "out_proj": lambda: pa.out_proj(o, wo, out=y),
+    }
+
+    def step(_):
+        for f in stages.values():
+            f()
+
+    ms_per_step = timed(step, args, dev)
+    stream = torch.cuda.current_stream(dev)
+    per = {}
+    for name, f in stages.items():
+        for _ in range(20):
+            f()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 100
+        e0.record(stream)
+        for _ in range(reps):
+            f()
+        e1.record(stream)
+        torch.cuda.synchronize(dev)
+        per[name] = e0.elapsed_time(e1) / reps
+    # the same GEMM in torch's library path, for context (o token-major and
+    # contiguous there: the head concatenation is a copy in that path)
+    ocat = o.permute(0, 2, 1, 3).reshape(B * n, Dm).contiguous()
+    lib_gemm = lambda: torch.nn.functional.linear(ocat, wo)
+    for _ in range(20):
+        lib_gemm()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(100):
+        lib_gemm()
+    e1.record(stream)
+    torch.cuda.synchronize(dev)
+    lib_ms = e0.elapsed_time(e1) / 100
+    M = B * n
+    flops = 2.0 * M * Dm * Dm
+    tflops = flops / (per["out_proj"] / 1e3) / 1e12
+    gate_bytes = M * Dm * 2 + M * H * 4
+    log("layer: %.4f ms/step  gate %.4f ms (%.0f GB/s)  attention %.4f ms  out_proj %.4f ms (%.0f TFLOP/s, "
+        "%.1f%% of bf16 MFMA peak); torch linear on a contiguous copy %.4f ms"
+        % (ms_per_step, per["gate"], gate_bytes / (per["gate"] / 1e3) / 1e9, per["attention"], per["out_proj"],
+           tflops, 100 * tflops / BF16_MFMA_PEAK_TFLOPS, lib_ms))
+    res = {"metric": "pi-attn layer (gate + attention + output projection) tokens/s, 1 GPU",
+           "value": round(M / (ms_per_step / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+           "data": "synthetic (seeded N(0,1) x, q/k/v; random-init gate and projection weights)",
+           "config": {"workload": w.name, "pass": "layer", "B": B, "H": H, "n": n, "d": d, "Dm": Dm, "k": w.k,
+                      "pi": w.pi, "M": w.M, "bidirectional": w.bidir},
+           "stages_ms": {k_: round(v_, 5) for k_, v_ in per.items()},
+           "torch_linear_ms": round(lib_ms, 5),
+           "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None},
+           "cpu_baseline": None}
+    print(json.dumps(res), flush=True)
+
+
 COPY_ELEMS = 256 << 20          # bf16 elements of the calibration copy (512 MiB each way)
 
 
@@ -370,6 +458,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--sets", type=int, default=0, help="input sets rotated (0 = auto)")
     ap.add_argument("--splits", type=int, default=0, help="decode key-range splits (0 = auto)")
+    ap.add_argument("--layer", action="store_true",
+                    help="time gate logits + attention + output projection (dense bf16 prefill workloads)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (piattn_bwd) instead of the forward (prefill workloads)")
     ap.add_argument("--rolling", action="store_true",
@@ -401,6 +491,8 @@ def main():
     w = wl.WORKLOADS[args.workload]
     if w.kind == "decode":
         return bench_decode(args, w, dev)
+    if args.layer:
+        return bench_layer(args, w, dev)
     lengths = wl.varlen_lengths(w) if w.nseq else None
     alg_bytes, alg_flops, rows, loc, sk = algorithmic(w, lengths)
     set_bytes = alg_bytes

@@ -180,6 +180,49 @@ int piattn_bwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d,
 size_t piattn_bwd_workspace_bytes(int32_t B, int32_t H, int32_t n);
 
 /*
+ * The linear maps around the attention.  The pages give the gate as a
+ * learnable shallow MLP of the input (gist.science section 2 "Methodology",
+ * item "Dynamic Adaptive Fusion") and end with a fusion-and-projection
+ * stage (section 2 "Execution & Scheduling", "Streaming Stages"); the
+ * plainest form is taken: one linear layer per head for the gate logit and
+ * the usual output projection of the concatenated heads.
+ *
+ * piattn_gate_logits -- g[b, h, i] = <x[b, i, :], w[h, :]> + bias[h], fp32,
+ * written in the prefill's gate layout.
+ *   x [B, n, Dm]     element (b, i, c) at x + b*x_strides[0] + i*x_strides[1] + c
+ *   w [H, Dm]        row-major, contiguous
+ *   bias [H]         fp32, or NULL
+ *   g                element (b, h, i) at g + b*s[0] + h*s[1] + i*s[2], s = g_strides
+ * PIATTN_BF16 (x, w) runs on MFMA and needs Dm % 32 == 0, H <= 32, x and w
+ * 16-byte aligned with strides multiples of 8 (else EUNSUPPORTED / EINVAL);
+ * PIATTN_F32 runs a plain kernel.  Returns PIATTN_OK, EINVAL, EUNSUPPORTED
+ * or EHIP.
+ */
+int piattn_gate_logits(piattn_dtype dtype, int32_t B, int32_t n, int32_t Dm, int32_t H,
+                       const void *x, const int64_t x_strides[2], const void *w,
+                       const float *bias, float *g, const int64_t g_strides[3],
+                       void *stream);
+
+/*
+ * piattn_out_proj -- y[b, i, :] = sum_{h, c} o[b, h, i, c] w[:, h*d + c] + bias,
+ * the output projection of the concatenated heads, read straight from the
+ * attention's output layout (no copy).
+ *   o [B, H, n, d]   element (b, h, i, c) at o + b*s[0] + h*s[1] + i*s[2] + c, s = o_strides
+ *   w [Dout, H*d]    row r at w + r*ldw (ldw >= H*d), contiguous columns
+ *   bias [Dout]      fp32, or NULL
+ *   y [B, n, Dout]   element (b, i, c) at y + b*y_strides[0] + i*y_strides[1] + c
+ * Element type of o, w, y: dtype.  PIATTN_BF16 with d % 32 == 0 runs an MFMA
+ * GEMM (fp32 accumulation, bf16 round-to-nearest-even store); other shapes
+ * and PIATTN_F32 a plain kernel.  bf16 needs 16-byte alignment and strides
+ * (and ldw) that are multiples of 8 elements.  y must not alias o or w.
+ * Returns PIATTN_OK, EINVAL or EHIP.
+ */
+int piattn_out_proj(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d,
+                    const void *o, const int64_t o_strides[3], int32_t Dout, const void *w,
+                    int64_t ldw, const float *bias, void *y, const int64_t y_strides[2],
+                    void *stream);
+
+/*
  * piattn_decode -- one new query per sequence against its KV cache (the
  * pages' inference mode, gist.science section 2 "Execution & Scheduling",
  * item "Inference").  The query of sequence s sits at position

@@ -5,9 +5,9 @@ include/piattn.h); this package is its thin Python binding plus the seeded
 synthetic workloads used by the tests and the benchmark.
 """
 from .binding import (Pattern, PiattnError, bwd, cache_append, decode, decode_workspace_bytes, fwd,
-                      fwd_workspace_bytes, lib, make_pattern, neighbors, neighbors_cap,
-                      rolling_slots, version)
+                      fwd_workspace_bytes, gate_logits, lib, make_pattern, neighbors, neighbors_cap,
+                      out_proj, rolling_slots, version)
 
 __all__ = ["Pattern", "PiattnError", "bwd", "cache_append", "decode", "decode_workspace_bytes", "fwd",
-           "fwd_workspace_bytes", "lib", "make_pattern", "neighbors", "neighbors_cap",
-           "rolling_slots", "version"]
+           "fwd_workspace_bytes", "gate_logits", "lib", "make_pattern", "neighbors", "neighbors_cap",
+           "out_proj", "rolling_slots", "version"]

@@ -22,6 +22,7 @@ STATUS = {0: "PIATTN_OK", 1: "PIATTN_EINVAL", 2: "PIATTN_EUNSUPPORTED", 3: "PIAT
           4: "PIATTN_EHIP"}
 
 EXPORTS = ["piattn_fwd", "piattn_fwd_workspace_bytes", "piattn_bwd", "piattn_bwd_workspace_bytes",
+           "piattn_gate_logits", "piattn_out_proj",
            "piattn_decode", "piattn_decode_workspace_bytes",
            "piattn_decode_auto_splits", "piattn_rolling_slots", "piattn_cache_append",
            "piattn_decode_rolling", "piattn_neighbors", "piattn_neighbors_cap",
@@ -87,6 +88,12 @@ def lib():
         L.piattn_cache_append.restype = ctypes.c_int
         L.piattn_neighbors.argtypes = [i32, pat, i32, i32, i32, vp, vp, vp, vp]
         L.piattn_neighbors.restype = ctypes.c_int
+        L.piattn_gate_logits.argtypes = [ctypes.c_int, i32, i32, i32, i32, vp, ctypes.POINTER(ctypes.c_int64 * 2),
+                                         vp, vp, vp, ctypes.POINTER(ctypes.c_int64 * 3), vp]
+        L.piattn_gate_logits.restype = ctypes.c_int
+        L.piattn_out_proj.argtypes = [ctypes.c_int, i32, i32, i32, i32, vp, ctypes.POINTER(ctypes.c_int64 * 3), i32,
+                                      vp, ctypes.c_int64, vp, vp, ctypes.POINTER(ctypes.c_int64 * 2), vp]
+        L.piattn_out_proj.restype = ctypes.c_int
         L.piattn_neighbors_cap.argtypes = [pat]
         L.piattn_neighbors_cap.restype = i32
         L.piattn_last_error.argtypes = []
@@ -265,6 +272,74 @@ def bwd(q, k, v, g, out, dout, *, window_k: int, period_pi: int, num_skips: int,
                           ctypes.byref(pat), _ptr(workspace), wbytes, ctypes.c_void_p(_stream(q.device)))
     _check(rc)
     return dq, dk, dv, dg
+
+
+def gate_logits(x, w, bias=None, *, out=None):
+    """Gate logits g = x w^T + bias of a linear gate per head.
+
+    x [B, n, Dm] (last dim contiguous) or packed [T, Dm]; w [H, Dm]
+    contiguous; bias [H] fp32 or None.  Returns g fp32 [B, H, n] (packed:
+    [T, H]), the prefill's gate layout, or writes into out of that shape."""
+    code = _dtype_code(x)
+    _need_cuda(x, w, bias, out)
+    if w.dtype != x.dtype or w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous [H, Dm] tensor of x's dtype")
+    if bias is not None and (bias.dtype != torch.float32 or bias.shape != (w.shape[0],)):
+        raise ValueError("bias must be float32 [H]")
+    packed_in = x.dim() == 2
+    x3 = x.unsqueeze(0) if packed_in else x
+    if x3.dim() != 3 or x3.stride(-1) != 1:
+        raise ValueError("x must be [B, n, Dm] or [T, Dm] with a contiguous last dim")
+    B, n, Dm = x3.shape
+    H = w.shape[0]
+    if w.shape[1] != Dm:
+        raise ValueError("w is [H, %d], x has Dm=%d" % (w.shape[1], Dm))
+    if out is None:
+        out = torch.empty((n, H) if packed_in else (B, H, n), dtype=torch.float32, device=x.device)
+    gs = (0, out.stride(1), out.stride(0)) if packed_in else tuple(out.stride())
+    xs = (ctypes.c_int64 * 2)(x3.stride(0), x3.stride(1))
+    gst = (ctypes.c_int64 * 3)(*gs)
+    rc = lib().piattn_gate_logits(code, B, n, Dm, H, _ptr(x3), ctypes.byref(xs), _ptr(w), _ptr(bias), _ptr(out),
+                                  ctypes.byref(gst), ctypes.c_void_p(_stream(x.device)))
+    _check(rc)
+    return out
+
+
+def out_proj(o, w, bias=None, *, out=None):
+    """Output projection y = concat_h(o) w^T + bias, read from the attention's
+    output layout.  o [B, H, n, d] (any strides, last dim contiguous) or
+    packed [T, H, d]; w [Dout, H*d] (last dim contiguous); bias [Dout] fp32
+    or None.  Returns y [B, n, Dout] (packed: [T, Dout]) of o's dtype."""
+    code = _dtype_code(o)
+    _need_cuda(o, w, bias, out)
+    if w.dtype != o.dtype or w.dim() != 2 or w.stride(-1) != 1:
+        raise ValueError("w must be a [Dout, H*d] tensor of o's dtype with a contiguous last dim")
+    packed_in = o.dim() == 3
+    if packed_in:
+        T, H, d = o.shape
+        B, n = 1, T
+        ost = (0, o.stride(1), o.stride(0))
+    else:
+        B, H, n, d = o.shape
+        ost = tuple(o.stride()[:3])
+    if o.stride(-1) != 1:
+        raise ValueError("the head dimension of o must be contiguous")
+    Dout = w.shape[0]
+    if w.shape[1] != H * d:
+        raise ValueError("w is [Dout, %d], o has H*d=%d" % (w.shape[1], H * d))
+    if bias is not None and (bias.dtype != torch.float32 or bias.shape != (Dout,)):
+        raise ValueError("bias must be float32 [Dout]")
+    if out is None:
+        out = torch.empty((n, Dout) if packed_in else (B, n, Dout), dtype=o.dtype, device=o.device)
+    if out.stride(-1) != 1:
+        raise ValueError("out must have a contiguous last dim")
+    ys = (0, out.stride(0)) if packed_in else (out.stride(0), out.stride(1))
+    os_ = (ctypes.c_int64 * 3)(*ost)
+    yst = (ctypes.c_int64 * 2)(*ys)
+    rc = lib().piattn_out_proj(code, B, H, n, d, _ptr(o), ctypes.byref(os_), Dout, _ptr(w), w.stride(0),
+                               _ptr(bias), _ptr(out), ctypes.byref(yst), ctypes.c_void_p(_stream(o.device)))
+    _check(rc)
+    return out
 
 
 def decode_workspace_bytes(S, H, d, num_splits, pattern: Pattern) -> int:

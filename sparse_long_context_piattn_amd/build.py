@@ -20,7 +20,8 @@ LIB = os.path.join(PKG, "libpiattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "neighbors.hip", "fwd_gather.hip", "fwd_resid.hip",
-           "fwd_split.hip", "decode.hip", "bwd.hip", "bwd_band.hip"]
+           "fwd_split.hip", "decode.hip", "bwd.hip", "bwd_band.hip",
+           "proj.hip"]
 
 # Packed-fp32 VALU forms are kept out of the device code (plain fp32 only).
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -372,6 +372,87 @@ int piattn_bwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
     return launch_status(band_ok ? launch_bwd_band(ba, st) : launch_bwd(dt, ba, st));
 }
 
+int piattn_gate_logits(piattn_dtype dtype, int32_t B, int32_t n, int32_t Dm, int32_t H, const void* x,
+                       const int64_t x_strides[2], const void* w, const float* bias, float* g,
+                       const int64_t g_strides[3], void* stream) {
+    if (dtype != PIATTN_F32 && dtype != PIATTN_BF16)
+        return fail(PIATTN_EINVAL, "dtype=%d is not PIATTN_F32 or PIATTN_BF16", (int)dtype);
+    if (B < 1 || n < 1 || Dm < 1 || H < 1)
+        return fail(PIATTN_EINVAL, "B=%d n=%d Dm=%d H=%d must all be >= 1", B, n, Dm, H);
+    if (!x || !w || !g || !x_strides || !g_strides) return fail(PIATTN_EINVAL, "a pointer argument is NULL");
+    const int64_t mult = dtype == PIATTN_BF16 ? 8 : 1;
+    if (x_strides[0] < 0 || x_strides[1] < 0 || x_strides[0] % mult || x_strides[1] % mult)
+        return fail(PIATTN_EINVAL, "x strides must be non-negative multiples of %lld elements", (long long)mult);
+    for (int j = 0; j < 3; ++j)
+        if (g_strides[j] < 0) return fail(PIATTN_EINVAL, "g stride[%d] is negative", j);
+    if (dtype == PIATTN_BF16) {
+        if (!aligned(x, 16) || !aligned(w, 16)) return fail(PIATTN_EINVAL, "x and w must be 16-byte aligned");
+        if (Dm % 32) return fail(PIATTN_EUNSUPPORTED, "bf16 gate: Dm=%d must be a multiple of 32", Dm);
+        if (H > 32) return fail(PIATTN_EUNSUPPORTED, "bf16 gate: H=%d above 32", H);
+    } else if (!aligned(x, 4) || !aligned(w, 4)) {
+        return fail(PIATTN_EINVAL, "x and w must be 4-byte aligned");
+    }
+    if (!aligned(g, 4) || (bias && !aligned(bias, 4))) return fail(PIATTN_EINVAL, "g and bias must be 4-byte aligned");
+    if (static_cast<const void*>(g) == x || static_cast<const void*>(g) == w)
+        return fail(PIATTN_EINVAL, "g aliases an input");
+    GateArgs a;
+    a.x = x;
+    a.sx_b = x_strides[0];
+    a.sx_t = x_strides[1];
+    a.w = w;
+    a.bias = bias;
+    a.g = g;
+    a.sg_b = g_strides[0];
+    a.sg_h = g_strides[1];
+    a.sg_t = g_strides[2];
+    a.B = B;
+    a.n = n;
+    a.H = H;
+    a.Dm = Dm;
+    return launch_status(launch_gate(dtype == PIATTN_BF16 ? 1 : 0, a, static_cast<hipStream_t>(stream)));
+}
+
+int piattn_out_proj(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, const void* o,
+                    const int64_t o_strides[3], int32_t Dout, const void* w, int64_t ldw, const float* bias,
+                    void* y, const int64_t y_strides[2], void* stream) {
+    if (dtype != PIATTN_F32 && dtype != PIATTN_BF16)
+        return fail(PIATTN_EINVAL, "dtype=%d is not PIATTN_F32 or PIATTN_BF16", (int)dtype);
+    if (B < 1 || H < 1 || n < 1 || d < 1 || Dout < 1)
+        return fail(PIATTN_EINVAL, "B=%d H=%d n=%d d=%d Dout=%d must all be >= 1", B, H, n, d, Dout);
+    if (!o || !w || !y || !o_strides || !y_strides) return fail(PIATTN_EINVAL, "a pointer argument is NULL");
+    const int64_t mult = dtype == PIATTN_BF16 ? 8 : 1;
+    for (int j = 0; j < 3; ++j)
+        if (o_strides[j] < 0 || o_strides[j] % mult)
+            return fail(PIATTN_EINVAL, "o stride[%d] must be a non-negative multiple of %lld", j, (long long)mult);
+    for (int j = 0; j < 2; ++j)
+        if (y_strides[j] < 0 || y_strides[j] % mult)
+            return fail(PIATTN_EINVAL, "y stride[%d] must be a non-negative multiple of %lld", j, (long long)mult);
+    if (ldw < (int64_t)H * d || ldw % mult)
+        return fail(PIATTN_EINVAL, "ldw=%lld must be >= H*d and a multiple of %lld", (long long)ldw, (long long)mult);
+    const size_t al = dtype == PIATTN_BF16 ? 16 : 4;
+    if (!aligned(o, al) || !aligned(w, al) || !aligned(y, al))
+        return fail(PIATTN_EINVAL, "o, w and y must be %zu-byte aligned", al);
+    if (bias && !aligned(bias, 4)) return fail(PIATTN_EINVAL, "bias must be 4-byte aligned");
+    if (y == o || y == w) return fail(PIATTN_EINVAL, "y aliases an input");
+    ProjArgs a;
+    a.o = o;
+    a.so_b = o_strides[0];
+    a.so_h = o_strides[1];
+    a.so_t = o_strides[2];
+    a.w = w;
+    a.ldw = ldw;
+    a.bias = bias;
+    a.y = y;
+    a.sy_b = y_strides[0];
+    a.sy_t = y_strides[1];
+    a.B = B;
+    a.n = n;
+    a.H = H;
+    a.d = d;
+    a.Dout = Dout;
+    return launch_status(launch_out_proj(dtype == PIATTN_BF16 ? 1 : 0, a, static_cast<hipStream_t>(stream)));
+}
+
 size_t piattn_decode_workspace_bytes(int32_t S, int32_t H, int32_t d, int32_t num_splits,
                                      const piattn_pattern* pattern) {
     if (S < 1 || H < 1 || d < 1 || num_splits < 0 || num_splits > 64) return 0;

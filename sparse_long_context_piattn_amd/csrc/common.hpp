@@ -44,6 +44,30 @@ struct BwdArgs {
     float scale;         // logit scale (natural units)
 };
 
+// Gate logits g[b, h, i] = <x[b, i, :], w[h, :]> + bias[h] (strides in elements;
+// the last dim of x contiguous, w row-major [H][Dm]).
+struct GateArgs {
+    const void* x;
+    int64_t sx_b, sx_t;
+    const void* w;
+    const float* bias;   // [H] or null
+    float* g;
+    int64_t sg_b, sg_h, sg_t;
+    int32_t B, n, H, Dm;
+};
+
+// Output projection y[b, i, :] = sum_{h,c} o[b, h, i, c] w[:, h d + c] + bias.
+struct ProjArgs {
+    const void* o;
+    int64_t so_b, so_h, so_t;
+    const void* w;       // [Dout] rows of ldw elements, columns h d + c
+    int64_t ldw;
+    const float* bias;   // [Dout] or null
+    void* y;
+    int64_t sy_b, sy_t;
+    int32_t B, n, H, d, Dout;
+};
+
 // Appends one token's key and value per (sequence, head) to a rolling cache.
 struct AppendArgs {
     const void* kn;

@@ -25,6 +25,10 @@ hipError_t launch_bwd(int dtype, const BwdArgs& a, hipStream_t stream);
 // pass in residue layout, then the window pass.
 bool bwd_band_supported(int dtype, const BwdArgs& a);
 hipError_t launch_bwd_band(const BwdArgs& a, hipStream_t stream);
+// Gate logits and output projection around the attention (bf16 on MFMA).
+hipError_t launch_gate(int dtype, const GateArgs& a, hipStream_t stream);
+bool out_proj_mfma_ok(int dtype, const ProjArgs& a);
+hipError_t launch_out_proj(int dtype, const ProjArgs& a, hipStream_t stream);
 hipError_t launch_neighbors(int32_t n, const PiPattern& p, int32_t q_begin, int32_t q_count,
                             int32_t cap, int32_t* idx, int8_t* kind, int32_t* count,
                             hipStream_t stream);

@@ -1,0 +1,297 @@
+// proj.hip -- the linear maps around pi-Attention (gfx950): the gate logits
+// in front of the kernel and the output projection behind it.
+//
+// The pages give the gate as a learnable shallow MLP that sets alpha from
+// the input (gist.science section 2 "Methodology", item "Dynamic Adaptive
+// Fusion") and end the pipeline with a fusion-and-projection stage (section
+// 2 "Execution & Scheduling", "Streaming Stages").  The plainest form is
+// taken: one linear layer per head for the gate logit, and the usual output
+// projection of the concatenated heads.
+//
+//   gate:      g[b, h, i] = <x[b, i, :], Wg[h, :]> + bg[h]        (fp32 out)
+//   out-proj:  y[b, i, :] = sum_{h, c} o[b, h, i, c] Wo[:, h d + c] + bo
+//
+// bf16 runs on v_mfma_f32_16x16x32_bf16.  The gate is a skinny contraction
+// (N = H heads, K = Dm) bound by reading x once: each wave takes 16 tokens,
+// its A operand straight from the x rows, its B operand (the gate weights)
+// from L2.  The output projection is a GEMM over M = tokens, N = Dout,
+// K = H d with the head concatenation folded into the A operand's addresses
+// (o stays in the attention's [B, H, n, d] layout, any strides): 128 x 128
+// tiles, K in chunks of 32 (always inside one head), a ring of three LDS
+// slots filled two stages ahead by LDS-direct loads, XOR-swizzled rows so
+// that the MFMA operand reads are free of bank conflicts, and an epilogue
+// that turns the accumulators into whole bf16 rows through LDS.  fp32 inputs
+// take plain per-element kernels.
+#include "kernels.hpp"
+#include "mfma_util.hpp"
+
+namespace {
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ void store_as(float* p, float v) { *p = v; }
+__device__ __forceinline__ void store_as(uint16_t* p, float v) { *p = (uint16_t)(cvt_pk_bf16(v, 0.0f) & 0xffffu); }
+
+// ------------------------------------------------------------------ gate (bf16)
+// One wave per 16 tokens, NB = ceil(H / 16) column blocks of heads.
+template <int NB>
+__global__ __launch_bounds__(256) void gate_mfma_kernel(GateArgs a) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
+    const int64_t t0 = ((int64_t)blockIdx.x * 4 + wave) * 16;   // first token of the wave (flat b * n + i)
+    const int64_t T = (int64_t)a.B * a.n;
+    if (t0 >= T) return;
+    const int64_t tl = t0 + x < T ? t0 + x : T - 1;                // the lane's A row (clamped)
+    const int64_t bl = tl / a.n, il = tl % a.n;
+    const uint16_t* xr = static_cast<const uint16_t*>(a.x) + bl * a.sx_b + il * a.sx_t;
+    const uint16_t* wr[NB];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb)
+        wr[cb] = static_cast<const uint16_t*>(a.w) + (int64_t)imin32(16 * cb + x, a.H - 1) * a.Dm;
+    f32x4_t acc[NB];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // four k-chunks of 32 per step: 4 independent A loads and 4 NB B loads in flight
+    int32_t k0 = 0;
+    for (; k0 + 128 <= a.Dm; k0 += 128) {
+        bf16x8_t av[4], bv[4][NB];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            av[u] = *reinterpret_cast<const bf16x8_t*>(xr + k0 + 32 * u + 8 * g);
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+                bv[u][cb] = *reinterpret_cast<const bf16x8_t*>(wr[cb] + k0 + 32 * u + 8 * g);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][cb], acc[cb], 0, 0, 0);
+    }
+    for (; k0 < a.Dm; k0 += 32) {                                  // Dm % 128 chunks of 32
+        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xr + k0 + 8 * g);
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+            const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(wr[cb] + k0 + 8 * g);
+            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[cb], 0, 0, 0);
+        }
+    }
+    // lane (x, g) holds tokens t0 + 4g + r of head 16 cb + x
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        const int32_t h = 16 * cb + x;
+        if (h >= a.H) continue;
+        const float bias = a.bias ? a.bias[h] : 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int64_t t = t0 + 4 * g + r;
+            if (t >= T) continue;
+            const int64_t b = t / a.n, i = t % a.n;
+            a.g[b * a.sg_b + h * a.sg_h + i * a.sg_t] = acc[cb][r] + bias;
+        }
+    }
+}
+
+// ------------------------------------------------------------------ gate (fp32)
+__global__ __launch_bounds__(256) void gate_f32_kernel(GateArgs a) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;     // (token, head)
+    const int64_t T = (int64_t)a.B * a.n;
+    if (e >= T * a.H) return;
+    const int64_t t = e / a.H;
+    const int32_t h = (int32_t)(e % a.H);
+    const int64_t b = t / a.n, i = t % a.n;
+    const float* xr = static_cast<const float*>(a.x) + b * a.sx_b + i * a.sx_t;
+    const float* wr = static_cast<const float*>(a.w) + (int64_t)h * a.Dm;
+    float s = 0.0f;
+    for (int32_t k = 0; k < a.Dm; ++k) s = fmaf(xr[k], wr[k], s);
+    a.g[b * a.sg_b + h * a.sg_h + i * a.sg_t] = s + (a.bias ? a.bias[h] : 0.0f);
+}
+
+// ------------------------------------------------------------ output projection
+constexpr int PM = 128, PN = 128, PK = 32;   // tile rows (tokens), columns (outputs), k-chunk
+constexpr int PSLOT = (PM + PN) * PK;        // elements of one ring slot (A rows, then W rows)
+
+// Element offset of 16-byte chunk c (of 4) of row r in a [rows][32] bf16
+// tile, XOR-swizzled by (r / 2) % 4: the 16 rows x 4 chunks of an MFMA
+// operand read then fall on distinct banks.
+__device__ __forceinline__ int psw(int r, int c) { return r * PK + ((c ^ ((r >> 1) & 3)) << 3); }
+
+__global__ __launch_bounds__(256, 2) void out_proj_mfma_kernel(ProjArgs a, int32_t mtiles, int32_t total) {
+    __shared__ __attribute__((aligned(16))) uint16_t ring[3 * PSLOT];
+    const int32_t logical = xcd_logical(blockIdx.x, total);
+    const int32_t mt = logical % mtiles, nt = logical / mtiles;   // neighbouring tiles share W columns
+    const int64_t M = (int64_t)a.B * a.n;
+    const int64_t m0 = (int64_t)mt * PM;
+    const int32_t n0 = nt * PN;
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63, x = lane & 15, g = lane >> 4;
+    const int32_t K = a.H * a.d;
+    const int32_t nk = K / PK;
+
+    // ---- staging.  One 1 KB load covers 16 rows x 64 bytes; lane l fills
+    // row l / 4, physical chunk l % 4 = logical chunk (l % 4) ^ ((row / 2) % 4).
+    // Waves 0-1 load the A rows (tokens), waves 2-3 the W rows (outputs),
+    // 64 rows each: 4 loads per wave per stage.
+    const bool isw = wave >= 2;
+    const int rbase = (wave & 1) * 64;
+    uint32_t voff[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int rr = rbase + 16 * j + lane / 4;                 // tile row of this lane's 16 bytes
+        const int lc = (lane % 4) ^ ((rr >> 1) & 3);
+        if (!isw) {
+            int64_t t = m0 + rr;
+            t = t < M ? t : M - 1;
+            const int64_t b = t / a.n, i = t % a.n;
+            voff[j] = (uint32_t)((b * a.so_b + i * a.so_t + 8 * lc) * 2);
+        } else {
+            const int32_t nn = imin32(n0 + rr, a.Dout - 1);
+            voff[j] = (uint32_t)(((int64_t)nn * a.ldw + 8 * lc) * 2);
+        }
+    }
+    const uint16_t* obase = static_cast<const uint16_t*>(a.o);
+    const uint16_t* wbase = static_cast<const uint16_t*>(a.w);
+    auto issue = [&](int32_t s, uint16_t* slot) __attribute__((always_inline)) {
+        s = imin32(s, nk - 1);                                     // past the end: a harmless reload
+        const int32_t k0 = s * PK;
+        const int32_t h = k0 / a.d, c0 = k0 - h * a.d;
+        const uint16_t* src = isw ? wbase + k0 : obase + (int64_t)h * a.so_h + c0;
+        uint16_t* dst = slot + (isw ? PM * PK : 0) + rbase * PK;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) dma16(src, voff[j], lds_addr(dst + 16 * j * PK));
+    };
+
+    f32x4_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;        // the wave's 64 x 64 sub-tile
+
+    auto compute = [&](const uint16_t* slot) __attribute__((always_inline)) {
+        bf16x8_t av[4], bv[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            av[i] = *reinterpret_cast<const bf16x8_t*>(slot + psw(wm + 16 * i + x, g));
+            bv[i] = *reinterpret_cast<const bf16x8_t*>(slot + PM * PK + psw(wn + 16 * i + x, g));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+    };
+
+    issue(0, ring);
+    issue(1, ring + PSLOT);
+    // step s: this wave's stage-s loads landed (stage s+1 may be in flight),
+    // barrier (everyone's landed, stage s-1 fully read), issue stage s+2
+    // into the slot of stage s-1, compute stage s
+    for (int32_t s = 0; s < nk; ++s) {
+        const int cur = s % 3;
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(4));
+        lds_barrier();
+        issue(s + 2, ring + ((s + 2) % 3) * PSLOT);
+        compute(ring + cur * PSLOT);
+    }
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));                   // the trailing reloads land
+    lds_barrier();                                                 // every wave done with the ring
+
+    // ---- epilogue: bias, bf16, and whole rows through the wave's own 8 KB
+    // of the ring ([64 rows][64 columns], 16-byte chunks swizzled by row % 8)
+    uint16_t* tile = ring + wave * 64 * 64;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int32_t col = n0 + wn + 16 * j + x;
+        const float bias = (a.bias && col < a.Dout) ? a.bias[col] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rr = 16 * i + 4 * g + r, cc = 16 * j + x;
+                tile[rr * 64 + ((((cc >> 3) ^ (rr & 7)) << 3) | (cc & 7))] =
+                    (uint16_t)(cvt_pk_bf16(acc[i][j][r] + bias, 0.0f) & 0xffffu);
+            }
+    }
+    lds_barrier();
+    uint16_t* yb = static_cast<uint16_t*>(a.y);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int rr = 8 * j + lane / 8, ch = lane % 8;            // 8 rows x 8 chunks per instruction
+        const int64_t t = m0 + wm + rr;
+        const int32_t col = n0 + wn + 8 * ch;
+        if (t >= M || col >= a.Dout) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(tile + rr * 64 + ((ch ^ (rr & 7)) << 3));
+        const int64_t b = t / a.n, i = t % a.n;
+        uint16_t* dst = yb + b * a.sy_b + i * a.sy_t + col;
+        if (col + 8 <= a.Dout) {
+            *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+            const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
+            for (int q = 0; q < a.Dout - col; ++q) dst[q] = e[q];
+        }
+    }
+}
+
+// fp32 (and a fallback for any shape): one thread per output element.
+template <typename T>
+__global__ __launch_bounds__(256) void out_proj_plain_kernel(ProjArgs a) {
+    const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int64_t M = (int64_t)a.B * a.n;
+    if (e >= M * a.Dout) return;
+    const int64_t t = e / a.Dout;
+    const int32_t col = (int32_t)(e % a.Dout);
+    const int64_t b = t / a.n, i = t % a.n;
+    const T* ob = static_cast<const T*>(a.o) + b * a.so_b + i * a.so_t;
+    const T* wr = static_cast<const T*>(a.w) + (int64_t)col * a.ldw;
+    float s = 0.0f;
+    for (int32_t h = 0; h < a.H; ++h)
+        for (int32_t c = 0; c < a.d; ++c) s = fmaf(to_f32(ob[h * a.so_h + c]), to_f32(wr[h * a.d + c]), s);
+    s += a.bias ? a.bias[col] : 0.0f;
+    store_as(static_cast<T*>(a.y) + b * a.sy_b + i * a.sy_t + col, s);
+}
+
+}  // namespace
+
+hipError_t launch_gate(int dtype, const GateArgs& a, hipStream_t stream) {
+    const int64_t T = (int64_t)a.B * a.n;
+    if (dtype == 1) {
+        const int64_t blocks = (T + 63) / 64;
+        if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+        auto k = a.H <= 16 ? gate_mfma_kernel<1> : gate_mfma_kernel<2>;
+        hipLaunchKernelGGL(k, dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+    } else {
+        const int64_t blocks = (T * a.H + 255) / 256;
+        if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(gate_f32_kernel, dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+    }
+    return hipGetLastError();
+}
+
+bool out_proj_mfma_ok(int dtype, const ProjArgs& a) {
+    if (dtype != 1 || a.d % PK != 0) return false;
+    // 32-bit byte offsets of the LDS-direct loads: any row of o from its base
+    // plus a head's columns, any row of W
+    const int64_t M = (int64_t)a.B * a.n;
+    const int64_t orow = (int64_t)(a.B - 1) * a.so_b + (int64_t)(a.n - 1) * a.so_t + a.d;
+    const int64_t wrow = (int64_t)(a.Dout - 1) * a.ldw + (int64_t)a.H * a.d;
+    return M >= 1 && orow * 2 < ((int64_t)1 << 31) && wrow * 2 < ((int64_t)1 << 31);
+}
+
+hipError_t launch_out_proj(int dtype, const ProjArgs& a, hipStream_t stream) {
+    const int64_t M = (int64_t)a.B * a.n;
+    if (out_proj_mfma_ok(dtype, a)) {
+        const int64_t mtiles = (M + PM - 1) / PM, ntiles = ((int64_t)a.Dout + PN - 1) / PN;
+        const int64_t total = mtiles * ntiles;
+        if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(out_proj_mfma_kernel, dim3((uint32_t)total), dim3(256), 0, stream, a, (int32_t)mtiles,
+                           (int32_t)total);
+        return hipGetLastError();
+    }
+    const int64_t blocks = (M * a.Dout + 255) / 256;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    if (dtype == 1)
+        hipLaunchKernelGGL(out_proj_plain_kernel<uint16_t>, dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL(out_proj_plain_kernel<float>, dim3((uint32_t)blocks), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}

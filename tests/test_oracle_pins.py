@@ -451,3 +451,54 @@ def test_schedule_backward_matches_finite_differences(oracle_lib, bidir):
             flat[e] = keep
             fd = (lp - lm) / (2 * h)
             assert abs(fd - gflat[e]) <= 1e-6 * max(1.0, abs(fd)), (name, e, fd, gflat[e])
+
+
+# ---------------------------------------------------------------- gate and output projection
+# oracle/proj.py writes the two maps as numpy products; the pins are
+# brute-force loops over every index on tiny sizes, and special cases whose
+# result is known without arithmetic (one-hot inputs pick a weight entry,
+# identity weights return the concatenated heads).
+from oracle import proj as oproj
+
+
+def test_proj_matches_brute_force_loops():
+    rng = np.random.default_rng(11)
+    B, n, Dm, H, d, Dout = 2, 3, 5, 4, 2, 3
+    x = rng.standard_normal((B, n, Dm))
+    wg = rng.standard_normal((H, Dm))
+    bg = rng.standard_normal(H)
+    g = oproj.gate_logits(x, wg, bg)
+    for b in range(B):
+        for h in range(H):
+            for i in range(n):
+                acc = bg[h]
+                for c in range(Dm):
+                    acc += x[b, i, c] * wg[h, c]
+                assert abs(g[b, h, i] - acc) <= 1e-12
+    o = rng.standard_normal((B, H, n, d))
+    wo = rng.standard_normal((Dout, H * d))
+    bo = rng.standard_normal(Dout)
+    y = oproj.out_proj(o, wo, bo)
+    for b in range(B):
+        for i in range(n):
+            for r in range(Dout):
+                acc = bo[r]
+                for h in range(H):
+                    for c in range(d):
+                        acc += o[b, h, i, c] * wo[r, h * d + c]
+                assert abs(y[b, i, r] - acc) <= 1e-12
+
+
+def test_proj_special_cases():
+    B, n, Dm, H, d = 1, 4, 6, 3, 2
+    x = np.zeros((B, n, Dm))
+    x[0, 2, 4] = 1.0                            # one-hot token 2, feature 4
+    wg = np.arange(H * Dm, dtype=np.float64).reshape(H, Dm)
+    g = oproj.gate_logits(x, wg)
+    assert np.array_equal(g[0, :, 2], wg[:, 4]) and not g[0, :, [0, 1, 3]].any()
+    o = np.arange(B * H * n * d, dtype=np.float64).reshape(B, H, n, d)
+    y = oproj.out_proj(o, np.eye(H * d))
+    for h in range(H):
+        assert np.array_equal(y[0, :, h * d:(h + 1) * d], o[0, h])
+    bits = np.array([[0x3f80, 0x4000]], np.uint16)   # bf16 1.0 and 2.0, read exactly
+    assert np.array_equal(oproj.gate_logits(bits[None], np.array([[0x3f80, 0x3f80]], np.uint16)), [[[3.0]]])
