@@ -16,7 +16,7 @@
 // its A operand straight from the x rows, its B operand (the gate weights)
 // from L2.  The output projection is a GEMM over M = tokens, N = Dout,
 // K = H d with the head concatenation folded into the A operand's addresses
-// (o stays in the attention's [B, H, n, d] layout, any strides): 128 x 128
+// (o stays in the attention's [B, H, n, d] layout, any strides): 256 x 256
 // tiles, K in chunks of 32 (always inside one head), a ring of three LDS
 // slots filled two stages ahead by LDS-direct loads, XOR-swizzled rows so
 // that the MFMA operand reads are free of bank conflicts, and an epilogue
@@ -107,18 +107,31 @@ __global__ __launch_bounds__(256) void gate_f32_kernel(GateArgs a) {
 }
 
 // ------------------------------------------------------------ output projection
-constexpr int PM = 128, PN = 128, PK = 32;   // tile rows (tokens), columns (outputs), k-chunk
+constexpr int PM = 256, PN = 256, PK = 32;   // tile rows (tokens), columns (outputs), k-chunk
 constexpr int PSLOT = (PM + PN) * PK;        // elements of one ring slot (A rows, then W rows)
+constexpr int PW = 8;                        // waves per workgroup (two per SIMD)
+constexpr int PLPW = 4;                      // 1 KB loads per wave per stage
 
 // Element offset of 16-byte chunk c (of 4) of row r in a [rows][32] bf16
 // tile, XOR-swizzled by (r / 2) % 4: the 16 rows x 4 chunks of an MFMA
 // operand read then fall on distinct banks.
 __device__ __forceinline__ int psw(int r, int c) { return r * PK + ((c ^ ((r >> 1) & 3)) << 3); }
 
-__global__ __launch_bounds__(256, 2) void out_proj_mfma_kernel(ProjArgs a, int32_t mtiles, int32_t total) {
+// 256 x 256 tile, eight waves of 64 x 128 (4 x 8 MFMA blocks), two per
+// SIMD so that one wave's MFMAs cover the other's barrier and LDS waits: per
+// k-chunk a wave reads 12 operand rows of 16 bytes for 32 MFMAs.
+// Tile order: groups of GM row tiles, rows fastest inside a group, so that
+// each XCD's run of 32 consecutive tiles is about 8 row tiles x 4 column
+// tiles sharing their A and W slabs in that XCD's L2.
+constexpr int32_t GM = 8;
+
+__global__ __launch_bounds__(PW * 64, 1) void out_proj_mfma_kernel(ProjArgs a, int32_t mtiles, int32_t ntiles,
+                                                                 int32_t total) {
     __shared__ __attribute__((aligned(16))) uint16_t ring[3 * PSLOT];
     const int32_t logical = xcd_logical(blockIdx.x, total);
-    const int32_t mt = logical % mtiles, nt = logical / mtiles;   // neighbouring tiles share W columns
+    const int32_t gsize = GM * ntiles, grp = logical / gsize, first = grp * GM;
+    const int32_t gm = imin32(mtiles - first, GM), w_in = logical - grp * gsize;
+    const int32_t mt = first + w_in % gm, nt = w_in / gm;
     const int64_t M = (int64_t)a.B * a.n;
     const int64_t m0 = (int64_t)mt * PM;
     const int32_t n0 = nt * PN;
@@ -130,13 +143,13 @@ __global__ __launch_bounds__(256, 2) void out_proj_mfma_kernel(ProjArgs a, int32
 
     // ---- staging.  One 1 KB load covers 16 rows x 64 bytes; lane l fills
     // row l / 4, physical chunk l % 4 = logical chunk (l % 4) ^ ((row / 2) % 4).
-    // Waves 0-1 load the A rows (tokens), waves 2-3 the W rows (outputs),
-    // 64 rows each: 4 loads per wave per stage.
-    const bool isw = wave >= 2;
-    const int rbase = (wave & 1) * 64;
-    uint32_t voff[4];
+    // Waves 0-3 load the A rows (tokens), waves 4-7 the W rows (outputs),
+    // 64 rows each.
+    const bool isw = wave >= PW / 2;
+    const int rbase = (wave & 3) * 64;
+    uint32_t voff[PLPW];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < PLPW; ++j) {
         const int rr = rbase + 16 * j + lane / 4;                 // tile row of this lane's 16 bytes
         const int lc = (lane % 4) ^ ((rr >> 1) & 3);
         if (!isw) {
@@ -158,27 +171,26 @@ __global__ __launch_bounds__(256, 2) void out_proj_mfma_kernel(ProjArgs a, int32
         const uint16_t* src = isw ? wbase + k0 : obase + (int64_t)h * a.so_h + c0;
         uint16_t* dst = slot + (isw ? PM * PK : 0) + rbase * PK;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) dma16(src, voff[j], lds_addr(dst + 16 * j * PK));
+        for (int j = 0; j < PLPW; ++j) dma16(src, voff[j], lds_addr(dst + 16 * j * PK));
     };
 
-    f32x4_t acc[4][4];
+    f32x4_t acc[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 64;        // the wave's 64 x 64 sub-tile
+        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;       // the wave's 64 x 128 sub-tile
 
     auto compute = [&](const uint16_t* slot) __attribute__((always_inline)) {
-        bf16x8_t av[4], bv[4];
+        bf16x8_t av[4], bv[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            av[i] = *reinterpret_cast<const bf16x8_t*>(slot + psw(wm + 16 * i + x, g));
-            bv[i] = *reinterpret_cast<const bf16x8_t*>(slot + PM * PK + psw(wn + 16 * i + x, g));
-        }
+        for (int j = 0; j < 8; ++j) bv[j] = *reinterpret_cast<const bf16x8_t*>(slot + PM * PK + psw(wn + 16 * j + x, g));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const bf16x8_t*>(slot + psw(wm + 16 * i + x, g));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
+            for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
     };
 
     issue(0, ring);
@@ -188,7 +200,7 @@ __global__ __launch_bounds__(256, 2) void out_proj_mfma_kernel(ProjArgs a, int32
     // into the slot of stage s-1, compute stage s
     for (int32_t s = 0; s < nk; ++s) {
         const int cur = s % 3;
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(4));
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(PLPW));
         lds_barrier();
         issue(s + 2, ring + ((s + 2) % 3) * PSLOT);
         compute(ring + cur * PSLOT);
@@ -196,39 +208,47 @@ __global__ __launch_bounds__(256, 2) void out_proj_mfma_kernel(ProjArgs a, int32
     __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));                   // the trailing reloads land
     lds_barrier();                                                 // every wave done with the ring
 
-    // ---- epilogue: bias, bf16, and whole rows through the wave's own 8 KB
-    // of the ring ([64 rows][64 columns], 16-byte chunks swizzled by row % 8)
-    uint16_t* tile = ring + wave * 64 * 64;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int32_t col = n0 + wn + 16 * j + x;
-        const float bias = (a.bias && col < a.Dout) ? a.bias[col] : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int rr = 16 * i + 4 * g + r, cc = 16 * j + x;
-                tile[rr * 64 + ((((cc >> 3) ^ (rr & 7)) << 3) | (cc & 7))] =
-                    (uint16_t)(cvt_pk_bf16(acc[i][j][r] + bias, 0.0f) & 0xffffu);
-            }
-    }
-    lds_barrier();
+    // ---- epilogue: bias, bf16, and whole rows through LDS, in two halves of
+    // 32 rows per wave ([32 rows][128 columns] = 8 KB, 16-byte chunks
+    // swizzled by row % 16)
+    uint16_t* tile = ring + wave * 32 * 128;
     uint16_t* yb = static_cast<uint16_t*>(a.y);
+    float bias[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-        const int rr = 8 * j + lane / 8, ch = lane % 8;            // 8 rows x 8 chunks per instruction
-        const int64_t t = m0 + wm + rr;
-        const int32_t col = n0 + wn + 8 * ch;
-        if (t >= M || col >= a.Dout) continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(tile + rr * 64 + ((ch ^ (rr & 7)) << 3));
-        const int64_t b = t / a.n, i = t % a.n;
-        uint16_t* dst = yb + b * a.sy_b + i * a.sy_t + col;
-        if (col + 8 <= a.Dout) {
-            *reinterpret_cast<uint4*>(dst) = v;
-        } else {
-            const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
-            for (int q = 0; q < a.Dout - col; ++q) dst[q] = e[q];
+        const int32_t col = n0 + wn + 16 * j + x;
+        bias[j] = (a.bias && col < a.Dout) ? a.bias[col] : 0.0f;
+    }
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int rr = 16 * i + 4 * g + r, cc = 16 * j + x;
+                    tile[rr * 128 + ((((cc >> 3) ^ (rr & 15)) << 3) | (cc & 7))] =
+                        (uint16_t)(cvt_pk_bf16(acc[2 * half + i][j][r] + bias[j], 0.0f) & 0xffffu);
+                }
+        lds_barrier();
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int rr = 4 * q + lane / 16, ch = lane % 16;      // 4 rows x 16 chunks per instruction
+            const int64_t t = m0 + wm + 32 * half + rr;
+            const int32_t col = n0 + wn + 8 * ch;
+            if (t >= M || col >= a.Dout) continue;
+            const uint4 v = *reinterpret_cast<const uint4*>(tile + rr * 128 + ((ch ^ (rr & 15)) << 3));
+            const int64_t b = t / a.n, i = t % a.n;
+            uint16_t* dst = yb + b * a.sy_b + i * a.sy_t + col;
+            if (col + 8 <= a.Dout) {
+                *reinterpret_cast<uint4*>(dst) = v;
+            } else {
+                const uint16_t* e = reinterpret_cast<const uint16_t*>(&v);
+                for (int c = 0; c < a.Dout - col; ++c) dst[c] = e[c];
+            }
         }
+        lds_barrier();                                             // the tile is rewritten next half
     }
 }
 
@@ -283,8 +303,8 @@ hipError_t launch_out_proj(int dtype, const ProjArgs& a, hipStream_t stream) {
         const int64_t mtiles = (M + PM - 1) / PM, ntiles = ((int64_t)a.Dout + PN - 1) / PN;
         const int64_t total = mtiles * ntiles;
         if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(out_proj_mfma_kernel, dim3((uint32_t)total), dim3(256), 0, stream, a, (int32_t)mtiles,
-                           (int32_t)total);
+        hipLaunchKernelGGL(out_proj_mfma_kernel, dim3((uint32_t)total), dim3(PW * 64), 0, stream, a, (int32_t)mtiles,
+                           (int32_t)ntiles, (int32_t)total);
         return hipGetLastError();
     }
     const int64_t blocks = (M * a.Dout + 255) / 256;
