@@ -429,21 +429,36 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void bwd_band_kernel(BwdArgs 
         lds_barrier();
         if (s + 1 < N) issue(s + 1, Xn, Yn, Cn, Dn);
     };
+    // The tile's own key and value rows, phase B's operands: taken from LDS
+    // when the tile is one of phase A's key tiles (always for the window),
+    // else loaded after phase A.
+    const int32_t sown = t - jlo;
+    auto grab_kv = [&](const uint16_t* Ks, const uint16_t* Vs) __attribute__((always_inline)) {
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            kf[c] = *reinterpret_cast<const bf16x8_t*>(Ks + swr<D>(16 * wave + x, 4 * c + g));
+            vf[c] = *reinterpret_cast<const bf16x8_t*>(Vs + swr<D>(16 * wave + x, 4 * c + g));
+        }
+    };
     for (int32_t s = 0; s < NA; ++s) {
         if (s & 1) {
             waitissue(s, x0s, y0s, c0s, d0s);
             computeA((jlo + s) * BT, x1s, y1s);
+            if (s == sown) grab_kv(x1s, y1s);
         } else {
             waitissue(s, x1s, y1s, c1s, d1s);
             computeA((jlo + s) * BT, x0s, y0s);
+            if (s == sown) grab_kv(x0s, y0s);
         }
     }
     finishA();
 
+    if (sown < 0 || sown >= NA) {
 #pragma unroll
-    for (int c = 0; c < DC; ++c) {
-        kf[c] = *reinterpret_cast<const bf16x8_t*>(Kb + pc * kst + 32 * c + 8 * g);
-        vf[c] = *reinterpret_cast<const bf16x8_t*>(Vb + pc * vst + 32 * c + 8 * g);
+        for (int c = 0; c < DC; ++c) {
+            kf[c] = *reinterpret_cast<const bf16x8_t*>(Kb + pc * kst + 32 * c + 8 * g);
+            vf[c] = *reinterpret_cast<const bf16x8_t*>(Vb + pc * vst + 32 * c + 8 * g);
+        }
     }
 #pragma unroll
     for (int bb = 0; bb < DB; ++bb) dka[bb] = dva[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
