@@ -39,7 +39,11 @@
 
 namespace {
 
-constexpr int BT = 64;   // rows per tile, query side and key side
+constexpr int BT = 64;    // rows per tile of the skip pass (query side and key side)
+// Rows per tile of the window pass.  128-row tiles on eight waves (fewer
+// halo rows per own row) measured 5-14% slower: eight waves meet at every
+// barrier.
+constexpr int BTW = 64;
 
 // Per-row record in the workspace.
 struct alignas(16) RowRec {
@@ -116,12 +120,14 @@ __global__ __launch_bounds__(256) void bwd_record_kernel(BwdArgs ba) {
 // MASKED: the skip multiples are a schedule's mask (skip pass only); a
 // separate instantiation keeps the mask test out of the other kernels'
 // register budget.
-template <int D, bool SKIP, bool BIDIR, bool MASKED>
-__global__ __launch_bounds__(256, D == 64 ? 4 : 2) void bwd_band_kernel(BwdArgs ba, int32_t step, int32_t nres,
-                                                                         int32_t tiles, int32_t total,
-                                                                         int32_t merge) {
+// TB: rows per tile, 16 per wave.
+template <int D, bool SKIP, bool BIDIR, bool MASKED, int TB>
+__global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdArgs ba, int32_t step, int32_t nres,
+                                                                            int32_t tiles, int32_t total,
+                                                                            int32_t merge) {
+    constexpr int BT = TB, NW = TB / 16;                // tile rows, waves
     constexpr int DC = D / 32, DB = D / 16, CH = D / 8, RPI = 64 / CH;
-    constexpr int LPH = 32 / RPI;                       // 1 KB loads per wave per stage: half a tile
+    constexpr int LPH = 32 / RPI;                       // 1 KB loads per wave per stage: 32 rows of one tensor
     __shared__ __attribute__((aligned(16))) uint16_t x0s[BT * D];
     __shared__ __attribute__((aligned(16))) uint16_t x1s[BT * D];
     __shared__ __attribute__((aligned(16))) uint16_t y0s[BT * D];
@@ -185,10 +191,10 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void bwd_band_kernel(BwdArgs 
         dma16(ub, (uint32_t)(row * rst + lc) * 2u, lds_addr(dst + r0 * D));
     };
     // stage s < NA: key tile jlo+s (K to x, V to y); then query tile
-    // ilo+s-NA (Q to x, dO to y, the rows' c and D to cs, ds).  Waves 0-1
-    // load the x tensor, waves 2-3 the y tensor; each wave's two sources
-    // are fixed here, as values.
-    const bool second = wave >= 2;
+    // ilo+s-NA (Q to x, dO to y, the rows' c and D to cs, ds).  The first
+    // half of the waves load the x tensor, the second half the y tensor, 32
+    // rows each; each wave's two sources are fixed here, as values.
+    const bool second = wave >= NW / 2;
     const uint16_t* const srcA = second ? Vb : Kb;
     const uint16_t* const srcB = second ? Ob : Qb;
     const int64_t rstA = second ? vst : kst;
@@ -205,13 +211,16 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void bwd_band_kernel(BwdArgs 
         uint16_t* dst = second ? Y : X;
 #pragma unroll
         for (int j = 0; j < LPH; ++j) {
-            const int r0 = (wave & 1) * 32 + j * RPI;
+            const int r0 = (wave % (NW / 2)) * 32 + j * RPI;
             stage_rows(src, rst, tb + r0, r0, dst);
         }
-        if (!pa && (wave & 1) == 0) {
-            const int32_t p = imin32(tb + lane, L - 1);
+        if (!pa && wave % (NW / 2) == 0) {
             const uint32_t field = wave == 0 ? (SKIP ? 8u : 4u) : 0u;
-            dma4(Rb, (uint32_t)(p * step) * 16u + field, lds_addr(wave == 0 ? C : Dd));
+#pragma unroll
+            for (int q = 0; q < BT / 64; ++q) {
+                const int32_t p = imin32(tb + 64 * q + lane, L - 1);
+                dma4(Rb, (uint32_t)(p * step) * 16u + field, lds_addr((wave == 0 ? C : Dd) + 64 * q));
+            }
         }
     };
 
@@ -266,7 +275,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void bwd_band_kernel(BwdArgs 
     auto computeA = [&](int32_t kb0, const uint16_t* Ks, const uint16_t* Vs) __attribute__((always_inline)) {
         if (!wave_live) return;
 #pragma unroll
-        for (int u = 0; u < 4; u += 2) {
+        for (int u = 0; u < BT / 16; u += 2) {
             s16x4_t db[2];
             bool act[2];
 #pragma unroll
@@ -347,7 +356,7 @@ __global__ __launch_bounds__(256, D == 64 ? 4 : 2) void bwd_band_kernel(BwdArgs 
         __attribute__((always_inline)) {
         if (!wave_live) return;
 #pragma unroll
-        for (int v = 0; v < 4; v += 2) {
+        for (int v = 0; v < BT / 16; v += 2) {
             s16x4_t pb[2], db[2];
             bool act[2];
 #pragma unroll
@@ -489,17 +498,18 @@ hipError_t launch_t(const BwdArgs& ba, hipStream_t stream) {
         const int32_t tiles = (lmax + BT - 1) / BT;
         const int64_t total = (int64_t)tiles * nres * a.H * a.B;
         if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-        auto kern = a.pat.masked ? bwd_band_kernel<D, true, BIDIR, true> : bwd_band_kernel<D, true, BIDIR, false>;
-        hipLaunchKernelGGL(kern, dim3((uint32_t)total), dim3(256), 0, stream, ba, a.pat.pi, nres, tiles,
+        auto kern = a.pat.masked ? bwd_band_kernel<D, true, BIDIR, true, BT>
+                                 : bwd_band_kernel<D, true, BIDIR, false, BT>;
+        hipLaunchKernelGGL(kern, dim3((uint32_t)total), dim3(BT * 4), 0, stream, ba, a.pat.pi, nres, tiles,
                            (int32_t)total, 0);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    const int32_t tiles = (a.n + BT - 1) / BT;
+    const int32_t tiles = (a.n + BTW - 1) / BTW;
     const int64_t total = (int64_t)tiles * a.H * a.B;
     if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_band_kernel<D, false, BIDIR, false>), dim3((uint32_t)total), dim3(256), 0, stream, ba, 1, 1,
-                       tiles, (int32_t)total, skips ? 1 : 0);
+    hipLaunchKernelGGL((bwd_band_kernel<D, false, BIDIR, false, BTW>), dim3((uint32_t)total), dim3(BTW * 4), 0, stream,
+                       ba, 1, 1, tiles, (int32_t)total, skips ? 1 : 0);
     return hipGetLastError();
 }
 
@@ -513,9 +523,9 @@ bool bwd_band_supported(int dtype, const BwdArgs& ba) {
     int64_t ts = a.sq.t;
     const int64_t s4[3] = {a.sk.t, a.sv.t, a.so.t};
     for (int64_t s : s4) ts = s > ts ? s : ts;
-    const int64_t rows = (int64_t)a.n + BT;
+    const int64_t rows = (int64_t)a.n + BTW;
     return rows * ts * 2 + a.d * 2 < ((int64_t)1 << 31) && rows * 16 < ((int64_t)1 << 31) &&
-           (int64_t)a.n + 2LL * a.pat.k + 2LL * a.pat.M + 2 * BT < ((int64_t)1 << 30);
+           (int64_t)a.n + 2LL * a.pat.k + 2LL * a.pat.M + 2 * BTW < ((int64_t)1 << 30);
 }
 
 hipError_t launch_bwd_band(const BwdArgs& ba, hipStream_t stream) {
