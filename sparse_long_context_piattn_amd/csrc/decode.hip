@@ -14,7 +14,7 @@
 
 namespace {
 
-template <typename T, int D>
+template <typename T, int D, bool MASKED>
 __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
     using G = GatherShape<D>;
     __shared__ float sm_acc[4][D];
@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
 
     if (!bad) {
         const int32_t i = len - 1;
-        const RowSpan sp = row_span(i, len, a.pat);
+        const RowSpan sp = row_span_t<MASKED>(i, len, a.pat);
         const int32_t U = sp.total();
         const int32_t u0 = imin32(U, split * a.chunk);
         const int32_t u1 = imin32(U, u0 + a.chunk);
@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         const T* vb = static_cast<const T*>(a.vc) + (int64_t)s * a.sv.s + (int64_t)h * a.sv.h;
         float pl, ps;
         gate_priors(a.g[(int64_t)s * a.sg.s + (int64_t)h * a.sg.h], sp.has_skip(), &pl, &ps);
-        gather_row<T, D>(qrow, kb, vb, a.sk.t, a.sv.t, sp, i, a.pat, w0, w1, pl, ps,
+        gather_row<T, D, MASKED>(qrow, kb, vb, a.sk.t, a.sv.t, sp, i, a.pat, w0, w1, pl, ps,
                          a.scale_log2, st, a.ring);
         reduce_slots<D>(st);
     }
@@ -124,7 +124,8 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
 template <typename T, int D>
 hipError_t launch_t(const DecodeArgs& a, hipStream_t stream) {
     dim3 grid(a.S * a.H, a.splits);
-    hipLaunchKernelGGL((decode_split_kernel<T, D>), grid, dim3(256), 0, stream, a);
+    auto split = a.pat.masked ? decode_split_kernel<T, D, true> : decode_split_kernel<T, D, false>;
+    hipLaunchKernelGGL(split, grid, dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     hipLaunchKernelGGL((decode_combine_kernel<T, D>), dim3(a.S * a.H), dim3(D), 0, stream, a);

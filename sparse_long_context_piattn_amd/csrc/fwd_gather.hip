@@ -5,7 +5,7 @@
 
 namespace {
 
-template <typename T, int D>
+template <typename T, int D, bool MASKED>
 __global__ __launch_bounds__(256) void fwd_gather_kernel(FwdArgs a) {
     const int wave = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
@@ -26,12 +26,12 @@ __global__ __launch_bounds__(256) void fwd_gather_kernel(FwdArgs a) {
     const T* vb = static_cast<const T*>(a.v) + bq * a.sv.s + h * a.sv.h + tok0 * a.sv.t;
     const int64_t goff = bq * a.sg.s + h * a.sg.h + tok * a.sg.t;
 
-    const RowSpan sp = row_span(i, n, a.pat);
+    const RowSpan sp = row_span_t<MASKED>(i, n, a.pat);
     float pl, ps;
     gate_priors(a.g[goff], sp.has_skip(), &pl, &ps);
 
     RowPartial st;
-    gather_row<T, D>(qrow, kb, vb, a.sk.t, a.sv.t, sp, i, a.pat, 0, sp.total(), pl, ps,
+    gather_row<T, D, MASKED>(qrow, kb, vb, a.sk.t, a.sv.t, sp, i, a.pat, 0, sp.total(), pl, ps,
                      a.scale_log2, st);
     reduce_slots<D>(st);
 
@@ -50,7 +50,8 @@ __global__ __launch_bounds__(256) void fwd_gather_kernel(FwdArgs a) {
 template <typename T, int D>
 hipError_t launch_t(const FwdArgs& a, hipStream_t stream) {
     dim3 grid((a.n + 3) / 4, a.H, a.B);
-    hipLaunchKernelGGL((fwd_gather_kernel<T, D>), grid, dim3(256), 0, stream, a);
+    auto kern = a.pat.masked ? fwd_gather_kernel<T, D, true> : fwd_gather_kernel<T, D, false>;
+    hipLaunchKernelGGL(kern, grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

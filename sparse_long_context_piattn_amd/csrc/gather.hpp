@@ -70,7 +70,7 @@ struct RowPartial {
 // of the row's (sequence, head); k_tok_stride / v_tok_stride are the token
 // strides of the key and value tensors.  ring > 0: key position j lives in
 // row j mod ring (a rolling cache); 0: in row j.
-template <typename T, int D>
+template <typename T, int D, bool MASKED>
 __device__ __forceinline__ void gather_row(const T* __restrict__ qrow, const T* __restrict__ kbase,
                                            const T* __restrict__ vbase, int64_t k_tok_stride,
                                            int64_t v_tok_stride,
@@ -98,7 +98,7 @@ __device__ __forceinline__ void gather_row(const T* __restrict__ qrow, const T* 
         float prior = 0.0f;
         if (valid) {
             bool loc;
-            int32_t key = span_key(sp, i, pat, u, &loc);
+            int32_t key = span_key_t<MASKED>(sp, i, pat, u, &loc);
             if (ring > 0) {                               // key >= i - ring + 1: row (i - delta) mod ring
                 const int32_t r = ri - (i - key);
                 key = r < 0 ? r + ring : r;

@@ -94,35 +94,43 @@ struct RowSpan {
     __host__ __device__ bool has_skip() const { return nb + nf > 0; }
 };
 
+// The enumeration comes in two compile-time forms, MASKED (a schedule's
+// mask) and not (the range [mlo, M]), so that the gather kernels of plain
+// patterns carry none of the mask code; the runtime forms below dispatch.
+
 // Number of skip multiples m <= lim (lim = the largest that fits in range).
-__host__ __device__ inline int32_t skips_upto(const PiPattern& p, int32_t lim) {
-    if (p.masked) return mask_rank(p, imin32(lim, p.M));
+template <bool MASKED>
+__host__ __device__ inline int32_t skips_upto_t(const PiPattern& p, int32_t lim) {
+    if (MASKED) return mask_rank(p, imin32(lim, p.M));
     return imax32(0, imin32(p.M, lim) - p.mlo + 1);
 }
 
 // The r-th smallest skip multiple (r < skips_upto(p, M)).
-__host__ __device__ inline int32_t skip_multiple(const PiPattern& p, int32_t r) {
-    return p.masked ? mask_select(p, r) : p.mlo + r;
+template <bool MASKED>
+__host__ __device__ inline int32_t skip_multiple_t(const PiPattern& p, int32_t r) {
+    return MASKED ? mask_select(p, r) : p.mlo + r;
 }
 
 // Requires 0 <= i < n, k >= 0, pi >= 1, M >= 0 and n + k < 2^31.
-__host__ __device__ inline RowSpan row_span(int32_t i, int32_t n, const PiPattern& p) {
+template <bool MASKED>
+__host__ __device__ inline RowSpan row_span_t(int32_t i, int32_t n, const PiPattern& p) {
     RowSpan r;
     r.lo = imax32(0, i - p.k);
     r.hi = p.bidir ? imin32(n - 1, i + p.k) : i;
-    r.nb = skips_upto(p, i / p.pi);
-    r.nf = p.bidir ? skips_upto(p, (n - 1 - i) / p.pi) : 0;
+    r.nb = skips_upto_t<MASKED>(p, i / p.pi);
+    r.nf = p.bidir ? skips_upto_t<MASKED>(p, (n - 1 - i) / p.pi) : 0;
     return r;
 }
 
 // Union position u in [0, total) -> key index, ascending in u:
 // backward skips (farthest first), the window, forward skips.
-__host__ __device__ inline int32_t span_key(const RowSpan& r, int32_t i, const PiPattern& p, int32_t u,
-                                            bool* is_local) {
+template <bool MASKED>
+__host__ __device__ inline int32_t span_key_t(const RowSpan& r, int32_t i, const PiPattern& p, int32_t u,
+                                              bool* is_local) {
     const int32_t nb = r.nb, nl = r.n_local();
     if (u < nb) {
         *is_local = false;
-        return i - skip_multiple(p, nb - 1 - u) * p.pi;
+        return i - skip_multiple_t<MASKED>(p, nb - 1 - u) * p.pi;
     }
     u -= nb;
     if (u < nl) {
@@ -131,5 +139,19 @@ __host__ __device__ inline int32_t span_key(const RowSpan& r, int32_t i, const P
     }
     u -= nl;
     *is_local = false;
-    return i + skip_multiple(p, u) * p.pi;
+    return i + skip_multiple_t<MASKED>(p, u) * p.pi;
+}
+
+__host__ __device__ inline int32_t skips_upto(const PiPattern& p, int32_t lim) {
+    return p.masked ? skips_upto_t<true>(p, lim) : skips_upto_t<false>(p, lim);
+}
+__host__ __device__ inline int32_t skip_multiple(const PiPattern& p, int32_t r) {
+    return p.masked ? skip_multiple_t<true>(p, r) : skip_multiple_t<false>(p, r);
+}
+__host__ __device__ inline RowSpan row_span(int32_t i, int32_t n, const PiPattern& p) {
+    return p.masked ? row_span_t<true>(i, n, p) : row_span_t<false>(i, n, p);
+}
+__host__ __device__ inline int32_t span_key(const RowSpan& r, int32_t i, const PiPattern& p, int32_t u,
+                                            bool* is_local) {
+    return p.masked ? span_key_t<true>(r, i, p, u, is_local) : span_key_t<false>(r, i, p, u, is_local);
 }
