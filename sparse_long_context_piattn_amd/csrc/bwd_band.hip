@@ -138,7 +138,11 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
     __shared__ __attribute__((aligned(16))) float d1s[BT];
 
     const FwdArgs& a = ba.f;
-    const int32_t logical = xcd_logical(blockIdx.x, total);
+    // Each pass walks its tiles in the reverse of the order of the kernel
+    // before it (record kernel, skip pass, window pass), so that it starts
+    // on the heads whose rows the memory-side cache still holds.
+    const bool reverse = SKIP || !merge;
+    const int32_t logical = reverse ? total - 1 - xcd_logical(blockIdx.x, total) : xcd_logical(blockIdx.x, total);
     const int32_t t = logical % tiles;
     int32_t rest = logical / tiles;
     const int32_t res = rest % nres;

@@ -565,7 +565,10 @@ __global__ __launch_bounds__(WinShape<D>::WW * 64, WinShape<D>::EU) void fwd_win
     __shared__ __attribute__((aligned(16))) uint16_t v2s[KT * D];
     __shared__ __attribute__((aligned(16))) float gls[QT];
 
-    const int32_t logical = xcd_logical(blockIdx.x, total);
+    // Tiles in the reverse of the skip pass's order: the window pass starts
+    // on the heads the skip pass touched last, whose q, k, v and partials
+    // the memory-side cache still holds.
+    const int32_t logical = total - 1 - xcd_logical(blockIdx.x, total);
     const int32_t qt = logical % q_tiles;
     const int32_t rest = logical / q_tiles;
     const int32_t h = rest % a.H, b = rest / a.H;
