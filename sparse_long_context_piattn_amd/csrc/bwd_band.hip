@@ -185,13 +185,13 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
     // ---- staging: rows s0 .. s0+RPI-1 of the view into slot rows r0 ..;
     // lane row r0 + lane/CH, physical chunk lane%CH = logical chunk
     // (lane%CH) ^ (row%8); rows past the view load its last row
-    auto stage_rows = [&](const uint16_t* src, int64_t rst, int32_t s0, int r0, uint16_t* dst)
+    auto stage_rows = [&](const uint16_t* src, int64_t rst, int32_t s0, int r0, uint16_t* dst, int ln)
         __attribute__((always_inline)) {
-        const int rl = r0 + lane / CH;
-        const int lc = ((lane % CH) ^ (rl & 7)) << 3;
+        const int rl = r0 + ln / CH;
+        const int lc = ((ln % CH) ^ (rl & 7)) << 3;
         const bool inside = s0 + RPI - 1 < L;
         const uint16_t* ub = inside ? src + (int64_t)s0 * rst : src;
-        const int64_t row = inside ? (int64_t)(lane / CH) : (int64_t)imin32(s0 + lane / CH, L - 1);
+        const int64_t row = inside ? (int64_t)(ln / CH) : (int64_t)imin32(s0 + ln / CH, L - 1);
         dma16(ub, (uint32_t)(row * rst + lc) * 2u, lds_addr(dst + r0 * D));
     };
     // stage s < NA: key tile jlo+s (K to x, V to y); then query tile
@@ -216,7 +216,7 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
 #pragma unroll
         for (int j = 0; j < LPH; ++j) {
             const int r0 = (wave % (NW / 2)) * 32 + j * RPI;
-            stage_rows(src, rst, tb + r0, r0, dst);
+            stage_rows(src, rst, tb + r0, r0, dst, lane);
         }
         if (!pa && wave % (NW / 2) == 0) {
             const uint32_t field = wave == 0 ? (SKIP ? 8u : 4u) : 0u;
@@ -319,27 +319,71 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
                 dqa[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(tr_pair(Ks, u, bb), dd, dqa[bb], 0, 0, 0);
         }
     };
-    // dq rows out (the skip pass stores partials, the window pass adds them)
-    // and the row sums of dS: the skip pass records its sum, the window
-    // pass forms the gate gradient
-    auto finishA = [&]() __attribute__((always_inline)) {
-        const float srow = sum4(ssum);
-        if (!mine) return;
-        uint16_t* dst = dQb + pme * qst;
+    // Result rows leave through LDS as whole rows.  The MFMA layout gives a
+    // lane 4 consecutive values of one row, so a direct store would write 32
+    // bytes of each of 16 rows per instruction; instead the wave writes its
+    // 16 rows into its own 16-row region of a free slot (swizzled as the
+    // stages are) and stores 16 bytes per lane, whole rows.  The window pass
+    // first brings the skip pass's partial rows into the region with
+    // LDS-direct loads and adds them in fp32.
+    // the lane index afresh (volatile: not merged with the other uses), so
+    // that no lane offset of the code after phase B stays live across it
+    auto fresh_lane = []() __attribute__((always_inline)) {
+        int32_t ln;
+        asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+        return ln;
+    };
+    auto partial_in = [&](const uint16_t* gb, int64_t rst, uint16_t* reg) __attribute__((always_inline)) {
+        const int ln = fresh_lane();
+#pragma unroll
+        for (int j = 0; j < 16 / RPI; ++j) stage_rows(gb, rst, pw + j * RPI, j * RPI, reg, ln);
+    };
+    // the wave's accumulators (MFMA layout, times mul, plus the partial in
+    // the region when merging) into its region as bf16
+    auto acc_to_lds = [&](const f32x4_t* acc, float mul, uint16_t* reg) __attribute__((always_inline)) {
+        const int ln = fresh_lane();
+        const int xl = ln & 15, gl = ln >> 4;
 #pragma unroll
         for (int bb = 0; bb < DB; ++bb) {
-            float v0 = dqa[bb][0] * ba.scale, v1 = dqa[bb][1] * ba.scale;
-            float v2 = dqa[bb][2] * ba.scale, v3 = dqa[bb][3] * ba.scale;
-            uint2* pd = reinterpret_cast<uint2*>(dst + 16 * bb + 4 * g);
+            uint2* pl = reinterpret_cast<uint2*>(reg + swr<D>(xl, 2 * bb + (gl >> 1)) + 4 * (gl & 1));
+            float v0 = acc[bb][0] * mul, v1 = acc[bb][1] * mul, v2 = acc[bb][2] * mul, v3 = acc[bb][3] * mul;
             if (!SKIP && merge) {
-                const uint2 pr = *pd;
+                const uint2 pr = *pl;
                 v0 += bf16_lo(pr.x);
                 v1 += bf16_hi(pr.x);
                 v2 += bf16_lo(pr.y);
                 v3 += bf16_hi(pr.y);
             }
-            *pd = make_uint2(cvt_pk_bf16(v0, v1), cvt_pk_bf16(v2, v3));
+            *pl = make_uint2(cvt_pk_bf16(v0, v1), cvt_pk_bf16(v2, v3));
         }
+    };
+    // the region's rows out, 16 bytes per lane (a 32-bit byte offset from
+    // the view's first row: within the bound the launcher checks)
+    auto lds_to_rows = [&](uint16_t* gb, int64_t rst, const uint16_t* reg) __attribute__((always_inline)) {
+        const int ln = fresh_lane();
+#pragma unroll
+        for (int j = 0; j < 16 / RPI; ++j) {
+            const int r = j * RPI + ln / CH, c = ln % CH;
+            const uint4 val = *reinterpret_cast<const uint4*>(reg + swr<D>(r, c));
+            const uint32_t off = (uint32_t)((pw + r) * (int32_t)rst + 8 * c) * 2u;
+            if (pw + r < L) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(gb) + off) = val;
+        }
+    };
+    // dq rows out (the skip pass stores partials, the window pass adds them)
+    // and the row sums of dS: the skip pass records its sum, the window
+    // pass forms the gate gradient.  reg: the wave's region of a slot no
+    // stage occupies, after a barrier.
+    auto finishA = [&](uint16_t* reg) __attribute__((always_inline)) {
+        const float srow = sum4(ssum);
+        if (wave_live) {
+            if (!SKIP && merge) {
+                partial_in(dQb, qst, reg);
+                __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+            }
+            acc_to_lds(dqa, ba.scale, reg);
+            lds_to_rows(dQb, qst, reg);
+        }
+        if (!mine) return;
         if (g == 0) {
             if (SKIP) {
                 Rb[(int64_t)pme * step].ss = srow;
@@ -406,31 +450,17 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
             }
         }
     };
-    auto finishB = [&]() __attribute__((always_inline)) {
-        if (!mine) return;
-        uint16_t* kd = dKb + pme * kst;
-        uint16_t* vd = dVb + pme * vst;
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) {
-            float k0 = dka[bb][0] * ba.scale, k1 = dka[bb][1] * ba.scale;
-            float k2 = dka[bb][2] * ba.scale, k3 = dka[bb][3] * ba.scale;
-            float v0 = dva[bb][0], v1 = dva[bb][1], v2 = dva[bb][2], v3 = dva[bb][3];
-            uint2* pk = reinterpret_cast<uint2*>(kd + 16 * bb + 4 * g);
-            uint2* pv = reinterpret_cast<uint2*>(vd + 16 * bb + 4 * g);
-            if (!SKIP && merge) {
-                const uint2 ok = *pk, ov = *pv;
-                k0 += bf16_lo(ok.x);
-                k1 += bf16_hi(ok.x);
-                k2 += bf16_lo(ok.y);
-                k3 += bf16_hi(ok.y);
-                v0 += bf16_lo(ov.x);
-                v1 += bf16_hi(ov.x);
-                v2 += bf16_lo(ov.y);
-                v3 += bf16_hi(ov.y);
-            }
-            *pk = make_uint2(cvt_pk_bf16(k0, k1), cvt_pk_bf16(k2, k3));
-            *pv = make_uint2(cvt_pk_bf16(v0, v1), cvt_pk_bf16(v2, v3));
+    auto finishB = [&](uint16_t* regk, uint16_t* regv) __attribute__((always_inline)) {
+        if (!wave_live) return;
+        if (!SKIP && merge) {
+            partial_in(dKb, kst, regk);
+            partial_in(dVb, vst, regv);
+            __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
         }
+        acc_to_lds(dka, ba.scale, regk);
+        acc_to_lds(dva, 1.0f, regv);
+        lds_to_rows(dKb, kst, regk);
+        lds_to_rows(dVb, vst, regv);
     };
 
     // step s: this wave's loads of stage s landed (wait), every wave's
@@ -464,7 +494,13 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
             if (s == sown) grab_kv(x0s, y0s);
         }
     }
-    finishA();
+    // the slot that does not hold stage NA, free once every wave is past
+    // its last phase-A step
+    lds_barrier();
+    if (NA & 1)
+        finishA(x0s + 16 * wave * D);
+    else
+        finishA(x1s + 16 * wave * D);
 
     if (sown < 0 || sown >= NA) {
 #pragma unroll
@@ -484,7 +520,8 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
             computeB((ilo + s - NA) * BT, x0s, y0s, c0s, d0s);
         }
     }
-    finishB();
+    lds_barrier();
+    finishB(x0s + 16 * wave * D, y0s + 16 * wave * D);
 }
 
 template <int D, bool BIDIR>
