@@ -1,6 +1,6 @@
 """Seeded random sweep of patterns through the GPU paths, against the oracle.
 
-Each case draws a window k, period pi, skip count M, direction, head dim,
+Each of 48 forward and 32 backward cases draws a window k, period pi, skip count M, direction, head dim,
 ragged length and (sometimes) a skip schedule of up to three levels, within
 the bounds the library accepts; the prefill runs on every kernel that takes
 the pattern (split, resid, gather; PIATTN_FWD_KERNEL), and the backward on
@@ -58,7 +58,7 @@ def _forced(env, kernel, fn):
             os.environ[env] = old
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(48))
 def test_sweep_fwd_every_kernel(seed):
     w = _case(seed)
     x = wl.make_fwd_inputs(w, device=DEV)
@@ -80,7 +80,7 @@ def test_sweep_fwd_every_kernel(seed):
     assert ran >= 1 or w.levels
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(32))
 def test_sweep_bwd_both_paths(seed):
     w = _case(100 + seed)
     if w.n > 900:
