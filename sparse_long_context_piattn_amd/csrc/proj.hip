@@ -33,30 +33,39 @@ __device__ __forceinline__ void store_as(float* p, float v) { *p = v; }
 __device__ __forceinline__ void store_as(uint16_t* p, float v) { *p = (uint16_t)(cvt_pk_bf16(v, 0.0f) & 0xffffu); }
 
 // ------------------------------------------------------------------ gate (bf16)
-// One wave per 16 tokens, NB = ceil(H / 16) column blocks of heads.
-template <int NB>
+// One wave per MB blocks of 16 tokens, NB = ceil(H / 16) column blocks of
+// heads.  The gate weights (B operand) are read once per k-chunk for all MB
+// token blocks, so larger MB cuts their re-reads per token.
+template <int NB, int MB>
 __global__ __launch_bounds__(256) void gate_mfma_kernel(GateArgs a) {
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, x = lane & 15, g = lane >> 4;
-    const int64_t t0 = ((int64_t)blockIdx.x * 4 + wave) * 16;   // first token of the wave (flat b * n + i)
+    const int64_t t0 = ((int64_t)blockIdx.x * 4 + wave) * 16 * MB;   // first token of the wave (flat b * n + i)
     const int64_t T = (int64_t)a.B * a.n;
     if (t0 >= T) return;
-    const int64_t tl = t0 + x < T ? t0 + x : T - 1;                // the lane's A row (clamped)
-    const int64_t bl = tl / a.n, il = tl % a.n;
-    const uint16_t* xr = static_cast<const uint16_t*>(a.x) + bl * a.sx_b + il * a.sx_t;
+    const uint16_t* xr[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const int64_t tl = t0 + 16 * mb + x < T ? t0 + 16 * mb + x : T - 1;   // the lane's A row (clamped)
+        const int64_t bl = tl / a.n, il = tl % a.n;
+        xr[mb] = static_cast<const uint16_t*>(a.x) + bl * a.sx_b + il * a.sx_t;
+    }
     const uint16_t* wr[NB];
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb)
         wr[cb] = static_cast<const uint16_t*>(a.w) + (int64_t)imin32(16 * cb + x, a.H - 1) * a.Dm;
-    f32x4_t acc[NB];
+    f32x4_t acc[MB][NB];
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) acc[cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // four k-chunks of 32 per step: 4 independent A loads and 4 NB B loads in flight
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) acc[mb][cb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // four k-chunks of 32 per step: 4 MB independent A loads and 4 NB B loads in flight
     int32_t k0 = 0;
     for (; k0 + 128 <= a.Dm; k0 += 128) {
-        bf16x8_t av[4], bv[4][NB];
+        bf16x8_t av[4][MB], bv[4][NB];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            av[u] = *reinterpret_cast<const bf16x8_t*>(xr + k0 + 32 * u + 8 * g);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) av[u][mb] = *reinterpret_cast<const bf16x8_t*>(xr[mb] + k0 + 32 * u + 8 * g);
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb)
                 bv[u][cb] = *reinterpret_cast<const bf16x8_t*>(wr[cb] + k0 + 32 * u + 8 * g);
@@ -64,30 +73,37 @@ __global__ __launch_bounds__(256) void gate_mfma_kernel(GateArgs a) {
 #pragma unroll
         for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int cb = 0; cb < NB; ++cb)
-                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u], bv[u][cb], acc[cb], 0, 0, 0);
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb)
+                    acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[u][mb], bv[u][cb], acc[mb][cb], 0, 0, 0);
     }
     for (; k0 < a.Dm; k0 += 32) {                                  // Dm % 128 chunks of 32
-        const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xr + k0 + 8 * g);
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) {
             const bf16x8_t bv = *reinterpret_cast<const bf16x8_t*>(wr[cb] + k0 + 8 * g);
-            acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[cb], 0, 0, 0);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) {
+                const bf16x8_t av = *reinterpret_cast<const bf16x8_t*>(xr[mb] + k0 + 8 * g);
+                acc[mb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bv, acc[mb][cb], 0, 0, 0);
+            }
         }
     }
-    // lane (x, g) holds tokens t0 + 4g + r of head 16 cb + x
+    // lane (x, g) holds tokens t0 + 16 mb + 4g + r of head 16 cb + x
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
         const int32_t h = 16 * cb + x;
         if (h >= a.H) continue;
         const float bias = a.bias ? a.bias[h] : 0.0f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int64_t t = t0 + 4 * g + r;
-            if (t >= T) continue;
-            const int64_t b = t / a.n, i = t % a.n;
-            a.g[b * a.sg_b + h * a.sg_h + i * a.sg_t] = acc[cb][r] + bias;
-        }
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t t = t0 + 16 * mb + 4 * g + r;
+                if (t >= T) continue;
+                const int64_t b = t / a.n, i = t % a.n;
+                a.g[b * a.sg_b + h * a.sg_h + i * a.sg_t] = acc[mb][cb][r] + bias;
+            }
     }
 }
 
@@ -275,9 +291,14 @@ __global__ __launch_bounds__(256) void out_proj_plain_kernel(ProjArgs a) {
 hipError_t launch_gate(int dtype, const GateArgs& a, hipStream_t stream) {
     const int64_t T = (int64_t)a.B * a.n;
     if (dtype == 1) {
-        const int64_t blocks = (T + 63) / 64;
+        // token blocks per wave: the most that still leave 1024 waves (four
+        // per CU); measured at the 8K and 128K layer shapes, 2 and 4 blocks
+        // read x at 4.2 and 3.6 TB/s against 3.8 and 2.9 with one
+        const int mbs = T >= 4 * 16 * 1024 ? 4 : T >= 2 * 16 * 1024 ? 2 : 1;
+        const int64_t blocks = (T + 64 * mbs - 1) / (64 * mbs);
         if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-        auto k = a.H <= 16 ? gate_mfma_kernel<1> : gate_mfma_kernel<2>;
+        auto k = a.H <= 16 ? (mbs == 4 ? gate_mfma_kernel<1, 4> : mbs == 2 ? gate_mfma_kernel<1, 2> : gate_mfma_kernel<1, 1>)
+                           : (mbs == 4 ? gate_mfma_kernel<2, 4> : mbs == 2 ? gate_mfma_kernel<2, 2> : gate_mfma_kernel<2, 1>);
         hipLaunchKernelGGL(k, dim3((uint32_t)blocks), dim3(256), 0, stream, a);
     } else {
         const int64_t blocks = (T * a.H + 255) / 256;

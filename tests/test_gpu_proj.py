@@ -60,6 +60,22 @@ def test_gate_logits_match_oracle(case):
     _check(g, ref, absref, False, "gate " + name)
 
 
+@pytest.mark.parametrize("T,Dm,H", [(40_000, 96, 20), (70_001, 128, 16), (66_000, 160, 32)])
+def test_gate_logits_long_inputs(T, Dm, H):
+    """Token counts that make the kernel take two (T >= 32768) or four
+    (T >= 65536) blocks of 16 tokens per wave, with one and two head blocks
+    and a ragged tail."""
+    x = _rand((1, T, Dm), 20, torch.bfloat16)
+    w = _rand((H, Dm), 21, torch.bfloat16, Dm ** -0.5)
+    bias = _rand((H,), 22, torch.float32)
+    print("gate long T=%d Dm=%d H=%d" % (T, Dm, H), flush=True)
+    g = pa.gate_logits(x, w, bias)
+    torch.cuda.synchronize()
+    ref = oproj.gate_logits(host_array(x), host_array(w), bias.cpu().numpy())
+    absref = oproj.gate_logits(np.abs(oproj._f64(host_array(x))), np.abs(oproj._f64(host_array(w))))
+    _check(g, ref, absref, False, "gate long %d" % T)
+
+
 def test_gate_logits_packed_and_strided():
     """Packed [T, Dm] input gives [T, H] logits (the varlen gate layout); a
     strided x view ([B, n, Dm] out of a wider buffer) and a preallocated
