@@ -219,6 +219,96 @@ def test_fwd_prefill_128k_sampled_rows():
         assert max_err(got, ref, "fwd prefill_128k head %d sampled" % h) <= BF16_TOL, h
 
 
+def test_fwd_bidir_varlen_every_row():
+    """Every row (token, head) of the full bidir_varlen workload: 8 packed
+    sequences, about 3 million rows, against the C oracle."""
+    w = wl.WORKLOADS["bidir_varlen"]
+    x = wl.make_fwd_inputs(w, device=DEV)
+    lse = torch.empty_like(x["g"])
+    out = run_fwd(x, w, lse=lse)
+    torch.cuda.synchronize()
+    T = x["q"].shape[0]
+    ref, rlse = oracle_varlen_fwd(x, w, want_lse=True)
+    assert max_err(out.reshape(T * w.H, w.d), ref, "fwd bidir_varlen all rows") <= BF16_TOL
+    assert max_err(lse.reshape(-1), rlse, "lse bidir_varlen all rows") <= LSE_TOL_BF16
+
+
+@pytest.mark.parametrize("pi", [32, 64])
+def test_fwd_bnhd_layout_matches_bhnd(pi):
+    w = wl.Workload("layout", "fwd", "bf16", B=2, H=4, n=1640, d=64, k=16, pi=pi, M=6, seed=11)
+    x = wl.make_fwd_inputs(w, device=DEV, layout="bnhd")        # [B, n, H, d] storage
+    view = dict(q=x["q"].transpose(1, 2), k=x["k"].transpose(1, 2), v=x["v"].transpose(1, 2),
+                g=x["g"])
+    out = torch.empty_like(x["q"]).transpose(1, 2)
+    run_fwd(view, w, out=out)
+    dense = {k: v.contiguous() for k, v in view.items()}
+    out2 = run_fwd(dense, w)
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2)
+    ref = oracle_dense_fwd(dense, w)
+    assert max_err(out2, ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("pi", [32, 64])
+@pytest.mark.parametrize("gval", [float("inf"), float("-inf"), 60.0, -60.0])
+def test_fwd_gate_limits(gval, pi):
+    w = wl.Workload("gate", "fwd", "bf16", B=1, H=2, n=1700, d=64, k=10, pi=pi, M=8, seed=5)
+    x = wl.make_fwd_inputs(w, device=DEV)
+    x["g"].fill_(gval)
+    out = run_fwd(x, w)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    ref = oracle_dense_fwd(x, w)
+    assert max_err(out, ref) <= BF16_TOL
+
+
+def test_fwd_empty_input_is_a_no_op():
+    q = torch.empty((0, 2, 16, 64), dtype=torch.bfloat16, device=DEV)
+    g = torch.empty((0, 2, 16), dtype=torch.float32, device=DEV)
+    out = pa.fwd(q, q, q, g, window_k=4, period_pi=8, num_skips=2)
+    assert out.shape == q.shape
+
+
+def test_fwd_deterministic():
+    w = wl.WORKLOADS["prefill_8k"]
+    x = wl.make_fwd_inputs(w, device=DEV)
+    a = run_fwd(x, w)
+    b = run_fwd(x, w)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_fwd_prefill_8k_every_row():
+    w = wl.WORKLOADS["prefill_8k"]
+    x = wl.make_fwd_inputs(w, device=DEV)
+    lse = torch.empty_like(x["g"])
+    out = run_fwd(x, w, lse=lse)
+    torch.cuda.synchronize()
+    ref, rlse = oracle_dense_fwd(x, w, want_lse=True)
+    assert max_err(out, ref, "fwd prefill_8k all rows") <= BF16_TOL
+    assert max_err(lse, rlse, "lse prefill_8k all rows") <= LSE_TOL_BF16
+
+
+def _sampled_rows(n, count, seed, edge=300):
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([np.arange(min(edge, n)), rng.integers(0, n, count),
+                           np.arange(max(0, n - edge), n)])
+    return np.unique(rows)
+
+
+def test_fwd_prefill_128k_sampled_rows():
+    w = wl.WORKLOADS["prefill_128k"]
+    x = wl.make_fwd_inputs(w, device=DEV)
+    out = run_fwd(x, w)
+    torch.cuda.synchronize()
+    for h in (0, 13, 31):
+        rows = _sampled_rows(w.n, 1500, h)
+        sl = {k: x[k][:, h:h + 1] for k in ("q", "k", "v", "g")}
+        ref = oracle_dense_fwd(sl, w, rows=rows)           # H = 1: flat id = row
+        got = out[0, h].index_select(0, torch.from_numpy(rows).to(DEV))
+        assert max_err(got, ref, "fwd prefill_128k head %d sampled" % h) <= BF16_TOL, h
+
+
 def test_fwd_bidir_varlen_sampled_rows():
     w = wl.WORKLOADS["bidir_varlen"]
     x = wl.make_fwd_inputs(w, device=DEV)
@@ -310,11 +400,17 @@ def test_decode_equals_prefill_last_row():
 
 
 def test_decode_32k_full_size_sampled_heads():
+    """48 (sequence, head) rows of the full 128 x 32 decode call: the four
+    corners and 44 seeded ones, each against the oracle on its own cache
+    slice (the whole cache is 68.7 GB)."""
     w = wl.WORKLOADS["decode_32k"]
     x = wl.make_decode_inputs(w, device=DEV)
     out = run_decode(x, w)
     torch.cuda.synchronize()
-    for s, h in ((0, 0), (77, 5), (127, 31)):
+    rng = np.random.default_rng(32)
+    pairs = [(0, 0), (0, 31), (127, 0), (127, 31)]
+    pairs += [(int(s_), int(h_)) for s_, h_ in zip(rng.integers(0, 128, 44), rng.integers(0, 32, 44))]
+    for s, h in pairs:
         sl = dict(q=x["q"][s:s + 1, h:h + 1], k_cache=x["k_cache"][s:s + 1, h:h + 1],
                   v_cache=x["v_cache"][s:s + 1, h:h + 1], lens=x["lens"][s:s + 1],
                   g=x["g"][s:s + 1, h:h + 1])
