@@ -164,6 +164,23 @@ def test_bwd_prefill_8k_one_head_every_row(path):
         assert _rel(g1, r, "bwd %s prefill_8k %s" % (path, nm)) <= TOL["bf16"], nm
 
 
+def test_bwd_band_prefill_128k_one_head_every_row():
+    """The prefill_128k shape (B1 H32 n131072 d128, k128 pi256 M64) on the
+    band kernels: every row of head 17 against the oracle on that slice."""
+    w = wl.WORKLOADS["prefill_128k"]
+    x = wl.make_fwd_inputs(w, device=DEV)
+    gen = torch.Generator(device=DEV).manual_seed(57)
+    dout = torch.randn(x["q"].shape, generator=gen, device=DEV).to(torch.bfloat16)
+    print("bwd prefill_128k band", flush=True)
+    out, grads = run(x, w, dout, "band")
+    torch.cuda.synchronize()
+    h = 17
+    xs = {k_: v_[:, h:h + 1] for k_, v_ in x.items()}
+    ref = oracle_grads_dense(xs, w, dout[:, h:h + 1])
+    for got, r, nm in zip(grads, ref, ("dq", "dk", "dv", "dg")):
+        assert _rel(got[:, h:h + 1], r, "bwd band prefill_128k %s" % nm) <= TOL["bf16"], nm
+
+
 def test_bwd_band_bidir_varlen_one_sequence_head():
     """The bidir_varlen shape (8 packed sequences of 4096..32768 tokens, H16
     d64, k32 pi64 M32 per direction) on the band kernels: every row of the

@@ -206,14 +206,21 @@ def _sampled_rows(n, count, seed, edge=300):
     return np.unique(rows)
 
 
-def test_fwd_prefill_128k_sampled_rows():
+def test_fwd_prefill_128k_head_every_row_and_sampled_rows():
+    """The full prefill_128k call: every row of head 13, and sampled rows
+    (edges plus random) of heads 0 and 31, each against the oracle on that
+    head's slice."""
     w = wl.WORKLOADS["prefill_128k"]
     x = wl.make_fwd_inputs(w, device=DEV)
     out = run_fwd(x, w)
     torch.cuda.synchronize()
     for h in (0, 13, 31):
-        rows = _sampled_rows(w.n, 1500, h)
         sl = {k: x[k][:, h:h + 1] for k in ("q", "k", "v", "g")}
+        if h == 13:                                        # every row of one head
+            ref = oracle_dense_fwd(sl, w)
+            assert max_err(out[:, h:h + 1], ref, "fwd prefill_128k head 13 all rows") <= BF16_TOL
+            continue
+        rows = _sampled_rows(w.n, 1500, h)
         ref = oracle_dense_fwd(sl, w, rows=rows)           # H = 1: flat id = row
         got = out[0, h].index_select(0, torch.from_numpy(rows).to(DEV))
         assert max_err(got, ref, "fwd prefill_128k head %d sampled" % h) <= BF16_TOL, h
@@ -296,7 +303,10 @@ def _sampled_rows(n, count, seed, edge=300):
     return np.unique(rows)
 
 
-def test_fwd_prefill_128k_sampled_rows():
+def test_fwd_prefill_128k_head_every_row_and_sampled_rows():
+    """The full prefill_128k call: every row of head 13, and sampled rows
+    (edges plus random) of heads 0 and 31, each against the oracle on that
+    head's slice."""
     w = wl.WORKLOADS["prefill_128k"]
     x = wl.make_fwd_inputs(w, device=DEV)
     out = run_fwd(x, w)
