@@ -680,8 +680,9 @@ bool fwd_resid_supported(int dtype, const FwdArgs& a) {
     if (a.pat.masked || a.pat.mlo != a.pat.k / a.pat.pi + 1) return false;
     int64_t ts = a.sk.t > a.sv.t ? a.sk.t : a.sv.t;
     ts = ts > a.sq.t ? ts : a.sq.t;
-    if ((int64_t)a.n * ts + D >= ((int64_t)1 << 31)) return false;   // 32-bit row offsets
-    if ((int64_t)a.n * a.sg.t >= ((int64_t)1 << 31)) return false;
+    // row offsets in bytes below 2^31 (the same value read as signed or unsigned)
+    if (((int64_t)a.n * ts + D) * 2 >= ((int64_t)1 << 31)) return false;
+    if ((int64_t)a.n * a.sg.t * 4 >= ((int64_t)1 << 31)) return false;
     // row indices such as a0 + (t0 + T + 15) * pi stay in int32
     if ((int64_t)a.n + (int64_t)(2 * T + 16) * a.pat.pi >= ((int64_t)1 << 31)) return false;
     const int64_t w = (int64_t)a.pat.k + 16 + (a.pat.bidir ? a.pat.k : 0);

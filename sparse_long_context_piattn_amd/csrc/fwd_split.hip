@@ -875,13 +875,14 @@ hipError_t launch_t(const FwdArgs& a, float* lse_s, hipStream_t stream) {
 
 bool fwd_split_supported(int dtype, const FwdArgs& a) {
     if (dtype != 1 || (a.d != 64 && a.d != 128)) return false;
-    // 32-bit element offsets: rows of the sequence, and the lane offsets of
-    // 16 rows one period apart
+    // 32-bit byte offsets below 2^31 (the same value read as signed or
+    // unsigned): rows of the sequence, and the lane offsets of 16 rows one
+    // period apart
     int64_t ts = a.sk.t > a.sv.t ? a.sk.t : a.sv.t;
     ts = ts > a.sq.t ? ts : a.sq.t;
     ts = ts > 2 * a.sg.t ? ts : 2 * a.sg.t;            // the gate's byte offsets are twice as large
     const int64_t span = (int64_t)a.n + 16LL * a.pat.pi + a.d;
-    return span * ts < ((int64_t)1 << 31) &&
+    return span * ts * 2 < ((int64_t)1 << 31) &&
            (int64_t)a.n + 2LL * a.pat.k + WinShape<64>::QTW < ((int64_t)1 << 30);
 }
 
