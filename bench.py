@@ -104,48 +104,202 @@ def traffic_record(workload: str):
     return rec.get("hbm_bytes_per_step")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _grow(run, budget_s, start, total):
+    """Call run(count) with growing counts (from `start`, at most `total`)
+    until one call takes about half of budget_s; (count, seconds)."""
+    count = min(start, total)
+    while True:
+        t0 = time.perf_counter()
+        run(count)
+        el = time.perf_counter() - t0
+        if el >= budget_s * 0.5:
+            return count, el
+        if count >= total:
+            # the whole workload is a small sample: repeat it up to half the budget
+            reps = max(1, min(200, int(budget_s * 0.5 / max(el, 1e-3))))
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                run(count)
+            return reps * count, time.perf_counter() - t0
+        count = min(total, int(count * max(2.0, budget_s * 0.5 / max(el, 1e-3))))
+
+
+def _baseline(unit, value, value1, threads, sample):
+    return {"value": value, "unit": unit, "cores": threads, "kind": "oracle", "sample": sample,
+            "value_1_thread": value1, "cpu_model": cpu_model()}
+
+
 def cpu_baseline(w, x, budget_s: float):
-    """Time the fp64 CPU oracle on a bounded sample of the same workload."""
+    """Time the fp64 CPU oracle on a bounded sample of the same workload:
+    uniformly sampled query rows, on every host thread and then on one."""
     import numpy as np
     import torch
 
     import oracle
 
     threads = oracle.max_threads()
-    B, H, n, d = x["q"].shape
+    if "cu_seqlens" in x:
+        q, k, v = (x[n_].detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+                   for n_ in ("q", "k", "v"))
+        g = x["g"].detach().double().cpu().numpy()
+        cu = x["cu_seqlens"].cpu().numpy().astype(np.int64)
+        total_rows = q.shape[0] * q.shape[1]
+    else:
+        B, H, n, d = x["q"].shape
 
-    def host(t):
-        t = t.detach().permute(0, 2, 1, 3).reshape(B * n, H, d).contiguous().cpu()
-        return t.view(torch.int16).numpy().view(np.uint16)
+        def host(t):
+            t = t.detach().permute(0, 2, 1, 3).reshape(B * n, H, d).contiguous().cpu()
+            return t.view(torch.int16).numpy().view(np.uint16)
 
-    q, k, v = host(x["q"]), host(x["k"]), host(x["v"])
-    g = x["g"].detach().permute(0, 2, 1).reshape(B * n, H).double().cpu().numpy()
-    cu = np.arange(B + 1, dtype=np.int64) * n
+        q, k, v = host(x["q"]), host(x["k"]), host(x["v"])
+        g = x["g"].detach().permute(0, 2, 1).reshape(B * n, H).double().cpu().numpy()
+        cu = np.arange(B + 1, dtype=np.int64) * n
+        total_rows = B * n * H
     rng = np.random.default_rng(0)
-    total_rows = B * n * H
-    count = 4096
-    elapsed = 0.0
-    while True:
-        rows = np.sort(rng.integers(0, total_rows, count))
+    rows_all = rng.permutation(total_rows)
+
+    def run(count, nthreads):
+        rows = np.sort(rows_all[:count])
+        oracle.fwd(q, k, v, g, cu, w.k, w.pi, w.M, w.bidir, w.scale, rows=rows, levels=w.levels,
+                   nthreads=nthreads)
+
+    count, el = _grow(lambda c: run(c, threads), budget_s * 0.75, 4096, total_rows)
+    c1, el1 = _grow(lambda c: run(c, 1), budget_s * 0.25, 256, total_rows)
+    run(16, threads)                                     # restore the thread count
+    return _baseline("queries/s", count / el, c1 / el1, threads,
+                     "%d query rows (uniformly sampled without repeats; the whole set repeated when it "
+                     "is smaller) of the %s workload's %d, fp64, OpenMP over rows, %.1f s on %d threads; "
+                     "%d rows on 1 thread, %.1f s" % (count, w.name, total_rows, el, threads, c1, el1))
+
+
+def cpu_baseline_decode(w, x, budget_s: float):
+    """The fp64 oracle on decode: for a sample of sequences, the key and value
+    rows the query reads (the oracle's own neighbour list) are gathered on the
+    GPU and placed in a zeroed host cache; only the oracle calls are timed
+    (one per sequence, OpenMP over its heads)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    threads = oracle.max_threads()
+    S, H, L, d = x["k_cache"].shape
+    ln = int(x["lens"][0])
+    seqs = np.nonzero(x["lens"].cpu().numpy() == ln)[0]
+    pos, _ = oracle.neighbors(ln, w.k, w.pi, w.M, False, ln - 1)
+    pidx = torch.from_numpy(pos.astype(np.int64)).to(x["q"].device)
+    bits = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    kbuf = np.zeros((1, H, L, d), np.uint16)
+    vbuf = np.zeros((1, H, L, d), np.uint16)
+    qh, gh = bits(x["q"]), x["g"].double().cpu().numpy()
+    lens1 = np.array([ln], np.int32)
+
+    def run(nseq, nthreads):
+        el = 0.0
+        for s in seqs[:nseq]:
+            kbuf[0][:, pos] = bits(x["k_cache"][s].index_select(1, pidx))
+            vbuf[0][:, pos] = bits(x["v_cache"][s].index_select(1, pidx))
+            t0 = time.perf_counter()
+            oracle.decode(qh[s:s + 1], kbuf, vbuf, lens1, gh[s:s + 1], w.k, w.pi, w.M, w.scale,
+                          nthreads=nthreads)
+            el += time.perf_counter() - t0
+        return el
+
+    el = run(min(len(seqs), 16), threads)
+    nseq = min(len(seqs), max(1, int(16 * budget_s * 0.75 / max(el, 1e-4))))
+    el = run(nseq, threads)
+    n1 = min(len(seqs), max(1, int(nseq * 0.25 * threads)))
+    el1 = run(n1, 1)
+    run(1, threads)
+    return _baseline("queries/s", nseq * H / el, n1 * H / el1, threads,
+                     "%d sequences x %d heads of the %s call (its %d rows the query reads, gathered from "
+                     "the GPU cache), fp64, %.2f s of oracle time on %d threads; %d sequences on 1 thread, "
+                     "%.2f s" % (nseq, H, w.name, pos.size, el, threads, n1, el1))
+
+
+def cpu_baseline_backward(w, x, budget_s: float):
+    """The fp64 backward oracle on whole (sequence, head) slices of the
+    workload (it takes a packed batch; one head at a time is the sample)."""
+    import numpy as np
+    import torch
+
+    import oracle
+
+    threads = oracle.max_threads()
+    bits = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    if "cu_seqlens" in x:
+        cu = x["cu_seqlens"].cpu().numpy()
+        heads = [(slice(int(cu[s]), int(cu[s + 1])), h) for s in range(len(cu) - 1) for h in range(w.H)]
+        get = lambda t, sl: t[sl[0], sl[1]:sl[1] + 1]
+    else:
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+        get = lambda t, sl: t[sl[0], sl[1]].unsqueeze(1)
+    gen = torch.Generator(device=x["q"].device).manual_seed(7)
+
+    def one(sl):
+        q, k, v = (bits(get(x[n_], sl)) for n_ in ("q", "k", "v"))
+        dout = bits(torch.randn(get(x["q"], sl).shape, generator=gen, device=x["q"].device).to(torch.bfloat16))
+        g = get(x["g"], sl).double().cpu().numpy().reshape(q.shape[0], 1)
         t0 = time.perf_counter()
+        oracle.bwd(q, k, v, g, dout, np.array([0, q.shape[0]], np.int64), w.k, w.pi, w.M, w.bidir, w.scale,
+                   levels=w.levels)
+        return time.perf_counter() - t0, q.shape[0]
+
+    el, rows, j = 0.0, 0, 0
+    while el < budget_s * 0.75 and j < len(heads):
+        e_, r_ = one(heads[j])
+        el, rows, j = el + e_, rows + r_, j + 1
+    return _baseline("queries/s", rows / el, None, threads,
+                     "%d whole (sequence, head) slices (%d rows) of the %s workload, fp64 backward, "
+                     "%.1f s" % (j, rows, w.name, el))
+
+
+def cpu_baseline_layer(w, xs, x, wg, wo, o, budget_s: float):
+    """The fp64 oracles of the three stages on sampled tokens: gate logits
+    (oracle.proj), attention of every head of those tokens (oracle.fwd on
+    their rows), output projection (oracle.proj on the GPU's attention output
+    of those tokens); tokens/s."""
+    import numpy as np
+    import torch
+
+    import oracle
+    from oracle import proj
+
+    threads = oracle.max_threads()
+    B, H, n, d = xs["q"].shape
+    bits = lambda t: t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
+    host = lambda t: bits(t.permute(0, 2, 1, 3).reshape(B * n, H, d))
+    q, k, v = host(xs["q"]), host(xs["k"]), host(xs["v"])
+    g = xs["g"].permute(0, 2, 1).reshape(B * n, H).double().cpu().numpy()
+    cu = np.arange(B + 1, dtype=np.int64) * n
+    xh, wgh, woh = bits(x.reshape(B * n, -1)), bits(wg), bits(wo)
+    oh = bits(o.permute(0, 2, 1, 3).reshape(B * n, H * d))
+    rng = np.random.default_rng(1)
+    toks_all = rng.permutation(B * n)
+
+    def run(count):
+        toks = np.sort(toks_all[:count])
+        proj.gate_logits(xh[toks][None], wgh)
+        rows = (toks[:, None] * H + np.arange(H)[None]).reshape(-1)
         oracle.fwd(q, k, v, g, cu, w.k, w.pi, w.M, w.bidir, w.scale, rows=rows, levels=w.levels)
-        elapsed = time.perf_counter() - t0
-        if elapsed >= budget_s * 0.5 or count >= total_rows:
-            break
-        count = min(total_rows, int(count * max(2.0, budget_s / max(elapsed, 1e-3))))
-    passes = 1
-    if elapsed < budget_s * 0.5:
-        # the whole workload is a small sample: repeat it up to half the budget
-        passes = max(1, min(200, int(budget_s * 0.5 / max(elapsed, 1e-3))))
-        t0 = time.perf_counter()
-        for _ in range(passes):
-            oracle.fwd(q, k, v, g, cu, w.k, w.pi, w.M, w.bidir, w.scale, rows=rows, levels=w.levels)
-        elapsed = time.perf_counter() - t0
-    what = ("%d uniformly sampled query rows" % count if count < total_rows
-            else "all query rows, %d pass%s," % (passes, "es" if passes > 1 else ""))
-    return {"value": passes * count / elapsed, "unit": "queries/s", "cores": threads, "kind": "oracle",
-            "sample": "%s of the %s workload (%d rows), fp64, OpenMP over rows, %.1f s"
-                      % (what, w.name, total_rows, elapsed)}
+        proj.out_proj(oh[toks].reshape(1, count, H, d).transpose(0, 2, 1, 3), woh)
+
+    count, el = _grow(run, budget_s * 0.75, 256, B * n)
+    return _baseline("tokens/s", count / el, None, threads,
+                     "%d of %d tokens, uniformly sampled: gate, every head's attention row and the output "
+                     "projection, fp64 (numpy products, C oracle over rows), %.1f s" % (count, B * n, el))
 
 
 def decode_algorithmic(w):
@@ -195,13 +349,20 @@ def bench_decode(args, w, dev):
                   period_pi=w.pi, num_skips=w.M, num_splits=splits, workspace=ws, out=out,
                   rolling=bool(args.rolling))
 
-    ms_per_step = timed(step, args, dev)
+    settle_clocks(dev)
+    t = timed(step, args, dev)
+    ms_per_step = t["median"]
     if args.calibrate_copy:
         calibrate_copy(dev)
     sec = ms_per_step / 1e3
     gbps = alg_bytes / sec / 1e9
     log("%.4f ms/call  %.3e row-queries/s  %.0f GB/s (%.1f%% of HBM peak)"
         % (ms_per_step, rows / sec, gbps, 100 * gbps / HBM_PEAK_GBPS))
+    cpu = None
+    if not args.no_cpu_baseline and not args.rolling:
+        log("timing the fp64 CPU oracle on a sample ...")
+        cpu = cpu_baseline_decode(w, x, args.cpu_budget)
+        log("oracle: %.3e queries/s on %d threads" % (cpu["value"], cpu["cores"]))
     res = {"metric": "pi-attn decode (sequence, head) queries/s, 32K cache d=128 bf16, 1 GPU",
            "value": round(rows / sec, 1), "unit": "queries/s", "n_gpus": 1, "steps": args.steps,
            "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5), "higher_is_better": True,
@@ -210,11 +371,11 @@ def bench_decode(args, w, dev):
            "config": {"workload": w.name, "sequences": w.B, "H": w.H, "cache_len": w.n,
                       "d": w.d, "k": w.k, "pi": w.pi, "M": w.M, "num_splits": splits,
                       "cache": "rolling, %d rows" % slots if slots else "linear"},
-           "hbm_gbps_algorithmic": round(gbps, 1), "kernel_digest": kernel_digest(),
+           "hbm_gbps_algorithmic": round(gbps, 1), **step_fields(t), "kernel_digest": kernel_digest(),
            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
                         "traffic": traffic_record(w.name)},
-           "cpu_baseline": None}
+           "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
 
 
@@ -252,11 +413,18 @@ def bench_backward(args, w, dev, sets, outs, lengths, rows):
                cu_seqlens=x.get("cu_seqlens"),
                max_seqlen=max(lengths) if lengths else None, lse=lses[j % nsets], workspace=ws)
 
-    ms_per_step = timed(step, args, dev)
+    settle_clocks(dev)
+    t = timed(step, args, dev)
+    ms_per_step = t["median"]
     sec = ms_per_step / 1e3
     gbps = alg_bytes / sec / 1e9
     log("backward: %.4f ms/step  %.3e rows/s  %.0f GB/s (%.1f%% of HBM peak)"
         % (ms_per_step, rows / sec, gbps, 100 * gbps / HBM_PEAK_GBPS))
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU backward oracle on a sample ...")
+        cpu = cpu_baseline_backward(w, sets[0], args.cpu_budget)
+        log("oracle: %.3e rows/s on %d threads" % (cpu["value"], cpu["cores"]))
     res = {"metric": "pi-attn backward (dq, dk, dv, d gate) query rows/s, 1 GPU", "value": round(rows / sec, 1),
            "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
            "ms_per_step": round(ms_per_step, 5), "higher_is_better": True, "scaling": "weak",
@@ -265,10 +433,10 @@ def bench_backward(args, w, dev, sets, outs, lengths, rows):
            "config": {"workload": w.name, "pass": "backward", "B": w.B if not w.nseq else len(lengths),
                       "H": w.H, "n": w.n if not w.nseq else max(lengths), "d": w.d, "k": w.k, "pi": w.pi,
                       "M": w.M, "bidirectional": w.bidir, **({"levels": [list(l) for l in w.levels]} if w.levels else {})},
-           "kernel_digest": kernel_digest(),
+           **step_fields(t), "kernel_digest": kernel_digest(),
            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
-           "cpu_baseline": None}
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_record(w.name + "_backward")},
+           "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
 
 
@@ -310,7 +478,9 @@ def bench_layer(args, w, dev):
         for f in stages.values():
             f()
 
-    ms_per_step = timed(step, args, dev)
+    settle_clocks(dev)
+    t = timed(step, args, dev)
+    ms_per_step = t["median"]
     stream = torch.cuda.current_stream(dev)
     per = {}
     for name, f in stages.items():
@@ -341,6 +511,11 @@ def bench_layer(args, w, dev):
     flops = 2.0 * M * Dm * Dm
     tflops = flops / (per["out_proj"] / 1e3) / 1e12
     gate_bytes = M * Dm * 2 + M * H * 4
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the fp64 CPU oracles of the layer on a sample ...")
+        cpu = cpu_baseline_layer(w, dict(xs, g=g), x, wg, wo, o, args.cpu_budget)
+        log("oracle: %.3e tokens/s on %d threads" % (cpu["value"], cpu["cores"]))
     log("layer: %.4f ms/step  gate %.4f ms (%.0f GB/s)  attention %.4f ms  out_proj %.4f ms (%.0f TFLOP/s, "
         "%.1f%% of bf16 MFMA peak); torch linear on a contiguous copy %.4f ms"
         % (ms_per_step, per["gate"], gate_bytes / (per["gate"] / 1e3) / 1e9, per["attention"], per["out_proj"],
@@ -353,10 +528,10 @@ def bench_layer(args, w, dev):
            "config": {"workload": w.name, "pass": "layer", "B": B, "H": H, "n": n, "d": d, "Dm": Dm, "k": w.k,
                       "pi": w.pi, "M": w.M, "bidirectional": w.bidir},
            "stages_ms": {k_: round(v_, 5) for k_, v_ in per.items()},
-           "torch_linear_ms": round(lib_ms, 5),
+           "torch_linear_ms": round(lib_ms, 5), **step_fields(t),
            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None},
-           "cpu_baseline": None}
+           "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
 
 
@@ -374,21 +549,11 @@ def calibrate_copy(dev):
     del src, dst
 
 
-def step_stats(step, dev, nsteps=60):
-    """Secondary timings after the timed region: per-step durations (HIP
-    events around each step on the launch stream; p10 / p50 / p90 in ms) and
-    a warm time with one input set repeated (which the Infinity Cache may then
-    serve)."""
+def warm_ms(step, dev, nsteps=60):
+    """Secondary timing after the timed region: one input set repeated (which
+    the Infinity Cache may then serve), ms per step."""
     import torch
     stream = torch.cuda.current_stream(dev)
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(nsteps + 1)]
-    evs[0].record(stream)
-    for j in range(nsteps):
-        step(j)
-        evs[j + 1].record(stream)
-    torch.cuda.synchronize(dev)
-    per = sorted(evs[j].elapsed_time(evs[j + 1]) for j in range(nsteps))
-    q = lambda f: per[min(nsteps - 1, int(f * nsteps))]
     for _ in range(10):
         step(0)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -397,8 +562,7 @@ def step_stats(step, dev, nsteps=60):
         step(0)
     e1.record(stream)
     torch.cuda.synchronize(dev)
-    return {"p10": round(q(0.1), 5), "p50": round(q(0.5), 5), "p90": round(q(0.9), 5),
-            "warm_ms_per_step": round(e0.elapsed_time(e1) / nsteps, 5)}
+    return round(e0.elapsed_time(e1) / nsteps, 5)
 
 
 def copy_peak_gbps(dev):
@@ -478,19 +642,48 @@ def pmc_summary(args):
 
 
 def timed(step, args, dev):
+    """W untimed warmup steps, then exactly K timed steps bracketed by a device
+    synchronisation on both sides, with a HIP event recorded on the launch
+    stream between consecutive steps.  Returns the per-step statistics in
+    ms: the median (the headline), the mean over the region, p10 and p90."""
+    import statistics
+
     import torch
     for j in range(args.warmup):
         step(j)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record(stream)
     for j in range(args.steps):
         step(j)
-    ev1.record(stream)
+        evs[j + 1].record(stream)
     torch.cuda.synchronize()
-    return ev0.elapsed_time(ev1) / args.steps
+    per = sorted(evs[j].elapsed_time(evs[j + 1]) for j in range(args.steps))
+    q = lambda f: per[min(len(per) - 1, int(f * len(per)))]
+    return {"median": statistics.median(per), "mean": evs[0].elapsed_time(evs[-1]) / args.steps,
+            "p10": q(0.1), "p90": q(0.9)}
+
+
+def settle_clocks(dev, ms: float = 150.0):
+    """Untimed streaming copies for about `ms` before the timed region, so that
+    the timed steps run at the steady clocks a long job sees (a fresh GPU
+    ramps its clocks over the first tens of milliseconds of work)."""
+    import torch
+    src = torch.empty(COPY_ELEMS // 4, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(8):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+    del src, dst
+
+
+def step_fields(t):
+    """Side fields of a timed region (ms, rounded)."""
+    return {"step_ms": {"mean": round(t["mean"], 5), "p10": round(t["p10"], 5), "p50": round(t["median"], 5),
+                        "p90": round(t["p90"], 5)}}
 
 
 def main():
@@ -565,7 +758,10 @@ def main():
     if args.backward:
         return bench_backward(args, w, dev, sets, outs, lengths, rows)
 
-    ms_per_step = timed(step, args, dev)
+    copy_gbps = copy_peak_gbps(dev)
+    settle_clocks(dev)
+    t = timed(step, args, dev)
+    ms_per_step = t["median"]
     if args.calibrate_copy:
         calibrate_copy(dev)
     sec = ms_per_step / 1e3
@@ -576,11 +772,9 @@ def main():
         % (ms_per_step, qps, achieved_gbps, 100 * achieved_gbps / HBM_PEAK_GBPS, tflops,
            100 * tflops / BF16_MFMA_PEAK_TFLOPS))
 
-    stats = step_stats(step, dev)
-    copy_gbps = copy_peak_gbps(dev)
-    log("steps p10/p50/p90 %.4f/%.4f/%.4f ms, warm (one input set) %.4f ms; copy %.0f GB/s -> %.1f%% of it"
-        % (stats["p10"], stats["p50"], stats["p90"], stats["warm_ms_per_step"], copy_gbps,
-           100 * achieved_gbps / copy_gbps))
+    warm = warm_ms(step, dev)
+    log("steps mean/p10/p50/p90 %.4f/%.4f/%.4f/%.4f ms, warm (one input set) %.4f ms; copy %.0f GB/s -> %.1f%% of it"
+        % (t["mean"], t["p10"], t["median"], t["p90"], warm, copy_gbps, 100 * achieved_gbps / copy_gbps))
 
     traffic = traffic_record(w.name)
     roof = {"bound": "hbm", "achieved": round(achieved_gbps, 1), "peak": HBM_PEAK_GBPS,
@@ -607,8 +801,8 @@ def main():
            "tflops_algorithmic": round(tflops, 3),
            "mfma_pct_algorithmic": round(100 * tflops / BF16_MFMA_PEAK_TFLOPS, 3),
            "tokens_per_s": round(qps / w.H, 1),
-           "step_ms": {k_: v_ for k_, v_ in stats.items() if k_ != "warm_ms_per_step"},
-           "warm_ms_per_step": stats["warm_ms_per_step"],
+           **step_fields(t),
+           "warm_ms_per_step": warm,
            "copy_gbps_measured": round(copy_gbps, 1),
            "frac_of_measured_copy": round(achieved_gbps / copy_gbps, 4),
            "kernel_digest": kernel_digest(),

@@ -104,9 +104,11 @@ typedef struct {
  * tokens [cu_seqlens[b], cu_seqlens[b+1]) of one packed token axis (device
  * int32 array of B+1 non-decreasing offsets starting at 0).  The sequence
  * stride s[0] is ignored and t is the packed token index.  n must be >= the
- * longest sequence (the grid covers n rows per sequence; the library reads
- * cu_seqlens on the device and does not check them).  No attention crosses a
- * sequence boundary.
+ * longest sequence: the grid covers n rows per sequence and the library reads
+ * cu_seqlens on the device only, so it cannot report a longer sequence; such
+ * a sequence is cut at n rows (its later rows are neither read as keys nor
+ * written), and nothing is indexed beyond n rows of any buffer.  No
+ * attention crosses a sequence boundary.
  *
  * Requirements: B, H, n >= 1; d in {32, 64, 128}; for PIATTN_BF16 the q, k,
  * v, out pointers are 16-byte aligned and their strides multiples of 8
@@ -332,6 +334,26 @@ int piattn_neighbors(int32_t n, const piattn_pattern *pattern, int32_t q_begin,
 /* Longest possible list: (k+1)+M causal, (2k+1)+2M bidirectional; -1 if the
  * pattern is invalid. */
 int32_t piattn_neighbors_cap(const piattn_pattern *pattern);
+
+/*
+ * Testing and measurement hook (not for production dispatch): force the
+ * kernel that piattn_fwd and piattn_bwd run for every later call in this
+ * process.  PIATTN_KERNEL_AUTO (0) restores the automatic choice (the first
+ * kernel that can take a call).  A forced kernel that cannot take a call
+ * makes that call return PIATTN_EUNSUPPORTED.  The setting is process-wide
+ * and read once per call; change it only while no other thread calls into
+ * the library.  Returns PIATTN_OK, or PIATTN_EINVAL for an unknown id.
+ */
+enum {
+    PIATTN_KERNEL_AUTO = 0,
+    PIATTN_FWD_SPLIT = 1,   /* skip pass + window pass (bf16, d 64 / 128) */
+    PIATTN_FWD_RESID = 2,   /* residue-tiled single kernel (bf16, d 64) */
+    PIATTN_FWD_GATHER = 3,  /* one wave per row (any dtype and d) */
+    PIATTN_FWD_LAST = PIATTN_FWD_GATHER,
+    PIATTN_BWD_BAND = 1,    /* MFMA band kernels (bf16, d 64 / 128, lse given) */
+    PIATTN_BWD_GATHER = 2   /* gather kernels (any dtype and d) */
+};
+int piattn_debug_force_kernels(int32_t fwd_kernel, int32_t bwd_kernel);
 
 /* Description of the last error on this thread ("" if none). */
 const char *piattn_last_error(void);

@@ -8,6 +8,7 @@ fallback.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import math
 import os
@@ -26,7 +27,7 @@ EXPORTS = ["piattn_fwd", "piattn_fwd_workspace_bytes", "piattn_bwd", "piattn_bwd
            "piattn_decode", "piattn_decode_workspace_bytes",
            "piattn_decode_auto_splits", "piattn_rolling_slots", "piattn_cache_append",
            "piattn_decode_rolling", "piattn_neighbors", "piattn_neighbors_cap",
-           "piattn_last_error", "piattn_version"]
+           "piattn_last_error", "piattn_version", "piattn_debug_force_kernels"]
 
 
 class PiattnError(RuntimeError):
@@ -100,6 +101,8 @@ def lib():
         L.piattn_last_error.restype = ctypes.c_char_p
         L.piattn_version.argtypes = []
         L.piattn_version.restype = ctypes.c_char_p
+        L.piattn_debug_force_kernels.argtypes = [i32, i32]
+        L.piattn_debug_force_kernels.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -437,6 +440,23 @@ def neighbors(n: int, *, window_k: int, period_pi: int, num_skips: int, bidirect
                                 _ptr(kind), _ptr(count), ctypes.c_void_p(_stream(idx.device)))
     _check(rc)
     return idx, kind, count
+
+
+FWD_KERNELS = {"auto": 0, "split": 1, "resid": 2, "gather": 3}
+BWD_KERNELS = {"auto": 0, "band": 1, "gather": 2}
+
+
+@contextlib.contextmanager
+def forced_kernels(fwd: str = "auto", bwd: str = "auto"):
+    """Testing and measurement: run fwd / bwd calls inside the block on the
+    named kernels (piattn_debug_force_kernels; process-wide).  A forced
+    kernel that cannot take a call makes it raise PiattnError
+    (PIATTN_EUNSUPPORTED).  The automatic choice is restored on exit."""
+    _check(lib().piattn_debug_force_kernels(FWD_KERNELS[fwd], BWD_KERNELS[bwd]))
+    try:
+        yield
+    finally:
+        _check(lib().piattn_debug_force_kernels(0, 0))
 
 
 def version() -> str:

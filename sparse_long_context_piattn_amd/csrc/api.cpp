@@ -2,6 +2,7 @@
 // and launches on the caller's stream.  Declarations and the contract of
 // every entry point are in include/piattn.h.
 #include <math.h>
+#include <atomic>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -15,6 +16,10 @@
 namespace {
 
 thread_local char g_err[512] = "";
+
+// Kernel overrides set by piattn_debug_force_kernels (0 = automatic choice).
+std::atomic<int32_t> g_force_fwd{0};
+std::atomic<int32_t> g_force_bwd{0};
 
 int fail(int code, const char* fmt, ...) {
     va_list ap;
@@ -166,7 +171,17 @@ extern "C" {
 
 const char* piattn_last_error(void) { return g_err; }
 
-const char* piattn_version(void) { return "libpiattn 0.1 (gfx950)"; }
+const char* piattn_version(void) { return "libpiattn 0.2 (gfx950)"; }
+
+int piattn_debug_force_kernels(int32_t fwd_kernel, int32_t bwd_kernel) {
+    if (fwd_kernel < PIATTN_KERNEL_AUTO || fwd_kernel > PIATTN_FWD_LAST)
+        return fail(PIATTN_EINVAL, "fwd_kernel=%d is not a prefill kernel id", fwd_kernel);
+    if (bwd_kernel < PIATTN_KERNEL_AUTO || bwd_kernel > PIATTN_BWD_GATHER)
+        return fail(PIATTN_EINVAL, "bwd_kernel=%d is not a backward kernel id", bwd_kernel);
+    g_force_fwd.store(fwd_kernel, std::memory_order_relaxed);
+    g_force_bwd.store(bwd_kernel, std::memory_order_relaxed);
+    return ok();
+}
 
 int32_t piattn_neighbors_cap(const piattn_pattern* pattern) {
     PiPattern p;
@@ -282,9 +297,8 @@ int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
     if (rc) return rc;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int dt = dtype == PIATTN_BF16 ? 1 : 0;
-    // Kernel choice.  PIATTN_FWD_KERNEL = split | resid | gather forces
-    // one kernel (testing and measurement; EUNSUPPORTED if it cannot take the
-    // call); unset or "auto" picks the first that can.
+    // Kernel choice: the first kernel that can take the call, unless
+    // piattn_debug_force_kernels forced one (EUNSUPPORTED if it cannot).
     // The split path checks the workspace first (the other kernels take none).
     auto split = [&]() -> int {
         const size_t need = fwd_split_workspace(dtype, B, H, n, d, p);
@@ -296,12 +310,12 @@ int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
         }
         return launch_status(launch_fwd_split(a, need ? static_cast<float*>(workspace) : nullptr, st));
     };
-    const char* force = getenv("PIATTN_FWD_KERNEL");
-    if (force && *force && strcmp(force, "auto") != 0) {
-        if (!strcmp(force, "resid") && fwd_resid_supported(dt, a)) return launch_status(launch_fwd_resid(a, st));
-        if (!strcmp(force, "split") && fwd_split_supported(dt, a)) return split();
-        if (!strcmp(force, "gather")) return launch_status(launch_fwd_gather(dt, a, st));
-        return fail(PIATTN_EUNSUPPORTED, "PIATTN_FWD_KERNEL=%s cannot take this call", force);
+    const int32_t force = g_force_fwd.load(std::memory_order_relaxed);
+    if (force != PIATTN_KERNEL_AUTO) {
+        if (force == PIATTN_FWD_RESID && fwd_resid_supported(dt, a)) return launch_status(launch_fwd_resid(a, st));
+        if (force == PIATTN_FWD_SPLIT && fwd_split_supported(dt, a)) return split();
+        if (force == PIATTN_FWD_GATHER) return launch_status(launch_fwd_gather(dt, a, st));
+        return fail(PIATTN_EUNSUPPORTED, "the forced prefill kernel (%d) cannot take this call", force);
     }
     if (fwd_split_supported(dt, a)) return split();
     if (fwd_resid_supported(dt, a)) return launch_status(launch_fwd_resid(a, st));
@@ -356,19 +370,15 @@ int piattn_bwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
     const int dt = dtype == PIATTN_BF16 ? 1 : 0;
     hipStream_t st = static_cast<hipStream_t>(stream);
     // Kernel choice: the MFMA band kernels when they take the call (bf16,
-    // d 64 / 128, lse given), else the gather kernels.  PIATTN_BWD_KERNEL =
-    // band | gather forces one (testing and measurement; EUNSUPPORTED if it
-    // cannot take the call).
-    const char* force = getenv("PIATTN_BWD_KERNEL");
+    // d 64 / 128, lse given), else the gather kernels, unless
+    // piattn_debug_force_kernels forced one (EUNSUPPORTED if it cannot).
+    const int32_t force = g_force_bwd.load(std::memory_order_relaxed);
     const bool band_ok = bwd_band_supported(dt, ba);
-    if (force && *force && strcmp(force, "auto") != 0) {
-        if (strcmp(force, "band") == 0) {
-            if (!band_ok) return fail(PIATTN_EUNSUPPORTED, "PIATTN_BWD_KERNEL=band cannot take this call");
-            return launch_status(launch_bwd_band(ba, st));
-        }
-        if (strcmp(force, "gather") == 0) return launch_status(launch_bwd(dt, ba, st));
-        return fail(PIATTN_EINVAL, "PIATTN_BWD_KERNEL=%s is not band, gather or auto", force);
+    if (force == PIATTN_BWD_BAND) {
+        if (!band_ok) return fail(PIATTN_EUNSUPPORTED, "the forced band backward cannot take this call");
+        return launch_status(launch_bwd_band(ba, st));
     }
+    if (force == PIATTN_BWD_GATHER) return launch_status(launch_bwd(dt, ba, st));
     return launch_status(band_ok ? launch_bwd_band(ba, st) : launch_bwd(dt, ba, st));
 }
 

@@ -35,8 +35,7 @@ __device__ __forceinline__ RowLoc row_loc(const FwdArgs& a, int32_t b) {
     r.n = a.n;
     r.tok0 = 0;
     if (a.cu) {
-        r.tok0 = a.cu[b];
-        r.n = a.cu[b + 1] - a.cu[b];
+        varlen_seq(a.cu, b, a.n, &r.tok0, &r.n);
     }
     r.bq = a.cu ? 0 : (int64_t)b;
     return r;

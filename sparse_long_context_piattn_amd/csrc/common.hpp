@@ -96,6 +96,18 @@ struct DecodeArgs {
     float scale_log2;
 };
 
+// Sequence b of a varlen batch: its first packed token and its length,
+// clamped into [0, nmax].  Grids and per-row workspaces are sized for nmax
+// rows per sequence, so a sequence longer than nmax is cut at nmax rows (its
+// later rows are left unwritten) rather than indexed past those buffers.
+__device__ __forceinline__ void varlen_seq(const int32_t* cu, int32_t b, int32_t nmax, int64_t* tok0,
+                                           int32_t* n) {
+    const int32_t c0 = cu[b], c1 = cu[b + 1];
+    *tok0 = c0;
+    const int32_t len = c1 - c0;
+    *n = len < 0 ? 0 : (len > nmax ? nmax : len);
+}
+
 // ---------------------------------------------------------------- bf16
 
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }

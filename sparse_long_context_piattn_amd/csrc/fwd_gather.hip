@@ -14,8 +14,7 @@ __global__ __launch_bounds__(256) void fwd_gather_kernel(FwdArgs a) {
     int32_t n = a.n;
     int64_t tok0 = 0;
     if (a.cu) {
-        tok0 = a.cu[b];
-        n = a.cu[b + 1] - a.cu[b];
+        varlen_seq(a.cu, b, a.n, &tok0, &n);
     }
     if (i >= n) return;
     const int64_t tok = tok0 + i;

@@ -220,8 +220,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     int32_t n = a.n;
     int64_t tok0 = 0;
     if (a.cu) {
-        tok0 = a.cu[b];
-        n = a.cu[b + 1] - a.cu[b];
+        varlen_seq(a.cu, b, a.n, &tok0, &n);
     }
     const int32_t pi = a.pat.pi, kw = a.pat.k, M = a.pat.M;
     const int32_t a0 = at * AT;

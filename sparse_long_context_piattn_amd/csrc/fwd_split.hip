@@ -160,8 +160,7 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_kernel(FwdArgs a, float* lse
     int32_t n = a.n;
     int64_t tok0 = 0;
     if (a.cu) {
-        tok0 = a.cu[b];
-        n = a.cu[b + 1] - a.cu[b];
+        varlen_seq(a.cu, b, a.n, &tok0, &n);
     }
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -367,8 +366,7 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
     int32_t n = a.n;
     int64_t tok0 = 0;
     if (a.cu) {
-        tok0 = a.cu[b];
-        n = a.cu[b + 1] - a.cu[b];
+        varlen_seq(a.cu, b, a.n, &tok0, &n);
     }
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -575,8 +573,7 @@ __global__ __launch_bounds__(WinShape<D>::WW * 64, WinShape<D>::EU) void fwd_win
     int32_t n = a.n;
     int64_t tok0 = 0;
     if (a.cu) {
-        tok0 = a.cu[b];
-        n = a.cu[b + 1] - a.cu[b];
+        varlen_seq(a.cu, b, a.n, &tok0, &n);
     }
     const int32_t q0 = qt * QT;
     if (q0 >= n) return;                                // workgroup-uniform
@@ -880,6 +877,7 @@ bool fwd_split_supported(int dtype, const FwdArgs& a) {
     // period apart
     int64_t ts = a.sk.t > a.sv.t ? a.sk.t : a.sv.t;
     ts = ts > a.sq.t ? ts : a.sq.t;
+    ts = ts > a.so.t ? ts : a.so.t;                    // the window pass reads the skip partials from out
     ts = ts > 2 * a.sg.t ? ts : 2 * a.sg.t;            // the gate's byte offsets are twice as large
     const int64_t span = (int64_t)a.n + 16LL * a.pat.pi + a.d;
     return span * ts * 2 < ((int64_t)1 << 31) &&

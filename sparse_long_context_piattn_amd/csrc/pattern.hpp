@@ -1,8 +1,12 @@
-// pattern.hpp -- the one closed-form neighbour enumerator of libpiattn.
+// pattern.hpp -- the closed-form neighbour enumerator of libpiattn.
 //
-// Every kernel (neighbour dump, prefill, decode) derives its key lists from
-// RowSpan, so the bit-exact check of the dump covers the compute kernels'
-// index arithmetic too.
+// The neighbour dump, the gather prefill and backward kernels and decode
+// walk their key lists through RowSpan.  The MFMA kernels (the split skip and
+// window passes, the residue-tiled kernel, the band backward) do not: they
+// test block membership with their own range arithmetic over 16-key blocks.
+// Each kernel's membership is therefore checked on its own, bit-exactly,
+// through its outputs (a probe key that dominates its row's scores, read back
+// per row and kind), besides the dump's check of RowSpan.
 //
 // pi-Attention pattern (gist.science "pi-Attention: Periodic Sparse
 // Transformers ...", section 2 "Methodology", items "Ring-Local Attention"

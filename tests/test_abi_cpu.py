@@ -274,3 +274,17 @@ def test_schedule_caps_and_validation():
     assert rc == EUNSUPPORTED and "gcd" in msg, msg
     # the same levels with the far multiples inside the window are fine
     assert cap(k=300, pi=5, M=4, levels=[(2, 100)]) == 301
+
+
+def test_debug_force_kernels_ids():
+    L = pa.lib()
+    assert L.piattn_debug_force_kernels(0, 0) == 0
+    for f, b in ((-1, 0), (99, 0), (0, -1), (0, 3)):
+        assert L.piattn_debug_force_kernels(f, b) == EINVAL
+        assert "kernel id" in pa.lib().piattn_last_error().decode()
+    for name in pa.binding.FWD_KERNELS:
+        with pa.forced_kernels(fwd=name):
+            pass
+    with pa.forced_kernels(bwd="band"):
+        pass
+    assert L.piattn_debug_force_kernels(0, 0) == 0

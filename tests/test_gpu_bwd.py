@@ -39,22 +39,14 @@ def _rel(got, ref, tag):
 
 def run(x, w, dout, path="gather"):
     """Forward, then the backward on `path`: gather (no lse) or band (the
-    forward's lse, and PIATTN_BWD_KERNEL=band so that a call the MFMA
+    forward's lse, with the band kernels forced so that a call the MFMA
     kernels cannot take fails instead of falling back)."""
-    import os
     kw = dict(window_k=w.k, period_pi=w.pi, num_skips=w.M, bidirectional=w.bidir,
               cu_seqlens=x.get("cu_seqlens"))
     lse = torch.empty_like(x["g"]) if path == "band" else None
     out = pa.fwd(x["q"], x["k"], x["v"], x["g"], lse=lse, **kw)
-    old = os.environ.get("PIATTN_BWD_KERNEL")
-    os.environ["PIATTN_BWD_KERNEL"] = path
-    try:
+    with pa.forced_kernels(bwd=path):
         return out, pa.bwd(x["q"], x["k"], x["v"], x["g"], out, dout, lse=lse, **kw)
-    finally:
-        if old is None:
-            del os.environ["PIATTN_BWD_KERNEL"]
-        else:
-            os.environ["PIATTN_BWD_KERNEL"] = old
 
 
 def oracle_grads_dense(x, w, dout):
@@ -239,9 +231,8 @@ def test_bwd_band_and_gather_agree():
 
 
 def test_bwd_band_refuses_what_it_cannot_take():
-    """PIATTN_BWD_KERNEL=band without lse, or for fp32, is EUNSUPPORTED
+    """The forced band backward without lse, or for fp32, is EUNSUPPORTED
     (refused on the host, before any launch)."""
-    import os
     w = wl.Workload("ref", "fwd", "bf16", B=1, H=1, n=64, d=64, k=4, pi=8, M=2, seed=59)
     x = wl.make_fwd_inputs(w, device=DEV)
     lse = torch.empty_like(x["g"])
@@ -249,12 +240,9 @@ def test_bwd_band_refuses_what_it_cannot_take():
     out = pa.fwd(x["q"], x["k"], x["v"], x["g"], lse=lse, **kw)
     xf = {k_: v_.float() if v_.dtype == torch.bfloat16 else v_ for k_, v_ in x.items()}
     outf = out.float()
-    os.environ["PIATTN_BWD_KERNEL"] = "band"
-    try:
+    with pa.forced_kernels(bwd="band"):
         for args, use_lse in (((x["q"], x["k"], x["v"], x["g"], out, torch.ones_like(out)), False),
                               ((xf["q"], xf["k"], xf["v"], xf["g"], outf, torch.ones_like(outf)), True)):
             with pytest.raises(pa.PiattnError) as e:
                 pa.bwd(*args, lse=lse if use_lse else None, **kw)
             assert e.value.code == 2
-    finally:
-        del os.environ["PIATTN_BWD_KERNEL"]

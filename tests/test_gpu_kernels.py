@@ -1,11 +1,10 @@
-"""GPU parity of every prefill kernel, each forced through PIATTN_FWD_KERNEL.
+"""GPU parity of every prefill kernel, each forced through pa.forced_kernels.
 
 The default dispatch runs one kernel per call shape; these tests pin each
 kernel (split, residue-layout, gather) to the fp64 oracle on
 the cases it accepts, so that a kernel the dispatch does not pick for the
 headline shapes stays covered.  Tolerances as in test_gpu_parity.
 """
-import os
 import zlib
 
 import numpy as np
@@ -26,20 +25,14 @@ KERNELS = ["split", "resid", "gather"]
 
 
 def run_fwd(x, w, kernel, **kw):
-    old = os.environ.get("PIATTN_FWD_KERNEL")
-    os.environ["PIATTN_FWD_KERNEL"] = kernel
     try:
-        return pa.fwd(x["q"], x["k"], x["v"], x["g"], window_k=w.k, period_pi=w.pi,
-                      num_skips=w.M, bidirectional=w.bidir, cu_seqlens=x.get("cu_seqlens"), **kw)
+        with pa.forced_kernels(fwd=kernel):
+            return pa.fwd(x["q"], x["k"], x["v"], x["g"], window_k=w.k, period_pi=w.pi,
+                          num_skips=w.M, bidirectional=w.bidir, cu_seqlens=x.get("cu_seqlens"), **kw)
     except pa.PiattnError as e:
         if "cannot take this call" in str(e):
             pytest.skip("%s does not take this shape" % kernel)
         raise
-    finally:
-        if old is None:
-            del os.environ["PIATTN_FWD_KERNEL"]
-        else:
-            os.environ["PIATTN_FWD_KERNEL"] = old
 
 
 CASES = [

@@ -9,7 +9,6 @@ residue-tiled one, whose own bound is n d H 2 bytes) that still matches.
 Rows checked: the first and last 300 and 2000 seeded ones of one head,
 against the oracle on that head's slice.
 """
-import os
 
 import numpy as np
 import pytest
@@ -18,7 +17,7 @@ import torch
 import sparse_long_context_piattn_amd as pa
 from sparse_long_context_piattn_amd import workloads as wl
 
-from helpers import max_err, oracle_dense_fwd
+from helpers import max_err, oracle_dense_fwd, oracle_varlen_fwd
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -38,16 +37,8 @@ def _inputs(n, seed):
 
 
 def _fwd(x, kernel=None):
-    old = os.environ.get("PIATTN_FWD_KERNEL")
-    if kernel:
-        os.environ["PIATTN_FWD_KERNEL"] = kernel
-    try:
+    with pa.forced_kernels(fwd=kernel or "auto"):
         return pa.fwd(x["q"], x["k"], x["v"], x["g"], window_k=K, period_pi=PI, num_skips=M)
-    finally:
-        if old is None:
-            os.environ.pop("PIATTN_FWD_KERNEL", None)
-        else:
-            os.environ["PIATTN_FWD_KERNEL"] = old
 
 
 def _check(x, out, n, tag):
@@ -79,3 +70,89 @@ def test_one_token_more_leaves_the_split_path():
     out = _fwd(x)
     torch.cuda.synchronize()
     _check(x, out, n, "default dispatch n=%d" % n)
+
+
+def test_out_token_stride_counts_in_the_split_bound():
+    """q, k, v in [B, H, n, d] storage (token stride d) but out in [B, n, H, d]
+    storage (token stride H d): the window pass reads the skip partials back
+    from out with 32-bit offsets, so out's stride alone must make the split
+    path refuse, and the default dispatch must still match the oracle."""
+    n = N_MAX + 1
+    gen = torch.Generator(device=DEV).manual_seed(63)
+    x = {k_: torch.randn((1, H, n, D), generator=gen, device=DEV, dtype=torch.bfloat16)
+         for k_ in ("q", "k", "v")}
+    x["g"] = torch.randn((1, H, n), generator=gen, device=DEV, dtype=torch.float32)
+    out = torch.empty((1, n, H, D), dtype=torch.bfloat16, device=DEV).permute(0, 2, 1, 3)
+    print("limit: out token stride %d at n=%d" % (out.stride(2), n), flush=True)
+    kw = dict(window_k=K, period_pi=PI, num_skips=M, out=out)
+    with pytest.raises(pa.PiattnError) as e:
+        with pa.forced_kernels(fwd="split"):
+            pa.fwd(x["q"], x["k"], x["v"], x["g"], **kw)
+    assert e.value.code == 2
+    pa.fwd(x["q"], x["k"], x["v"], x["g"], **kw)
+    torch.cuda.synchronize()
+    _check(x, out, n, "default dispatch, strided out, n=%d" % n)
+
+
+def test_d128_beyond_the_split_bound_runs_the_gather_kernel():
+    """d = 128 in token-major storage one token past the split path's bound:
+    the residue-tiled kernel takes d = 64 only, so the gather kernel (64-bit
+    offsets) runs, and must match the oracle."""
+    d, pi, k, m, h = 128, 256, 128, 8, 16
+    n = (1 << 31) // (2 * h * d) - 16 * pi - d
+    gen = torch.Generator(device=DEV).manual_seed(64)
+    t = [torch.randn((1, n, h, d), generator=gen, device=DEV, dtype=torch.bfloat16) for _ in range(3)]
+    g = torch.randn((1, n, h), generator=gen, device=DEV, dtype=torch.float32)
+    x = {"q": t[0].permute(0, 2, 1, 3), "k": t[1].permute(0, 2, 1, 3), "v": t[2].permute(0, 2, 1, 3),
+         "g": g.permute(0, 2, 1)}
+    kw = dict(window_k=k, period_pi=pi, num_skips=m)
+    print("limit: d=128 n=%d" % n, flush=True)
+    with pytest.raises(pa.PiattnError) as e:
+        with pa.forced_kernels(fwd="split"):
+            pa.fwd(x["q"], x["k"], x["v"], x["g"], **kw)
+    assert e.value.code == 2
+    out = pa.fwd(x["q"], x["k"], x["v"], x["g"], **kw)
+    torch.cuda.synchronize()
+    w = wl.Workload("limit128", "fwd", "bf16", B=1, H=1, n=n, d=d, k=k, pi=pi, M=m, seed=0)
+    rng = np.random.default_rng(65)
+    rows = np.unique(np.concatenate([np.arange(200), rng.integers(0, n, 1000), np.arange(n - 200, n)]))
+    hh = 5
+    sl = {k_: x[k_][:, hh:hh + 1] for k_ in ("q", "k", "v", "g")}
+    ref = oracle_dense_fwd(sl, w, rows=rows)
+    got = out[0, hh].index_select(0, torch.from_numpy(rows).to(DEV))
+    assert max_err(got, ref, "gather d=128 n=%d" % n) <= BF16_TOL
+
+
+@pytest.mark.parametrize("kernel", ["auto", "split", "resid", "gather"])
+def test_varlen_sequence_longer_than_n_is_cut_not_overrun(kernel):
+    """A varlen call whose n (max_seqlen) is below a sequence's length: that
+    sequence is cut at n rows -- rows < n match the oracle on the sequence
+    truncated to n, rows >= n are left untouched -- and no write lands past
+    the caller's workspace."""
+    lens = [300, 1000, 64]
+    nmax = 700
+    wv = wl.Workload("cut", "fwd", "bf16", H=2, d=64, k=20, pi=64, M=4, bidir=False, nseq=3,
+                     len_lo=1, len_hi=1000, seed=66)
+    x = wl.make_fwd_inputs(wv, device=DEV, lengths=lens)
+    out = torch.full_like(x["q"], 7.0)
+    need = pa.fwd_workspace_bytes(1, 3, 2, nmax, 64, pa.make_pattern(20, 64, 4))
+    guard = 1 << 16
+    ws = torch.full((need + guard,), 0xAB, dtype=torch.uint8, device=DEV)
+    try:
+        with pa.forced_kernels(fwd=kernel):
+            pa.fwd(x["q"], x["k"], x["v"], x["g"], window_k=20, period_pi=64, num_skips=4,
+                   cu_seqlens=x["cu_seqlens"], max_seqlen=nmax, out=out, workspace=ws)
+    except pa.PiattnError as e:
+        if e.code == 2:
+            pytest.skip("%s does not take this shape" % kernel)
+        raise
+    torch.cuda.synchronize()
+    assert bool((ws[need:] == 0xAB).all()), "write past the workspace"
+    cu = x["cu_seqlens"].cpu().numpy()
+    cut = [min(L, nmax) for L in lens]
+    xs = {k_: torch.cat([x[k_][cu[s]:cu[s] + cut[s]] for s in range(3)]) for k_ in ("q", "k", "v", "g")}
+    xs["cu_seqlens"] = torch.tensor(np.concatenate([[0], np.cumsum(cut)]), dtype=torch.int32, device=DEV)
+    ref = oracle_varlen_fwd(xs, wv)
+    got = torch.cat([out[cu[s]:cu[s] + cut[s]] for s in range(3)])
+    assert max_err(got.reshape(-1, 64), ref, "varlen cut at n (%s)" % kernel) <= BF16_TOL
+    assert bool((out[cu[1] + nmax:cu[2]].float() == 7.0).all()), "rows past n were written"

@@ -8,7 +8,6 @@ test_oracle_pins.py): the neighbour dump bit for bit, the prefill kernels
 (split on MFMA, gather), decode (linear and rolling caches) and both
 backward paths, to the tolerances of the single-period tests.
 """
-import os
 import zlib
 
 import numpy as np
@@ -49,16 +48,9 @@ def _w(name, dt, B, H, n, d, k, pi, M, levels, bidir):
                        levels=tuple(levels), seed=seed)
 
 
-def _forced(env, kernel, fn):
-    old = os.environ.get(env)
-    os.environ[env] = kernel
-    try:
+def _forced(which, kernel, fn):
+    with pa.forced_kernels(**{which: kernel}):
         return fn()
-    finally:
-        if old is None:
-            del os.environ[env]
-        else:
-            os.environ[env] = old
 
 
 @pytest.mark.parametrize("case", SCHEDS, ids=[c[0] for c in SCHEDS])
@@ -88,7 +80,7 @@ def test_schedule_fwd_matches_oracle(case, dt, d, kernel):
     x = wl.make_fwd_inputs(w, device=DEV)
     lse = torch.empty_like(x["g"])
     print("schedule fwd %s %s d%d %s" % (name, dt, d, kernel), flush=True)
-    out = _forced("PIATTN_FWD_KERNEL", kernel, lambda: pa.fwd(
+    out = _forced("fwd", kernel, lambda: pa.fwd(
         x["q"], x["k"], x["v"], x["g"], window_k=k, period_pi=pi, num_skips=M, bidirectional=bidir,
         levels=levels, lse=lse))
     torch.cuda.synchronize()
@@ -156,7 +148,7 @@ def test_schedule_bwd_matches_oracle(case, path):
     lse = torch.empty_like(x["g"]) if path == "band" else None
     out = pa.fwd(x["q"], x["k"], x["v"], x["g"], lse=lse, **kw)
     print("schedule bwd %s %s" % (name, path), flush=True)
-    grads = _forced("PIATTN_BWD_KERNEL", path,
+    grads = _forced("bwd", path,
                     lambda: pa.bwd(x["q"], x["k"], x["v"], x["g"], out, dout, lse=lse, **kw))
     torch.cuda.synchronize()
     B, H, n_, d = x["q"].shape

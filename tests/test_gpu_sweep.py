@@ -3,12 +3,11 @@
 Each of 48 forward and 32 backward cases draws a window k, period pi, skip count M, direction, head dim,
 ragged length and (sometimes) a skip schedule of up to three levels, within
 the bounds the library accepts; the prefill runs on every kernel that takes
-the pattern (split, resid, gather; PIATTN_FWD_KERNEL), and the backward on
+the pattern (split, resid, gather; pa.forced_kernels), and the backward on
 both paths.  Tolerances as in the other parity tests: 1e-5 (fp32) / 2e-2
 (bf16) for the forward, 1e-5 / 3e-2 relative to the gradient's scale for
 the backward.
 """
-import os
 
 import numpy as np
 import pytest
@@ -46,16 +45,9 @@ def _case(seed):
                        levels=levels, seed=seed)
 
 
-def _forced(env, kernel, fn):
-    old = os.environ.get(env)
-    os.environ[env] = kernel
-    try:
+def _forced(which, kernel, fn):
+    with pa.forced_kernels(**{which: kernel}):
         return fn()
-    finally:
-        if old is None:
-            del os.environ[env]
-        else:
-            os.environ[env] = old
 
 
 @pytest.mark.parametrize("seed", range(48))
@@ -67,7 +59,7 @@ def test_sweep_fwd_every_kernel(seed):
     for kern in ("split", "resid", "gather"):
         print("sweep fwd seed %d %s: %s" % (seed, kern, w), flush=True)
         try:
-            out = _forced("PIATTN_FWD_KERNEL", kern, lambda: pa.fwd(
+            out = _forced("fwd", kern, lambda: pa.fwd(
                 x["q"], x["k"], x["v"], x["g"], window_k=w.k, period_pi=w.pi, num_skips=w.M,
                 bidirectional=w.bidir, levels=w.levels))
         except pa.PiattnError as e:
@@ -106,7 +98,7 @@ def test_sweep_bwd_both_paths(seed):
     for path in ("band", "gather"):
         print("sweep bwd seed %d %s: %s" % (seed, path, w), flush=True)
         try:
-            grads = _forced("PIATTN_BWD_KERNEL", path, lambda: pa.bwd(
+            grads = _forced("bwd", path, lambda: pa.bwd(
                 x["q"], x["k"], x["v"], x["g"], out, dout, lse=lse if path == "band" else None, **kw))
         except pa.PiattnError as e:
             if e.code == 2 and path == "band":     # fp32 or d = 32
