@@ -133,6 +133,28 @@ int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d,
                size_t workspace_bytes, void *stream);
 
 /*
+ * piattn_fwd_noalloc -- for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): piattn_fwd with the same arguments and results, whose
+ * workspace is a library-held device array of PIATTN_NOALLOC_SCRATCH_BYTES
+ * instead of a caller buffer.  The caller still passes the inputs and the
+ * outputs.  Nothing is allocated by the call: each GPU the library runs on
+ * holds its own copy of the array, zero when first used, until the process
+ * ends; its address is looked up once per device.  A call whose workspace
+ * need (piattn_fwd_workspace_bytes) exceeds the array returns
+ * PIATTN_EWORKSPACE.  Every call on one GPU shares that GPU's array, which
+ * keeps the last call's contents: calls that may overlap on one GPU (on
+ * different streams without ordering, or from several threads) race and
+ * must not be issued.  Returns what piattn_fwd returns.
+ */
+#define PIATTN_NOALLOC_SCRATCH_BYTES (64u << 20)
+int piattn_fwd_noalloc(piattn_dtype dtype, int32_t B, int32_t H, int32_t n,
+                       int32_t d, const void *q, const void *k, const void *v,
+                       const float *gate_logits, void *out, float *lse_out,
+                       const int64_t strides[5][3], const int32_t *cu_seqlens,
+                       const piattn_pattern *pattern, void *stream);
+
+/*
  * Workspace piattn_fwd needs for these sizes and pattern: 8*B*H*n bytes for
  * PIATTN_BF16 with d in {64, 128} when the pattern has skip keys
  * (num_skips_M > window_k / period_pi), else 0.  0 also for invalid

@@ -27,7 +27,9 @@ EXPORTS = ["piattn_fwd", "piattn_fwd_workspace_bytes", "piattn_bwd", "piattn_bwd
            "piattn_decode", "piattn_decode_workspace_bytes",
            "piattn_decode_auto_splits", "piattn_rolling_slots", "piattn_cache_append",
            "piattn_decode_rolling", "piattn_neighbors", "piattn_neighbors_cap",
-           "piattn_last_error", "piattn_version", "piattn_debug_force_kernels"]
+           "piattn_last_error", "piattn_version", "piattn_debug_force_kernels", "piattn_fwd_noalloc"]
+
+NOALLOC_SCRATCH_BYTES = 64 << 20     # PIATTN_NOALLOC_SCRATCH_BYTES
 
 
 class PiattnError(RuntimeError):
@@ -66,6 +68,9 @@ def lib():
         L.piattn_fwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
                                  ctypes.POINTER(Strides), vp, pat, vp, sz, vp]
         L.piattn_fwd.restype = ctypes.c_int
+        L.piattn_fwd_noalloc.argtypes = [ctypes.c_int, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp,
+                                         ctypes.POINTER(Strides), vp, pat, vp]
+        L.piattn_fwd_noalloc.restype = ctypes.c_int
         L.piattn_fwd_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32, pat]
         L.piattn_fwd_workspace_bytes.restype = sz
         L.piattn_bwd.argtypes = [ctypes.c_int, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
@@ -230,6 +235,33 @@ def fwd(q, k, v, g, *, window_k: int, period_pi: int, num_skips: int, bidirectio
     rc = lib().piattn_fwd(code, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out),
                           _ptr(lse), ctypes.byref(strides), cu_ptr, ctypes.byref(pat),
                           _ptr(workspace), wbytes, ctypes.c_void_p(_stream(q.device)))
+    _check(rc)
+    return out
+
+
+def fwd_noalloc(q, k, v, g, *, out, window_k: int, period_pi: int, num_skips: int, bidirectional=False,
+                scale: float = 0.0, cu_seqlens=None, max_seqlen: int | None = None, lse=None, levels=()):
+    """fwd through piattn_fwd_noalloc: the library-held scratch array stands in
+    for the workspace, so the C call allocates nothing; the caller passes
+    out (and lse, if wanted).  Arguments as for fwd."""
+    code = _dtype_code(q)
+    _need_cuda(q, k, v, g, out, lse, cu_seqlens)
+    if k.dtype != q.dtype or v.dtype != q.dtype:
+        raise TypeError("q, k, v must share a dtype")
+    if g.dtype != torch.float32:
+        raise TypeError("gate logits must be float32")
+    if q.numel() == 0 or (cu_seqlens is not None and cu_seqlens.numel() <= 1):
+        return out
+    geo = _prefill_geometry(q, k, v, g, out, cu_seqlens, max_seqlen)
+    if geo is None:
+        return out
+    B, H, n, d, strides, cu_ptr = geo
+    if lse is not None and (lse.shape != g.shape or lse.stride() != g.stride()):
+        raise ValueError("lse must have g's shape and strides")
+    pat = make_pattern(window_k, period_pi, num_skips, bidirectional, scale, levels)
+    rc = lib().piattn_fwd_noalloc(code, B, H, n, d, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(out), _ptr(lse),
+                                  ctypes.byref(strides), cu_ptr, ctypes.byref(pat),
+                                  ctypes.c_void_p(_stream(q.device)))
     _check(rc)
     return out
 

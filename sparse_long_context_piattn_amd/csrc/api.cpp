@@ -167,6 +167,14 @@ int decode_splits_for(int32_t S, int32_t H, const PiPattern& p) {
 
 }  // namespace
 
+int api_fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
 extern "C" {
 
 const char* piattn_last_error(void) { return g_err; }
@@ -282,6 +290,14 @@ static int fwd_args(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t
     a.pat = p;
     a.scale_log2 = scale_log2(pattern, d);
     return PIATTN_OK;
+}
+
+int api_check_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, const void* q, const void* k,
+                  const void* v, const float* gate_logits, void* out, float* lse_out, const int64_t strides[5][3],
+                  const int32_t* cu_seqlens, const piattn_pattern* pattern) {
+    FwdArgs a;
+    PiPattern p;
+    return fwd_args(dtype, B, H, n, d, q, k, v, gate_logits, out, lse_out, strides, cu_seqlens, pattern, a, p);
 }
 
 extern "C" {

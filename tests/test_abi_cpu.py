@@ -288,3 +288,27 @@ def test_debug_force_kernels_ids():
     with pa.forced_kernels(bwd="band"):
         pass
     assert L.piattn_debug_force_kernels(0, 0) == 0
+
+
+def _fwd_noalloc(dtype=1, B=1, H=1, n=64, d=64, q=A, k=A2, v=A3, g=A, out=OUT, pat=None):
+    L = pa.lib()
+    p = pat if pat is not None else pa.make_pattern(4, 16, 2)
+    rc = L.piattn_fwd_noalloc(dtype, B, H, n, d, q, k, v, g, out, None, ctypes.byref(_strides()), None,
+                              ctypes.byref(p), None)
+    return rc, L.piattn_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,expect", [
+    (dict(dtype=7), EINVAL), (dict(n=0), EINVAL), (dict(d=48), EUNSUPPORTED), (dict(q=None), EINVAL),
+    (dict(out=A), EINVAL), (dict(pat=pa.make_pattern(4, 0, 2)), EINVAL),
+])
+def test_fwd_noalloc_validates_before_touching_the_device(kw, expect):
+    rc, msg = _fwd_noalloc(**kw)
+    assert rc == expect and msg
+
+
+def test_fwd_noalloc_refuses_a_workspace_beyond_its_array():
+    # 8 bytes per row on the split path: B H n rows above the array's size
+    n = binding.NOALLOC_SCRATCH_BYTES // (8 * 16) + 64
+    rc, msg = _fwd_noalloc(B=1, H=16, n=n, pat=pa.make_pattern(64, 128, 16))
+    assert rc == EWORKSPACE and "scratch" in msg
