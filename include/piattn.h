@@ -44,8 +44,17 @@
 extern "C" {
 #endif
 
-/* Element type of q, k, v and the output.  Gate logits are always fp32. */
-typedef enum { PIATTN_F32 = 0, PIATTN_BF16 = 1 } piattn_dtype;
+/* Element type of q, k, v and the output.  Gate logits are always fp32.
+ * The two range enumerators only widen the type's range of values to every
+ * int32, so that any value a caller passes is a value of the type; the
+ * entry points accept PIATTN_F32 and PIATTN_BF16 and reject the rest with
+ * PIATTN_EINVAL. */
+typedef enum {
+    PIATTN_F32 = 0,
+    PIATTN_BF16 = 1,
+    PIATTN_DTYPE_RANGE_LO_ = -0x7fffffff - 1,
+    PIATTN_DTYPE_RANGE_HI_ = 0x7fffffff
+} piattn_dtype;
 
 /* Status codes. */
 enum {

@@ -28,6 +28,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "piattn_oracle.c")
 _LIB = os.path.join(_HERE, "liboracle_piattn.so")
+# A prebuilt copy of the same source to load instead (the sanitizer tests
+# build one with AddressSanitizer and UBSan and point this at it).
+_LIB_OVERRIDE = os.environ.get("PIATTN_ORACLE_LIB")
 _lib = None
 
 OR_F64, OR_F32, OR_BF16 = 0, 1, 2
@@ -35,6 +38,8 @@ OR_F64, OR_F32, OR_BF16 = 0, 1, 2
 
 def build(force: bool = False) -> str:
     """Compile the C oracle with gcc (fp64, OpenMP).  Returns the .so path."""
+    if _LIB_OVERRIDE:
+        return _LIB_OVERRIDE
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(
@@ -48,7 +53,7 @@ def _load():
     global _lib
     if _lib is None:
         build()
-        lib = ctypes.CDLL(_LIB)
+        lib = ctypes.CDLL(_LIB_OVERRIDE or _LIB)
         i32, i64, dbl, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
         lib.oracle_neighbors.argtypes = [i32, i32, i32, i32, i32, i32, vp, vp]
         lib.oracle_neighbors.restype = i32

@@ -67,6 +67,7 @@ def _fwd(dtype=1, B=1, H=1, n=64, d=64, q=A, k=A2, v=A3, g=A, out=OUT, lse=None,
 
 @pytest.mark.parametrize("kw,expect", [
     (dict(dtype=7), EINVAL),
+    (dict(dtype=-1), EINVAL),
     (dict(B=0), EINVAL),
     (dict(H=0), EINVAL),
     (dict(n=0), EINVAL),
