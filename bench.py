@@ -29,7 +29,8 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16
 MALL_BYTES = 256 << 20
 KERNEL_SOURCES = ["pattern.hpp", "common.hpp", "gather.hpp", "mfma_util.hpp", "fwd_gather.hip",
-                  "fwd_resid.hip", "fwd_split.hip", "decode.hip", "api.cpp"]
+                  "fwd_resid.hip", "fwd_split.hip", "decode.hip", "api.cpp", "noalloc.hip",
+                  "kernels.hpp", "api_internal.hpp"]
 
 
 def log(*a):

@@ -12,6 +12,7 @@
 
 #include "piattn.h"
 #include "kernels.hpp"
+#include "api_internal.hpp"
 
 namespace {
 

@@ -32,12 +32,3 @@ hipError_t launch_out_proj(int dtype, const ProjArgs& a, hipStream_t stream);
 hipError_t launch_neighbors(int32_t n, const PiPattern& p, int32_t q_begin, int32_t q_count,
                             int32_t cap, int32_t* idx, int8_t* kind, int32_t* count,
                             hipStream_t stream);
-
-// Sets the thread's error string (piattn_last_error) and returns code.
-int api_fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
-
-// piattn_fwd's argument checks alone (no launch): PIATTN_OK or the error.
-#include "piattn.h"
-int api_check_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, const void* q, const void* k,
-                  const void* v, const float* gate_logits, void* out, float* lse_out, const int64_t strides[5][3],
-                  const int32_t* cu_seqlens, const piattn_pattern* pattern);

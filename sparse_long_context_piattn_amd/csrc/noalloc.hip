@@ -14,6 +14,7 @@
 #include <hip/hip_runtime.h>
 
 #include "kernels.hpp"
+#include "api_internal.hpp"
 #include "piattn.h"
 
 namespace {
