@@ -28,8 +28,8 @@ METRIC = "π-attn fwd queries/s + achieved HBM GB/s & MFMA %, n=8192 d=64 bf16, 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16
 MALL_BYTES = 256 << 20
-KERNEL_SOURCES = ["pattern.hpp", "common.hpp", "gather.hpp", "mfma_util.hpp", "fwd_gather.hip",
-                  "fwd_resid.hip", "fwd_split.hip", "decode.hip", "api.cpp", "noalloc.hip",
+KERNEL_SOURCES = ["pattern.hpp", "common.hpp", "gather.hpp", "mfma_util.hpp", "fwd_common.hpp", "fwd_gather.hip",
+                  "fwd_resid.hip", "fwd_split.hip", "fwd_fused.hip", "decode.hip", "api.cpp", "noalloc.hip",
                   "kernels.hpp", "api_internal.hpp"]
 
 
@@ -703,6 +703,8 @@ def main():
                     help="time gate logits + attention + output projection (dense bf16 prefill workloads)")
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (piattn_bwd) instead of the forward (prefill workloads)")
+    ap.add_argument("--kernel", default="auto",
+                    help="prefill kernel to force (auto, fused, split, resid, gather) for comparisons")
     ap.add_argument("--rolling", action="store_true",
                     help="decode over a rolling cache of max(k, M pi) + 1 rows")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -730,6 +732,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     w = wl.WORKLOADS[args.workload]
+    if args.kernel != "auto":
+        pa.binding.lib().piattn_debug_force_kernels(pa.binding.FWD_KERNELS[args.kernel], 0)
+        log("prefill kernel forced: %s" % args.kernel)
     if w.kind == "decode":
         return bench_decode(args, w, dev)
     if args.layer:
@@ -806,7 +811,7 @@ def main():
            "warm_ms_per_step": warm,
            "copy_gbps_measured": round(copy_gbps, 1),
            "frac_of_measured_copy": round(achieved_gbps / copy_gbps, 4),
-           "kernel_digest": kernel_digest(),
+           "kernel_digest": kernel_digest(), "kernel": args.kernel,
            "roofline": roof, "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
 

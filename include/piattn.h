@@ -126,11 +126,12 @@ typedef struct {
  *
  * workspace: device scratch of at least piattn_fwd_workspace_bytes(dtype, B,
  * H, n, d, pattern) bytes, 256-byte aligned; may be NULL when that is 0.
- * The bf16 d = 64 / 128 path splits the work into a skip pass and a window
- * pass and hands one (log-sum-exp, exponent) float pair per row from the
- * first to the second through it.  Calls that share a workspace must be
- * ordered (the same stream, or synchronised); its contents are scratch
- * before and after a call.
+ * The bf16 d = 64 / 128 paths split each row's softmax into a skip part and
+ * a window part and hand one (log-sum-exp, exponent) float pair per row from
+ * the first to the second through it; the fused path also keeps the
+ * counters of its work schedule there (zeroed by the call itself).  Calls
+ * that share a workspace must be ordered (the same stream, or
+ * synchronised); its contents are scratch before and after a call.
  * Returns PIATTN_OK, PIATTN_EINVAL, PIATTN_EUNSUPPORTED, PIATTN_EWORKSPACE
  * (workspace NULL or too small) or PIATTN_EHIP.
  */
@@ -164,10 +165,12 @@ int piattn_fwd_noalloc(piattn_dtype dtype, int32_t B, int32_t H, int32_t n,
                        const piattn_pattern *pattern, void *stream);
 
 /*
- * Workspace piattn_fwd needs for these sizes and pattern: 8*B*H*n bytes for
- * PIATTN_BF16 with d in {64, 128} when the pattern has skip keys
- * (num_skips_M > window_k / period_pi), else 0.  0 also for invalid
- * arguments (piattn_fwd reports those).
+ * Workspace piattn_fwd needs for these sizes and pattern: for PIATTN_BF16
+ * with d in {64, 128} when the pattern has skip keys (num_skips_M >
+ * window_k / period_pi), 8*B*H*n bytes rounded up to a multiple of 256, plus
+ * 128*(9 + B*H*ceil(ceil(n/pi)/16)) bytes of schedule counters (one 128-byte
+ * line each; pi: the period, or the periods' gcd of a skip schedule); else
+ * 0.  0 also for invalid arguments (piattn_fwd reports those).
  */
 size_t piattn_fwd_workspace_bytes(piattn_dtype dtype, int32_t B, int32_t H,
                                   int32_t n, int32_t d,
@@ -380,7 +383,8 @@ enum {
     PIATTN_FWD_SPLIT = 1,   /* skip pass + window pass (bf16, d 64 / 128) */
     PIATTN_FWD_RESID = 2,   /* residue-tiled single kernel (bf16, d 64) */
     PIATTN_FWD_GATHER = 3,  /* one wave per row (any dtype and d) */
-    PIATTN_FWD_LAST = PIATTN_FWD_GATHER,
+    PIATTN_FWD_FUSED = 4,   /* skip and window work items in one kernel (bf16, d 64 / 128) */
+    PIATTN_FWD_LAST = PIATTN_FWD_FUSED,
     PIATTN_BWD_BAND = 1,    /* MFMA band kernels (bf16, d 64 / 128, lse given) */
     PIATTN_BWD_GATHER = 2   /* gather kernels (any dtype and d) */
 };

@@ -33,102 +33,15 @@
 // and masked.  Row data leaves (and the partial re-enters) through LDS as
 // whole rows: 16 bytes per lane, a row from neighbouring lanes, rather than
 // the MFMA layout's 8 bytes of each of 16 rows per instruction.
-#include "kernels.hpp"
-#include "mfma_util.hpp"
+#include "fwd_common.hpp"
 
 #include <type_traits>
 
 namespace {
 
-constexpr int32_t EMPTY = 0x40000000;   // lower bound of an empty key range
-
-template <int D>
-struct Geo {
-    static constexpr int DC = D / 32;    // QK^T depth chunks (16x16x32)
-    static constexpr int DB = D / 16;    // O^T row blocks
-    static constexpr int CH = D / 8;     // 16-byte chunks per row
-    static constexpr int RPI = 64 / CH;  // rows covered by one 64-lane 16-byte load
-};
-
-// Same, swizzled by (r / 2) % 8: the 16 rows of a K-operand read then fall
-// on distinct banks when a row is 128 bytes.
-template <int D>
-__device__ __forceinline__ int swu(int r, int c) { return r * D + ((c ^ ((r >> 1) & 7)) << 3); }
-
-// Whether key period kp is a skip key of query period tq under a skip
-// schedule's mask of multiples (masked patterns only).
-template <bool BIDIR>
-__device__ __forceinline__ bool in_schedule(const PiPattern& p, int32_t tq, int32_t kp) {
-    return mask_has(p, BIDIR ? abs(tq - kp) : tq - kp);
-}
-
-// Whether row (residue a, period t) with pr periods in its residue has any
-// skip key.
-template <bool BIDIR>
-__device__ __forceinline__ bool row_has_skip(int32_t t, int32_t pr, int32_t mlo, int32_t M) {
-    return M >= mlo && (t >= mlo || (BIDIR && t + mlo < pr));
-}
-
-// Skip partial of one row, handed from the skip pass to the window pass.
-// The normalised O_s goes into the row's output slots as fp16 scaled by
-// 2^-e, e chosen from the row's largest magnitude m so that m 2^-e lies in
-// [2^14, 2^15): no overflow, full fp16 precision (4x that of bf16, so the
-// merge adds well under a quarter ulp of the final bf16 rounding).  Its
-// log2-sum-exp and e go into the row's two-float record of the workspace.
-typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
-typedef float f32x2_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t cvt_pk_f16(float lo, float hi) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){lo, hi}, f16x2_t));
-}
-__device__ __forceinline__ float f16lo(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[0]; }
-__device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit_cast(f16x2_t, w)[1]; }
-
-// One wave's chunk of the skip partial -- query periods 16c .. 16c+15 of
-// residue res -- goes through the free LDS tile tt (16 D elements) so that
-// every store instruction writes whole rows: the lanes write their MFMA
-// layout (lane (x, g) holds d = 16 bb + 4 g + 0..3 of row x), then read back
-// 16 bytes each, a row's 2D bytes from 2D/16 neighbouring lanes.  Rows past
-// the residue or without skip keys are not stored; hs says whether row x has
-// skip keys (its record (lse2, e) is written then).
-template <int D, bool BIDIR>
-__device__ __forceinline__ void store_skip_chunk(uint16_t* tt, const f32x4_t (&sacc)[D / 16], float sl, float sm,
-                                                 bool hs, int32_t c, int32_t res, int32_t pr, int32_t pi,
-                                                 int32_t mlo, int32_t M, uint16_t* Ob, int64_t sot, float* Ls,
-                                                 int lane) {
-    constexpr int DB = D / 16;
-    const int x = lane & 15, g = lane >> 4;
-    const float inv = 1.0f / sl;
-    float mloc = 0.0f;
-#pragma unroll
-    for (int bb = 0; bb < DB; ++bb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) mloc = fmax_ieee(mloc, fabsf(sacc[bb][r]));
-    const float m = max4(mloc) * inv;
-    const int32_t ex = (int32_t)((__float_as_uint(m) >> 23) & 0xff);   // m < 2^(ex - 126)
-    const int32_t e = imax32(-64, ex - 141);                           // m * 2^-e in [2^14, 2^15)
-    const float sc = __builtin_amdgcn_ldexpf(inv, -e);
-#pragma unroll
-    for (int bb = 0; bb < DB; ++bb) {
-        uint2 w;
-        w.x = cvt_pk_f16(sacc[bb][0] * sc, sacc[bb][1] * sc);
-        w.y = cvt_pk_f16(sacc[bb][2] * sc, sacc[bb][3] * sc);
-        *reinterpret_cast<uint2*>(tt + swr<D>(x, 2 * bb + (g >> 1)) + 4 * (g & 1)) = w;
-    }
-    if (hs && g == 0)
-        *reinterpret_cast<f32x2_t*>(Ls + 2 * (res + (16 * c + x) * pi)) = f32x2_t{sm + __log2f(sl), (float)e};
-#pragma unroll
-    for (int j = 0; j < 32 * D / 1024; ++j) {
-        const int o = 1024 * j + 16 * lane;               // byte offset in the [16][D] fp16 tile
-        const int r = o / (2 * D), cc = (o % (2 * D)) / 16;
-        const uint4 val = *reinterpret_cast<const uint4*>(tt + swr<D>(r, cc));
-        const int32_t tr = 16 * c + r;
-        if (tr < pr && row_has_skip<BIDIR>(tr, pr, mlo, M))
-            *reinterpret_cast<uint4*>(Ob + (int64_t)(res + tr * pi) * sot + 8 * cc) = val;
-    }
-}
+using namespace fwdk;
 
 // ================================================================= skip pass
-constexpr int SW = 4;                    // waves per skip workgroup (one residue each)
 
 template <int D>
 struct SkipGeo {
@@ -528,304 +441,18 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
 
 // =============================================================== window pass
 
-// Window-pass shape: WW waves of 16 query rows (a 64-row tile), KT key rows
-// per LDS slot.  Small workgroups with small slots keep several tiles in
-// flight per CU, each at a different point of its load / compute cycle:
-// 24 KB of LDS at d = 64 (four workgroups per CU, the register budget set
-// for four waves per SIMD), 48 KB at d = 128 (three per CU).  A 128-row
-// tile with 64-key slots, which halves the halo re-reads, measured slower
-// at both head dims: 97 KB of LDS at d = 128 allow one workgroup per CU,
-// whose loads then stall at every tile start.
-template <int D>
-struct WinShape {
-    static constexpr int WW = 4;
-    static constexpr int KT = 32;
-    static constexpr int QTW = 16 * WW;
-    static constexpr int EU = D == 64 ? 4 : 3;           // waves per SIMD the register budget must allow
-};
-
 template <int D, bool BIDIR>
 __global__ __launch_bounds__(WinShape<D>::WW * 64, WinShape<D>::EU) void fwd_window_kernel(FwdArgs a, const float* lse_s,
                                                                         int32_t q_tiles, int32_t total,
                                                                         int32_t merge) {
-    using G = Geo<D>;
-    constexpr int DC = G::DC, DB = G::DB, CH = G::CH, RPI = G::RPI;
-    constexpr int WW = WinShape<D>::WW, KT = WinShape<D>::KT, QT = WinShape<D>::QTW, NB = KT / 16;
-    constexpr int LPW = KT / RPI / (WW / 2);            // loads per wave per slot (first half K, second V)
-    static_assert(KT % (RPI * (WW / 2)) == 0, "slot split");
-    static_assert(2 * KT == QT, "query rows are staged through one slot pair");
-    static_assert(NB % 2 == 0, "PV runs on pairs of 16-key blocks");
-    __shared__ __attribute__((aligned(16))) uint16_t k0s[KT * D];
-    __shared__ __attribute__((aligned(16))) uint16_t k1s[KT * D];
-    __shared__ __attribute__((aligned(16))) uint16_t k2s[KT * D];
-    __shared__ __attribute__((aligned(16))) uint16_t v0s[KT * D];
-    __shared__ __attribute__((aligned(16))) uint16_t v1s[KT * D];
-    __shared__ __attribute__((aligned(16))) uint16_t v2s[KT * D];
-    __shared__ __attribute__((aligned(16))) float gls[QT];
-
+    __shared__ __attribute__((aligned(16))) uint16_t lds[WinShape<D>::LDS / 2];
     // Tiles in the reverse of the skip pass's order: the window pass starts
     // on the heads the skip pass touched last, whose q, k, v and partials
     // the memory-side cache still holds.
     const int32_t logical = total - 1 - xcd_logical(blockIdx.x, total);
     const int32_t qt = logical % q_tiles;
     const int32_t rest = logical / q_tiles;
-    const int32_t h = rest % a.H, b = rest / a.H;
-    int32_t n = a.n;
-    int64_t tok0 = 0;
-    if (a.cu) {
-        varlen_seq(a.cu, b, a.n, &tok0, &n);
-    }
-    const int32_t q0 = qt * QT;
-    if (q0 >= n) return;                                // workgroup-uniform
-    const int tid = threadIdx.x;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int lane = tid & 63, x = lane & 15, g = lane >> 4;
-    const int32_t pi = a.pat.pi, kw = a.pat.k, M = a.pat.M, mlo = a.pat.mlo;
-
-    const int64_t bq = a.cu ? 0 : (int64_t)b;
-    const uint16_t* Qb = static_cast<const uint16_t*>(a.q) + bq * a.sq.s + h * a.sq.h + tok0 * a.sq.t;
-    const uint16_t* Kb = static_cast<const uint16_t*>(a.k) + bq * a.sk.s + h * a.sk.h + tok0 * a.sk.t;
-    const uint16_t* Vb = static_cast<const uint16_t*>(a.v) + bq * a.sv.s + h * a.sv.h + tok0 * a.sv.t;
-    uint16_t* Ob = static_cast<uint16_t*>(a.o) + bq * a.so.s + h * a.so.h + tok0 * a.so.t;
-    const float* Gb = a.g + bq * a.sg.s + h * a.sg.h + tok0 * a.sg.t;
-    const float* Ls = lse_s ? lse_s + ((int64_t)b * a.H + h) * a.n * 2 : nullptr;
-
-    const int32_t klo = imax32(0, q0 - kw);
-    const int32_t khi = imin32(n - 1, q0 + QT - 1 + (BIDIR ? kw : 0));
-    const int32_t ntiles = (khi - klo) / KT + 1;
-
-    // ---- staging: slot rows r0 .. r0+RPI-1 per load; lane row r0 + lane/CH,
-    // physical chunk lane%CH = logical chunk (lane%CH) ^ (row%8)
-    const bool isv = wave >= WW / 2;
-    const uint16_t* src0 = isv ? Vb : Kb;
-    const int32_t st = isv ? (int32_t)a.sv.t : (int32_t)a.sk.t;
-    auto stage_rows = [&](const uint16_t* src, int32_t stt, int32_t s0, int r0, uint16_t* dst) __attribute__((always_inline)) {
-        const int rl = r0 + lane / CH;
-        const int lc = ((lane % CH) ^ (rl & 7)) << 3;
-        const bool inside = s0 >= 0 && s0 + RPI - 1 < n;
-        const uint16_t* ub = inside ? src + (int64_t)s0 * stt : src;
-        const uint32_t off = inside ? (uint32_t)((lane / CH) * stt + lc)
-                                    : (uint32_t)(imin32(imax32(s0 + lane / CH, 0), n - 1) * stt + lc);
-        dma16(ub, off * 2u, lds_addr(dst + r0 * D));
-    };
-    // Stage t < ntiles: key tile t.  Stage ntiles, when skip partials are
-    // merged: the tile's fp16 skip partial rows, each wave its own 16 rows
-    // (the layout of the query rows: rows 0..KT-1 in the K array, the rest
-    // in the V array).  Later stages: a harmless reload of the last key
-    // tile, which keeps every wave's count of loads in flight uniform.
-    auto issue = [&](uint16_t* Ks, uint16_t* Vs, int32_t t) __attribute__((always_inline)) {
-        if (merge && t == ntiles) {
-#pragma unroll
-            for (int j = 0; j < LPW; ++j) {
-                const int r0 = ((wave % (WW / 2)) * LPW + j) * RPI;
-                stage_rows(Ob, (int32_t)a.so.t, q0 + (isv ? KT : 0) + r0, r0, isv ? Vs : Ks);
-            }
-            return;
-        }
-        t = imin32(t, ntiles - 1);
-#pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-            const int r0 = ((wave % (WW / 2)) * LPW + j) * RPI;
-            stage_rows(src0, st, klo + t * KT + r0, r0, isv ? Vs : Ks);
-        }
-    };
-
-    // ---- prologue: key tiles 0 and 1, the 128 query rows through slot 2
-    // (rows 0-63 in k2s, 64-127 in v2s) and the gate logits
-    issue(k0s, v0s, 0);
-    {
-#pragma unroll
-        for (int j = 0; j < LPW; ++j) {
-            const int r0 = ((wave % (WW / 2)) * LPW + j) * RPI;
-            stage_rows(Qb, (int32_t)a.sq.t, q0 + (isv ? KT : 0) + r0, r0, isv ? v2s : k2s);
-        }
-        if (wave == 0) {
-#pragma unroll
-            for (int j = 0; j < QT / 64; ++j) {
-                const int32_t rr = imin32(q0 + 64 * j + lane, n - 1);
-                dma4(Gb, (uint32_t)(rr * (int32_t)a.sg.t) * 4u, lds_addr(gls + 64 * j));
-            }
-        }
-    }
-    issue(k1s, v1s, 1);
-
-    const float sl2 = a.scale_log2;
-    const int tr_row = 4 * g + (x >> 2);
-    const int tr_col = 4 * (x & 3);
-    const bf16x8_t ones8 = __builtin_bit_cast(bf16x8_t, make_uint4(0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u));
-    const s16x4_t ones4 = __builtin_bit_cast(s16x4_t, make_uint2(0x3f803f80u, 0x3f803f80u));
-
-    // ---- the lane's query row
-    const int32_t i = q0 + 16 * wave + x;
-    const bool qv = i < n;
-    const int32_t ic = qv ? i : n - 1;
-    const int32_t ti = ic / pi, ai = ic - ti * pi;
-    const int32_t pr = (n - 1 - ai) / pi + 1;
-    const bool hs = row_has_skip<BIDIR>(ti, pr, mlo, M);
-    const int32_t lo = qv ? imax32(0, i - kw) : EMPTY;
-    const uint32_t span = qv ? (uint32_t)(imin32(n - 1, BIDIR ? i + kw : i) - lo) : 0u;
-    const int32_t w0 = q0 + 16 * wave;                  // the wave's key span
-    const int32_t wlo = imax32(0, w0 - kw);
-    const int32_t whi = w0 < n ? imin32(n - 1, imin32(w0 + 15, n - 1) + (BIDIR ? kw : 0)) : -1;
-
-    // wait for tile 0, the query rows and the gates (tile 1 may be in flight)
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPW));
-    lds_barrier();
-    bf16x8_t qf[DC];
-    float pl, ps;
-    {
-        const int qr = 16 * wave + x;                   // slot 2 holds rows 0..KT-1 in K, the rest in V
-        const uint16_t* qsrc = qr < KT ? k2s : v2s;
-        const int rr = qr & (KT - 1);
-#pragma unroll
-        for (int c = 0; c < DC; ++c) qf[c] = *reinterpret_cast<const bf16x8_t*>(qsrc + swr<D>(rr, 4 * c + g));
-        gate_priors(gls[qr], hs, &pl, &ps);
-    }
-    lds_barrier();                                       // slot 2 is free for tile 2
-
-    // the record of the lane's row (written by the skip pass), loaded now so
-    // that its latency hides behind the window loop
-    const bool mg = merge && hs && qv;
-    f32x2_t rec = {0.0f, 0.0f};                          // (log2-sum-exp, e)
-    if (mg) rec = *reinterpret_cast<const f32x2_t*>(Ls + 2 * ic);
-
-    f32x4_t acc[DB];
-#pragma unroll
-    for (int bb = 0; bb < DB; ++bb) acc[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float mrun = -INFINITY, lrun = 0.0f, mL = -INFINITY, cst = pl;
-
-    auto compute = [&](int32_t t, const uint16_t* Ks, const uint16_t* Vs) __attribute__((always_inline)) {
-        const int32_t kt0 = klo + t * KT;
-        if (kt0 > whi || kt0 + KT - 1 < wlo) return;    // wave-uniform
-        float sc[NB][4];
-        bool act[NB];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int u = 0; u < NB; ++u) {
-            const int32_t kb0 = kt0 + 16 * u;
-            act[u] = kb0 <= whi && kb0 + 15 >= wlo;     // wave-uniform
-#pragma unroll
-            for (int r = 0; r < 4; ++r) sc[u][r] = -INFINITY;
-            if (act[u]) {
-                f32x4_t s4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < DC; ++c) {
-                    const bf16x8_t kk = *reinterpret_cast<const bf16x8_t*>(Ks + swr<D>(16 * u + x, 4 * c + g));
-                    s4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kk, qf[c], s4, 0, 0, 0);
-                }
-                const int32_t rel = kb0 + 4 * g - lo;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) sc[u][r] = (uint32_t)(rel + r) <= span ? s4[r] : -INFINITY;
-                mx = fmax_ieee(mx, fmax_ieee(fmax_ieee(sc[u][0], sc[u][1]), fmax_ieee(sc[u][2], sc[u][3])));
-            }
-        }
-        mx = fmaf(max4(mx), sl2, pl);
-        if (__builtin_amdgcn_ballot_w64(mx > mL)) {
-            const float mnew = fmax_ieee(mrun, mx);
-            const float mu = mnew == -INFINITY ? 0.0f : mnew;
-            const float fac = exp2_fast(mrun - mu);
-#pragma unroll
-            for (int bb = 0; bb < DB; ++bb) acc[bb] *= fac;
-            lrun *= fac;
-            mrun = mnew;
-            mL = mnew + LAZY;
-            cst = pl - mu;
-        }
-        s16x4_t pb[NB];
-#pragma unroll
-        for (int u = 0; u < NB; ++u) {
-            const uint32_t w0 = cvt_pk_bf16(exp2_fast(fmaf(sc[u][0], sl2, cst)), exp2_fast(fmaf(sc[u][1], sl2, cst)));
-            const uint32_t w1 = cvt_pk_bf16(exp2_fast(fmaf(sc[u][2], sl2, cst)), exp2_fast(fmaf(sc[u][3], sl2, cst)));
-            pb[u] = __builtin_bit_cast(s16x4_t, make_uint2(w0, w1));
-        }
-        f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < NB; u += 2) {
-            if (!act[u] && !act[u + 1]) continue;
-            const bf16x8_t pp =
-                __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(pb[u], pb[u + 1], 0, 1, 2, 3, 4, 5, 6, 7));
-            lsum = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones8, pp, lsum, 0, 0, 0);
-#pragma unroll
-            for (int bb = 0; bb < DB; ++bb) {
-                const s16x4_t v0 = ld_tr16(Vs + swr<D>(16 * u + tr_row, 2 * bb + (tr_col >> 3)) + (tr_col & 7));
-                const s16x4_t v1 = ld_tr16(Vs + swr<D>(16 * u + 16 + tr_row, 2 * bb + (tr_col >> 3)) + (tr_col & 7));
-                const bf16x8_t va = __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7));
-                acc[bb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pp, acc[bb], 0, 0, 0);
-            }
-        }
-        lrun += 0.25f * lsum[0];                        // quarter per lane; sum4 restores the row sum
-    };
-    // Epilogue, with the slot of stage ntiles (P):
-    // the window partial, merged with the skip partial (read from P) when
-    // the row has skip keys (its lse gets the log(1-alpha) prior here); the
-    // bf16 rows then go back through the wave's own rows of P so that each
-    // store instruction writes whole rows.
-    auto epilogue = [&](uint16_t* Kp, uint16_t* Vp) __attribute__((always_inline)) {
-        // stage ntiles landed (stage ntiles+1 may be in flight); the
-        // barrier also lets every wave's reload into P land when P holds no
-        // partials
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPW));
-        lds_barrier();
-        uint16_t* prow = (16 * wave < KT ? Kp : Vp);
-        const int qr = 16 * wave + x, rr = qr & (KT - 1), rr0 = (16 * wave) & (KT - 1);
-        const float ltot = sum4(lrun);
-        const float lw = mrun + __log2f(ltot);          // log2-sum-exp of the window part
-        float fw = 1.0f / ltot, fs = 0.0f, lfin = lw;
-        uint2 os[DB];
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) os[bb] = make_uint2(0, 0);
-        if (mg) {
-#pragma unroll
-            for (int bb = 0; bb < DB; ++bb)
-                os[bb] = *reinterpret_cast<const uint2*>(prow + swr<D>(rr, 2 * bb + (g >> 1)) + 4 * (g & 1));
-            const float lsk = rec[0] + ps;
-            const float mx = fmaxf(lw, lsk);
-            const float aw = exp2_fast(lw - mx), as = exp2_fast(lsk - mx);
-            const float inv = 1.0f / (aw + as);
-            fw = ltot > 0.0f ? aw * inv / ltot : 0.0f; // alpha = 0: the window part is empty
-            fs = __builtin_amdgcn_ldexpf(as * inv, (int)rec[1]);   // undo the fp16 scaling
-            lfin = mx + __log2f(aw + as);
-        }
-#pragma unroll
-        for (int bb = 0; bb < DB; ++bb) {
-            uint2 w;
-            w.x = cvt_pk_bf16(fmaf(acc[bb][0], fw, f16lo(os[bb].x) * fs), fmaf(acc[bb][1], fw, f16hi(os[bb].x) * fs));
-            w.y = cvt_pk_bf16(fmaf(acc[bb][2], fw, f16lo(os[bb].y) * fs), fmaf(acc[bb][3], fw, f16hi(os[bb].y) * fs));
-            *reinterpret_cast<uint2*>(prow + swr<D>(rr, 2 * bb + (g >> 1)) + 4 * (g & 1)) = w;
-        }
-        if (a.lse && qv && g == 0) a.lse[bq * a.sg.s + h * a.sg.h + (tok0 + i) * a.sg.t] = lfin * PIATTN_LN2;
-#pragma unroll
-        for (int j = 0; j < 32 * D / 1024; ++j) {
-            const int o = 1024 * j + 16 * lane;           // byte offset in the wave's [16][D] bf16 rows
-            const int r = o / (2 * D), cc = (o % (2 * D)) / 16;
-            const uint4 val = *reinterpret_cast<const uint4*>(prow + swr<D>(rr0 + r, cc));
-            const int32_t row = q0 + 16 * wave + r;
-            if (row < n) *reinterpret_cast<uint4*>(Ob + (int64_t)row * a.so.t + 8 * cc) = val;
-        }
-    };
-    // step t: wait for this wave's loads of tile t (tile t+1 may be in
-    // flight), barrier (everyone's tile t landed, tile t-1 fully read), issue
-    // stage t+2 into the slot of tile t-1, compute tile t
-    auto step = [&](int32_t t, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn)
-        __attribute__((always_inline)) {
-        if (t > 0) {
-            __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPW));
-            lds_barrier();
-        }
-        issue(Kn, Vn, t + 2);
-        compute(t, Kc, Vc);
-    };
-    for (int32_t t = 0; t < ntiles; t += 3) {
-        step(t, k0s, v0s, k2s, v2s);
-        if (t + 1 >= ntiles) break;
-        step(t + 1, k1s, v1s, k0s, v0s);
-        if (t + 2 >= ntiles) break;
-        step(t + 2, k2s, v2s, k1s, v1s);
-    }
-    // stage ntiles went to slot ntiles % 3
-    const int pslot = ntiles % 3;
-    epilogue(pslot == 0 ? k0s : pslot == 1 ? k1s : k2s, pslot == 0 ? v0s : pslot == 1 ? v1s : v2s);
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));         // loads past the end land before the LDS retires
+    window_tile<D, BIDIR, false>(a, lse_s, merge, qt, rest % a.H, rest / a.H, lds, SegWait{});
 }
 
 // lse_s: the caller's workspace of B*H*n (log2-sum-exp, e) float pairs, or

@@ -18,7 +18,7 @@ import pytest
 
 CSRC = os.path.join(os.path.dirname(__file__), "..", "sparse_long_context_piattn_amd", "csrc")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-SOURCES = ["fwd_split.hip", "fwd_resid.hip", "decode.hip", "bwd_band.hip", "proj.hip"]
+SOURCES = ["fwd_split.hip", "fwd_fused.hip", "fwd_resid.hip", "decode.hip", "bwd_band.hip", "proj.hip"]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="needs hipcc")
 
@@ -52,7 +52,7 @@ def scan(asm_text):
     for i, (fn, line) in enumerate(ins):
         if not line.startswith("global_load_lds"):
             continue
-        base = _sregs(line.split(None, 1)[1].split(",")[1].strip())
+        base = _sregs(line.split(None, 1)[1].split(",")[1].split()[0])   # "s[2:3]" before any cache bits
         waited = 0
         for j in range(i - 1, max(-1, i - 8), -1):
             prev = ins[j][1]
@@ -86,6 +86,8 @@ def test_scanner_flags_a_short_distance():
     good = "\n".join(["_Zk:", "v_readfirstlane_b32 s2, v8", "s_cselect_b32 m0, s8, -1", "s_nop 4",
                       "global_load_lds_dwordx4 v7, s[2:3]"])
     assert scan(good) == []
+    bad_sc1 = "\n".join(["_Zk:", "v_readfirstlane_b32 s3, v8", "global_load_lds_dwordx4 v7, s[2:3] sc1"])
+    assert scan(bad_sc1)
 
 
 def test_lds_direct_loads_have_their_wait_states(tmp_path):
