@@ -29,7 +29,7 @@ HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16
 MALL_BYTES = 256 << 20
 KERNEL_SOURCES = ["pattern.hpp", "common.hpp", "gather.hpp", "mfma_util.hpp", "fwd_common.hpp", "fwd_gather.hip",
-                  "fwd_resid.hip", "fwd_split.hip", "fwd_fused.hip", "decode.hip", "api.cpp", "noalloc.hip",
+                  "fwd_resid.hip", "fwd_split.hip", "decode.hip", "api.cpp", "noalloc.hip",
                   "kernels.hpp", "api_internal.hpp"]
 
 
@@ -704,7 +704,7 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (piattn_bwd) instead of the forward (prefill workloads)")
     ap.add_argument("--kernel", default="auto",
-                    help="prefill kernel to force (auto, fused, split, resid, gather) for comparisons")
+                    help="prefill kernel to force (auto, split, resid, gather) for comparisons")
     ap.add_argument("--rolling", action="store_true",
                     help="decode over a rolling cache of max(k, M pi) + 1 rows")
     ap.add_argument("--calibrate-copy", action="store_true",

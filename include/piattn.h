@@ -126,12 +126,11 @@ typedef struct {
  *
  * workspace: device scratch of at least piattn_fwd_workspace_bytes(dtype, B,
  * H, n, d, pattern) bytes, 256-byte aligned; may be NULL when that is 0.
- * The bf16 d = 64 / 128 paths split each row's softmax into a skip part and
- * a window part and hand one (log-sum-exp, exponent) float pair per row from
- * the first to the second through it; the fused path also keeps the
- * counters of its work schedule there (zeroed by the call itself).  Calls
- * that share a workspace must be ordered (the same stream, or
- * synchronised); its contents are scratch before and after a call.
+ * The bf16 d = 64 / 128 path splits the work into a skip pass and a window
+ * pass and hands one (log-sum-exp, exponent) float pair per row from the
+ * first to the second through it.  Calls that share a workspace must be
+ * ordered (the same stream, or synchronised); its contents are scratch
+ * before and after a call.
  * Returns PIATTN_OK, PIATTN_EINVAL, PIATTN_EUNSUPPORTED, PIATTN_EWORKSPACE
  * (workspace NULL or too small) or PIATTN_EHIP.
  */
@@ -383,8 +382,7 @@ enum {
     PIATTN_FWD_SPLIT = 1,   /* skip pass + window pass (bf16, d 64 / 128) */
     PIATTN_FWD_RESID = 2,   /* residue-tiled single kernel (bf16, d 64) */
     PIATTN_FWD_GATHER = 3,  /* one wave per row (any dtype and d) */
-    PIATTN_FWD_FUSED = 4,   /* skip and window work items in one kernel (bf16, d 64 / 128) */
-    PIATTN_FWD_LAST = PIATTN_FWD_FUSED,
+    PIATTN_FWD_LAST = PIATTN_FWD_GATHER,
     PIATTN_BWD_BAND = 1,    /* MFMA band kernels (bf16, d 64 / 128, lse given) */
     PIATTN_BWD_GATHER = 2   /* gather kernels (any dtype and d) */
 };

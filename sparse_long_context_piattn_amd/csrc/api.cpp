@@ -221,19 +221,13 @@ int piattn_neighbors(int32_t n, const piattn_pattern* pattern, int32_t q_begin, 
                                           static_cast<hipStream_t>(stream)));
 }
 
-// Workspace of the split and fused prefill paths: one (log2-sum-exp,
-// exponent) float pair per row, written by the skip work and read by the
-// window work; the fused path adds its schedule counters after them (queue
-// tickets, an error word, one counter per 16-period segment of each
-// (sequence, head)).  Only bf16 at d = 64 / 128 with a non-empty skip set
-// takes those paths.
+// Workspace of the split prefill path: one (log2-sum-exp, exponent) float
+// pair per row, written by its skip pass and read by its window pass.  Only
+// bf16 at d = 64 / 128 with a non-empty skip set can take that path.
 static size_t fwd_split_workspace(int dtype, int32_t B, int32_t H, int32_t n, int32_t d, const PiPattern& p) {
     if (dtype != PIATTN_BF16 || (d != 64 && d != 128)) return 0;
     if (p.M < p.mlo) return 0;
-    const size_t records = ((size_t)B * H * n * 2 * sizeof(float) + 255) / 256 * 256;
-    const size_t periods = ((size_t)n + p.pi - 1) / p.pi;
-    const size_t segments = (periods + 15) / 16;
-    return records + (9 + (size_t)B * H * segments) * 32 * sizeof(int32_t);   // a 128-byte line per counter
+    return (size_t)B * H * n * 2 * sizeof(float);
 }
 
 size_t piattn_fwd_workspace_bytes(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d,
@@ -323,7 +317,7 @@ int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
     // Kernel choice: the first kernel that can take the call, unless
     // piattn_debug_force_kernels forced one (EUNSUPPORTED if it cannot).
     // The split path checks the workspace first (the other kernels take none).
-    auto split = [&](bool fused) -> int {
+    auto split = [&]() -> int {
         const size_t need = fwd_split_workspace(dtype, B, H, n, d, p);
         if (need) {
             if (!workspace) return fail(PIATTN_EWORKSPACE, "workspace is NULL (%zu bytes needed)", need);
@@ -332,17 +326,16 @@ int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
             if (!aligned(workspace, 256)) return fail(PIATTN_EINVAL, "workspace is not 256-byte aligned");
         }
         float* ws = need ? static_cast<float*>(workspace) : nullptr;
-        return launch_status(fused ? launch_fwd_fused(a, ws, st) : launch_fwd_split(a, ws, st));
+        return launch_status(launch_fwd_split(a, ws, st));
     };
     const int32_t force = g_force_fwd.load(std::memory_order_relaxed);
     if (force != PIATTN_KERNEL_AUTO) {
         if (force == PIATTN_FWD_RESID && fwd_resid_supported(dt, a)) return launch_status(launch_fwd_resid(a, st));
-        if (force == PIATTN_FWD_SPLIT && fwd_split_supported(dt, a)) return split(false);
-        if (force == PIATTN_FWD_FUSED && fwd_fused_supported(dt, a)) return split(true);
+        if (force == PIATTN_FWD_SPLIT && fwd_split_supported(dt, a)) return split();
         if (force == PIATTN_FWD_GATHER) return launch_status(launch_fwd_gather(dt, a, st));
         return fail(PIATTN_EUNSUPPORTED, "the forced prefill kernel (%d) cannot take this call", force);
     }
-    if (fwd_split_supported(dt, a)) return split(false);
+    if (fwd_split_supported(dt, a)) return split();
     if (fwd_resid_supported(dt, a)) return launch_status(launch_fwd_resid(a, st));
     return launch_status(launch_fwd_gather(dt, a, st));
 }

@@ -1,13 +1,13 @@
-// fwd_common.hpp -- pieces shared by the split prefill (skip pass, then
-// window pass) and the fused prefill (skip and window work items in one
-// kernel): geometry, the skip-partial hand-off format, the band tests of the
-// residue layout, and the window tile.
+// fwd_common.hpp -- pieces of the split prefill (skip pass, then window
+// pass): geometry, the skip-partial hand-off format, the band tests of the
+// residue layout, and the window tile (a device function the window pass
+// runs once per workgroup).
 //
 // Skip partial hand-off.  Row i's skip part (its keys i -/+ m*pi) is a
 // normalised partial output O_s and its log2-sum-exp; it travels from the
-// skip work to the window work in the row's output slots (fp16, scaled by a
+// skip pass to the window pass in the row's output slots (fp16, scaled by a
 // per-row power of two) and a two-float record per row in the workspace.
-// The window work merges it with the window part (one softmax over the
+// The window pass merges it with the window part (one softmax over the
 // union: the partials' log-sum-exp weights, the gate prior log(1 - alpha)
 // added to the skip part's).
 #pragma once
@@ -108,82 +108,6 @@ __device__ __forceinline__ void store_skip_chunk(uint16_t* tt, const f32x4_t (&s
 // Waves per skip workgroup (one residue each).
 constexpr int SW = 4;
 
-// What a window tile of the fused kernel waits for before it reads its
-// rows' skip partials: the completion counters of the segments that hold its
-// rows (one increment per skip wave).
-struct SegWait {
-    int32_t* cnt;        // counters of this (sequence, head), one per segment
-    int32_t seg_lo, seg_hi;
-    int32_t target;      // increments that mark a segment complete
-    int32_t* err;        // set when a wait gives up
-};
-
-// Bound on one wait, in ticks of the 100 MHz constant clock (200 ms): past
-// it the tile gives up, writes NaN for its merged rows and sets the error word
-// instead of hanging the GPU.  In a correct schedule a wait ends long before
-// it: every item waited on holds a smaller ticket of the same queue and is
-// running.
-constexpr uint64_t kWaitTicks = 20000000ull;
-
-// The producers of a tile's partials ran on the tile's own XCD (one queue per
-// XCD), so the hand-off needs that XCD's L2 only: the skip waves' stores are
-// complete in L2 before their counter increments (an L2 atomic); the counter
-// is polled with an atomic add of zero, which L2 performs (a plain load may be
-// served from the CU's L1, stale); the partial rows and records are then read
-// with device-scope loads, which L2 serves (a CU may hold a stale L1 copy of a
-// line that other tiles' rows share).  No cache is written back or
-// invalidated: an L2 write-back or invalidate walks the whole L2 and made the
-// kernel over ten times slower.
-// Counters sit a cache line apart (kCounterStride ints), so that a producer's
-// increment and the polls of other segments' consumers never share a line.
-constexpr int32_t kCounterStride = 32;
-
-__device__ __forceinline__ int32_t poll_l2(const int32_t* p) {
-    int32_t v;
-    asm volatile("global_load_dword %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=v"(v) : "v"(p) : "memory");
-    return v;
-}
-
-// Called by every wave of the tile at the same point: the first wave polls
-// (sleeping between polls, so that few loads reach the counter's L2 line),
-// the others wait at the barrier.  Returns false (on every wave) when the
-// wait gave up.
-__device__ __forceinline__ bool wait_segments(const SegWait& w, uint16_t* flag_lds) {
-    if (threadIdx.x < 64) {
-        bool ok = true;
-        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-        for (int32_t s = w.seg_lo; s <= w.seg_hi && ok; ++s) {
-            while (poll_l2(w.cnt + (int64_t)s * kCounterStride) < w.target) {
-                if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
-                    if (threadIdx.x == 0) __hip_atomic_fetch_or(w.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    ok = false;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(8);
-            }
-        }
-        if (threadIdx.x == 0) *flag_lds = ok ? 1 : 0;
-    }
-    lds_barrier();                                               // LDS only: the tile's loads keep flowing
-    return *flag_lds != 0;
-}
-
-// A row's record (log2-sum-exp, exponent) read from L2 (device scope).
-__device__ __forceinline__ f32x2_t load_record_dev(const float* p) {
-    f32x2_t r;
-    asm volatile("global_load_dwordx2 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=v"(r) : "v"(p) : "memory");
-    return r;
-}
-
-// Skip-wave side of the hand-off: wait until this wave's stores are complete
-// in L2, then count the wave (an L2 atomic, one lane).  `done` points at the
-// segment's counter (counters kCounterStride ints apart).
-__device__ __forceinline__ void signal_segment(int32_t* done) {
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
-    asm volatile("" ::: "memory");
-    if ((threadIdx.x & 63) == 0) __hip_atomic_fetch_add(done, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
 // Window-pass shape: WW waves of 16 query rows (a 64-row tile), KT key rows
 // per LDS slot.  Small workgroups with small slots keep several tiles in
 // flight per CU, each at a different point of its load / compute cycle:
@@ -198,16 +122,15 @@ struct WinShape {
     static constexpr int KT = 32;
     static constexpr int QTW = 16 * WW;
     static constexpr int EU = D == 64 ? 4 : 3;           // waves per SIMD the register budget must allow
-    static constexpr int LDS = 6 * KT * D * 2 + QTW * 4 + 16; // bytes: three K and three V slots, the gates, a flag
+    static constexpr int LDS = 6 * KT * D * 2 + QTW * 4;  // bytes: three K and three V slots, the gates
 };
 
 // Window tile qt of (sequence b, head h): 64 query rows, their window keys,
 // and (merge) the merge with the rows' skip partials.  lds: WinShape<D>::LDS
-// bytes.  With WAIT, each wave first waits on the completion counters of the
-// segments holding its tile's rows (sw) before it reads their partials.
-template <int D, bool BIDIR, bool WAIT>
+// bytes.
+template <int D, bool BIDIR>
 __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s, int32_t merge, int32_t qt,
-                                            int32_t h, int32_t b, uint16_t* lds, const SegWait& sw) {
+                                            int32_t h, int32_t b, uint16_t* lds) {
     using G = Geo<D>;
     constexpr int DC = G::DC, DB = G::DB, CH = G::CH, RPI = G::RPI;
     constexpr int WW = WinShape<D>::WW, KT = WinShape<D>::KT, QT = WinShape<D>::QTW, NB = KT / 16;
@@ -268,18 +191,15 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
     const bool isv = wave >= WW / 2;
     const uint16_t* src0 = isv ? Vb : Kb;
     const int32_t st = isv ? (int32_t)a.sv.t : (int32_t)a.sk.t;
-    auto stage_rows = [&](const uint16_t* src, int32_t stt, int32_t s0, int r0, uint16_t* dst,
-                          bool dev = false) __attribute__((always_inline)) {
+    auto stage_rows = [&](const uint16_t* src, int32_t stt, int32_t s0, int r0, uint16_t* dst)
+        __attribute__((always_inline)) {
         const int rl = r0 + lane / CH;
         const int lc = ((lane % CH) ^ (rl & 7)) << 3;
         const bool inside = s0 >= 0 && s0 + RPI - 1 < n;
         const uint16_t* ub = inside ? src + (int64_t)s0 * stt : src;
         const uint32_t off = inside ? (uint32_t)((lane / CH) * stt + lc)
                                     : (uint32_t)(imin32(imax32(s0 + lane / CH, 0), n - 1) * stt + lc);
-        if (dev)
-            dma16_dev(ub, off * 2u, lds_addr(dst + r0 * D));
-        else
-            dma16(ub, off * 2u, lds_addr(dst + r0 * D));
+        dma16(ub, off * 2u, lds_addr(dst + r0 * D));
     };
     // Stage t < ntiles: key tile t.  Stage ntiles, when skip partials are
     // merged: the tile's fp16 skip partial rows, each wave its own 16 rows
@@ -288,16 +208,10 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
     // tile, which keeps every wave's count of loads in flight uniform.
     auto issue = [&](uint16_t* Ks, uint16_t* Vs, int32_t t) __attribute__((always_inline)) {
         if (merge && t == ntiles) {
-            if constexpr (WAIT) {
-                // the partials and records of this tile's rows: ready once
-                // every skip wave of their segments has signalled
-                const bool ok = wait_segments(sw, reinterpret_cast<uint16_t*>(gls + QT));
-                if (mg) rec = ok ? load_record_dev(Ls + 2 * ic) : f32x2_t{NAN, 0.0f};
-            }
 #pragma unroll
             for (int j = 0; j < LPW; ++j) {
                 const int r0 = ((wave % (WW / 2)) * LPW + j) * RPI;
-                stage_rows(Ob, (int32_t)a.so.t, q0 + (isv ? KT : 0) + r0, r0, isv ? Vs : Ks, WAIT);
+                stage_rows(Ob, (int32_t)a.so.t, q0 + (isv ? KT : 0) + r0, r0, isv ? Vs : Ks);
             }
             return;
         }
@@ -350,8 +264,8 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
     lds_barrier();                                       // slot 2 is free for tile 2
 
     // the record of the lane's row, loaded now so that its latency hides
-    // behind the window loop (after the wait when the skip pass runs beside)
-    if (!WAIT && mg) rec = *reinterpret_cast<const f32x2_t*>(Ls + 2 * ic);
+    // behind the window loop
+    if (mg) rec = *reinterpret_cast<const f32x2_t*>(Ls + 2 * ic);
 
     f32x4_t acc[DB];
 #pragma unroll

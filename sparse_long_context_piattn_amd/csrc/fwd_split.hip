@@ -452,7 +452,7 @@ __global__ __launch_bounds__(WinShape<D>::WW * 64, WinShape<D>::EU) void fwd_win
     const int32_t logical = total - 1 - xcd_logical(blockIdx.x, total);
     const int32_t qt = logical % q_tiles;
     const int32_t rest = logical / q_tiles;
-    window_tile<D, BIDIR, false>(a, lse_s, merge, qt, rest % a.H, rest / a.H, lds, SegWait{});
+    window_tile<D, BIDIR>(a, lse_s, merge, qt, rest % a.H, rest / a.H, lds);
 }
 
 // lse_s: the caller's workspace of B*H*n (log2-sum-exp, e) float pairs, or

@@ -16,22 +16,6 @@ hipError_t launch_fwd_resid(const FwdArgs& a, hipStream_t stream);
 // window pass that merges the two partial softmaxes.
 bool fwd_split_supported(int dtype, const FwdArgs& a);
 hipError_t launch_fwd_split(const FwdArgs& a, float* ws, hipStream_t stream);
-// Fused prefill (bf16, d 64/128, pi % 4 == 0, short skip bands): the skip and
-// window work of the split path as items of one kernel, handed over through
-// the L2 of one XCD.  Workspace: the split path's per-row records, then the
-// counters of the schedule (zeroed by the launch).
-struct FusedLayout {
-    int64_t BH, S, R, W, E;       // (sequence, head) pairs, segments, skip items and tiles per segment, items per pair
-    int64_t T;                    // window tiles per pair
-    int64_t items;                // work items
-    int64_t NQ, QI;               // queues (XCDs) and the longest queue's items
-    int64_t CUs;                  // compute units of the device
-    int64_t counters;             // int32 counters (tickets, error word, per-segment counts)
-    int64_t counters_offset;      // byte offset of the counters in the workspace
-};
-bool fused_layout(const FwdArgs& a, FusedLayout* L);
-bool fwd_fused_supported(int dtype, const FwdArgs& a);
-hipError_t launch_fwd_fused(const FwdArgs& a, float* ws, hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_cache_append(int dtype, const AppendArgs& a, hipStream_t stream);
 // Backward of the prefill (gather path, any supported dtype and d; the

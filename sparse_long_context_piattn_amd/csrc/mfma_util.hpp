@@ -114,15 +114,6 @@ __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t
                  "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
 }
 
-// dma16 at device scope (sc1): the load is served by the L2, never by the
-// CU's L1, so it sees every store that completed in that L2 before it --
-// including stores of other CUs of the XCD, which may have left a stale copy
-// of the line in this CU's L1.
-__device__ __forceinline__ void dma16_dev(const void* sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 sc1" : : "v"(voff), "s"(uniform_ptr(sbase)),
-                 "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
-}
-
 // 4-byte LDS-direct load of each active lane (lane l writes lds + 4 l);
 // wait states as for dma16.
 __device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {

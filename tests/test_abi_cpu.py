@@ -88,7 +88,7 @@ def _fwd(dtype=1, B=1, H=1, n=64, d=64, q=A, k=A2, v=A3, g=A, out=OUT, lse=None,
     # the split path (bf16, d = 64, skips) needs 8 bytes per row of workspace
     (dict(ws=None), EWORKSPACE),
     (dict(ws=ctypes.c_void_p(1 << 24), wsb=8 * 64 - 1), EWORKSPACE),
-    (dict(ws=ctypes.c_void_p((1 << 24) + 16), wsb=8 * 64 + 4096), EINVAL),   # not 256-aligned
+    (dict(ws=ctypes.c_void_p((1 << 24) + 16), wsb=8 * 64), EINVAL),   # not 256-aligned
 ])
 def test_fwd_rejects_bad_arguments(kw, expect):
     rc, msg = _fwd(**kw)
@@ -104,13 +104,10 @@ def test_fwd_strides_null_rejected():
 
 
 def test_fwd_workspace_query():
-    # 8 bytes per (sequence, head, row) on the bf16 d = 64 / 128 path with skip
-    # keys (rounded up to 256), then 9 + B H ceil(ceil(n / pi) / 16) counters
-    # of a 128-byte line each
+    # 8 bytes per (sequence, head, row) on the bf16 d = 64 / 128 path with skip keys
     p = pa.make_pattern(64, 128, 16)
-    assert pa.fwd_workspace_bytes(1, 4, 16, 8192, 64, p) == 8 * 4 * 16 * 8192 + 128 * (9 + 64 * 4)
-    assert pa.fwd_workspace_bytes(1, 1, 32, 131072, 128, p) == 8 * 32 * 131072 + 128 * (9 + 32 * 64)
-    assert pa.fwd_workspace_bytes(1, 1, 1, 100, 64, pa.make_pattern(4, 16, 2)) == 1024 + 128 * (9 + 1)
+    assert pa.fwd_workspace_bytes(1, 4, 16, 8192, 64, p) == 8 * 4 * 16 * 8192
+    assert pa.fwd_workspace_bytes(1, 1, 32, 131072, 128, p) == 8 * 32 * 131072
     assert pa.fwd_workspace_bytes(0, 4, 16, 8192, 64, p) == 0            # fp32: gather path
     assert pa.fwd_workspace_bytes(1, 4, 16, 8192, 32, p) == 0            # d = 32: gather path
     assert pa.fwd_workspace_bytes(1, 4, 16, 8192, 64, pa.make_pattern(64, 128, 0)) == 0  # no skips

@@ -123,7 +123,7 @@ def test_d128_beyond_the_split_bound_runs_the_gather_kernel():
     assert max_err(got, ref, "gather d=128 n=%d" % n) <= BF16_TOL
 
 
-@pytest.mark.parametrize("kernel", ["auto", "fused", "split", "resid", "gather"])
+@pytest.mark.parametrize("kernel", ["auto", "split", "resid", "gather"])
 def test_varlen_sequence_longer_than_n_is_cut_not_overrun(kernel):
     """A varlen call whose n (max_seqlen) is below a sequence's length: that
     sequence is cut at n rows -- rows < n match the oracle on the sequence

@@ -117,7 +117,7 @@ def fwd_probe(n, d, k, pi, M, bidir, levels, kernel, dtype=torch.bfloat16):
     return shows
 
 
-@pytest.mark.parametrize("kernel", ["fused", "split", "resid", "gather"])
+@pytest.mark.parametrize("kernel", ["split", "resid", "gather"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_forward_membership_bit_exact(case, kernel):
     name, n, d, k, pi, M, bidir, levels = case
@@ -138,7 +138,7 @@ def test_forward_membership_fp32_gather():
         assert np.array_equal(got_skip, exp_skip), bidir
 
 
-@pytest.mark.parametrize("kernel", ["fused", "split", "resid", "gather"])
+@pytest.mark.parametrize("kernel", ["split", "resid", "gather"])
 def test_forward_membership_varlen(kernel):
     """Packed sequences of several lengths (one empty, one of a single
     token): head h probes key h of every sequence longer than h."""

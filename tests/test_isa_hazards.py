@@ -18,7 +18,7 @@ import pytest
 
 CSRC = os.path.join(os.path.dirname(__file__), "..", "sparse_long_context_piattn_amd", "csrc")
 HIPCC = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
-SOURCES = ["fwd_split.hip", "fwd_fused.hip", "fwd_resid.hip", "decode.hip", "bwd_band.hip", "proj.hip"]
+SOURCES = ["fwd_split.hip", "fwd_resid.hip", "decode.hip", "bwd_band.hip", "proj.hip"]
 
 pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="needs hipcc")
 
