@@ -28,23 +28,40 @@ METRIC = "π-attn fwd queries/s + achieved HBM GB/s & MFMA %, n=8192 d=64 bf16, 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16
 MALL_BYTES = 256 << 20
-KERNEL_SOURCES = ["pattern.hpp", "common.hpp", "gather.hpp", "mfma_util.hpp", "fwd_common.hpp", "fwd_gather.hip",
-                  "fwd_resid.hip", "fwd_split.hip", "decode.hip", "api.cpp", "noalloc.hip",
-                  "kernels.hpp", "api_internal.hpp"]
+# The sources each leg's kernels are built from (shared headers and the
+# dispatching C-ABI layer, then the leg's own kernels): a counter record is
+# valid while the digest of its leg's sources is unchanged.
+_SHARED_SOURCES = ["pattern.hpp", "common.hpp", "gather.hpp", "mfma_util.hpp", "kernels.hpp", "api.cpp",
+                   "api_internal.hpp"]
+LEG_SOURCES = {
+    "fwd": _SHARED_SOURCES + ["fwd_common.hpp", "fwd_gather.hip", "fwd_resid.hip", "fwd_split.hip", "noalloc.hip"],
+    "decode": _SHARED_SOURCES + ["decode.hip"],
+    "backward": _SHARED_SOURCES + ["bwd.hip", "bwd_band.hip"],
+    "layer": _SHARED_SOURCES + ["proj.hip"],
+}
+# The kernels of one step of each leg whose counters make up its traffic
+# (the layer's roofline is the output projection's, so its record is that
+# kernel's bytes).
+LEG_KERNELS = {
+    "fwd": lambda name: "fwd_" in name and "kernel" in name,
+    "decode": lambda name: "decode_split_kernel" in name or "decode_combine_kernel" in name,
+    "backward": lambda name: "bwd_" in name and "kernel" in name,
+    "layer": lambda name: "out_proj" in name,
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_digest() -> str:
-    """Digest of the kernel sources with comments and blank space removed, so
-    that counters stay matched to the code they were taken on across edits
-    that change no code."""
+def kernel_digest(leg: str = "fwd") -> str:
+    """Digest of one leg's kernel sources with comments and blank space
+    removed, so that counters stay matched to the code they were taken on
+    across edits that change no code."""
     import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "sparse_long_context_piattn_amd", "csrc")
-    for name in KERNEL_SOURCES:
+    for name in LEG_SOURCES[leg]:
         p = os.path.join(csrc, name)
         if os.path.exists(p):
             text = open(p).read()
@@ -93,14 +110,18 @@ def algorithmic(w, lengths=None):
     return bytes_, flops, rows, loc, sk
 
 
-def traffic_record(workload: str):
-    """HBM bytes per step (all kernels of one hot-path pass) from the committed
+def traffic_name(workload: str, leg: str) -> str:
+    return workload if leg in ("fwd", "decode") else "%s_%s" % (workload, leg)
+
+
+def traffic_record(workload: str, leg: str = "fwd"):
+    """HBM bytes per step (the leg's kernels of one step) from the committed
     rocprofv3 counter summary, if it was taken on the current kernel sources."""
-    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % workload)
+    p = os.path.join(ROOT, "profiles", "traffic_%s.json" % traffic_name(workload, leg))
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
-    if rec.get("kernel_digest") != kernel_digest():
+    if rec.get("kernel_digest") != kernel_digest(leg):
         return None
     return rec.get("hbm_bytes_per_step")
 
@@ -135,6 +156,14 @@ def _grow(run, budget_s, start, total):
                 run(count)
             return reps * count, time.perf_counter() - t0
         count = min(total, int(count * max(2.0, budget_s * 0.5 / max(el, 1e-3))))
+
+
+def _sample_size(count, total, what):
+    """'N of the T <what>' for a sample, or 'P passes over all T <what>' when
+    the sample repeats the whole workload (it is smaller than the budget)."""
+    if count > total:
+        return "%.1f passes over all %d %s" % (count / total, total, what)
+    return "%d of the %d %s (uniformly sampled without repeats)" % (count, total, what)
 
 
 def _baseline(unit, value, value1, threads, sample):
@@ -180,9 +209,9 @@ def cpu_baseline(w, x, budget_s: float):
     c1, el1 = _grow(lambda c: run(c, 1), budget_s * 0.25, 256, total_rows)
     run(16, threads)                                     # restore the thread count
     return _baseline("queries/s", count / el, c1 / el1, threads,
-                     "%d query rows (uniformly sampled without repeats; the whole set repeated when it "
-                     "is smaller) of the %s workload's %d, fp64, OpenMP over rows, %.1f s on %d threads; "
-                     "%d rows on 1 thread, %.1f s" % (count, w.name, total_rows, el, threads, c1, el1))
+                     "%s, fp64, OpenMP over rows, %.1f s on %d threads; %s on 1 thread, %.1f s"
+                     % (_sample_size(count, total_rows, "query rows of the %s workload" % w.name), el, threads,
+                        _sample_size(c1, total_rows, "rows"), el1))
 
 
 def cpu_baseline_decode(w, x, budget_s: float):
@@ -232,7 +261,8 @@ def cpu_baseline_decode(w, x, budget_s: float):
 
 def cpu_baseline_backward(w, x, budget_s: float):
     """The fp64 backward oracle on whole (sequence, head) slices of the
-    workload (it takes a packed batch; one head at a time is the sample)."""
+    workload (it takes a packed batch; one head at a time is the sample).
+    The backward oracle is serial C: the rate is one thread's."""
     import numpy as np
     import torch
 
@@ -262,9 +292,9 @@ def cpu_baseline_backward(w, x, budget_s: float):
     while el < budget_s * 0.75 and j < len(heads):
         e_, r_ = one(heads[j])
         el, rows, j = el + e_, rows + r_, j + 1
-    return _baseline("queries/s", rows / el, None, threads,
-                     "%d whole (sequence, head) slices (%d rows) of the %s workload, fp64 backward, "
-                     "%.1f s" % (j, rows, w.name, el))
+    return _baseline("queries/s", rows / el, rows / el, 1,
+                     "%d whole (sequence, head) slices (%d rows) of the %s workload, fp64 backward "
+                     "(serial), %.1f s on 1 thread" % (j, rows, w.name, el))
 
 
 def cpu_baseline_layer(w, xs, x, wg, wo, o, budget_s: float):
@@ -299,8 +329,9 @@ def cpu_baseline_layer(w, xs, x, wg, wo, o, budget_s: float):
 
     count, el = _grow(run, budget_s * 0.75, 256, B * n)
     return _baseline("tokens/s", count / el, None, threads,
-                     "%d of %d tokens, uniformly sampled: gate, every head's attention row and the output "
-                     "projection, fp64 (numpy products, C oracle over rows), %.1f s" % (count, B * n, el))
+                     "%s: gate, every head's attention row and the output projection, fp64 (numpy "
+                     "products, C oracle over rows on %d threads), %.1f s"
+                     % (_sample_size(count, B * n, "tokens"), threads, el))
 
 
 def decode_algorithmic(w):
@@ -372,10 +403,10 @@ def bench_decode(args, w, dev):
            "config": {"workload": w.name, "sequences": w.B, "H": w.H, "cache_len": w.n,
                       "d": w.d, "k": w.k, "pi": w.pi, "M": w.M, "num_splits": splits,
                       "cache": "rolling, %d rows" % slots if slots else "linear"},
-           "hbm_gbps_algorithmic": round(gbps, 1), **step_fields(t), "kernel_digest": kernel_digest(),
+           "hbm_gbps_algorithmic": round(gbps, 1), **step_fields(t), "kernel_digest": kernel_digest("decode"),
            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                         "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4),
-                        "traffic": traffic_record(w.name)},
+                        "traffic": traffic_record(w.name, "decode")},
            "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
 
@@ -417,6 +448,8 @@ def bench_backward(args, w, dev, sets, outs, lengths, rows):
     settle_clocks(dev)
     t = timed(step, args, dev)
     ms_per_step = t["median"]
+    if args.calibrate_copy:
+        calibrate_copy(dev)
     sec = ms_per_step / 1e3
     gbps = alg_bytes / sec / 1e9
     log("backward: %.4f ms/step  %.3e rows/s  %.0f GB/s (%.1f%% of HBM peak)"
@@ -434,9 +467,9 @@ def bench_backward(args, w, dev, sets, outs, lengths, rows):
            "config": {"workload": w.name, "pass": "backward", "B": w.B if not w.nseq else len(lengths),
                       "H": w.H, "n": w.n if not w.nseq else max(lengths), "d": w.d, "k": w.k, "pi": w.pi,
                       "M": w.M, "bidirectional": w.bidir, **({"levels": [list(l) for l in w.levels]} if w.levels else {})},
-           **step_fields(t), "kernel_digest": kernel_digest(),
+           **step_fields(t), "kernel_digest": kernel_digest("backward"),
            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_record(w.name + "_backward")},
+                        "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic_record(w.name, "backward")},
            "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
 
@@ -482,6 +515,8 @@ def bench_layer(args, w, dev):
     settle_clocks(dev)
     t = timed(step, args, dev)
     ms_per_step = t["median"]
+    if args.calibrate_copy:
+        calibrate_copy(dev)
     stream = torch.cuda.current_stream(dev)
     per = {}
     for name, f in stages.items():
@@ -529,9 +564,10 @@ def bench_layer(args, w, dev):
            "config": {"workload": w.name, "pass": "layer", "B": B, "H": H, "n": n, "d": d, "Dm": Dm, "k": w.k,
                       "pi": w.pi, "M": w.M, "bidirectional": w.bidir},
            "stages_ms": {k_: round(v_, 5) for k_, v_ in per.items()},
-           "torch_linear_ms": round(lib_ms, 5), **step_fields(t),
+           "torch_linear_ms": round(lib_ms, 5), **step_fields(t), "kernel_digest": kernel_digest("layer"),
            "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_MFMA_PEAK_TFLOPS,
-                        "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None},
+                        "unit": "TFLOP/s", "frac": round(tflops / BF16_MFMA_PEAK_TFLOPS, 4),
+                        "traffic": traffic_record(w.name, "layer")},
            "cpu_baseline": cpu}
     print(json.dumps(res), flush=True)
 
@@ -540,12 +576,14 @@ COPY_ELEMS = 256 << 20          # bf16 elements of the calibration copy (512 MiB
 
 
 def calibrate_copy(dev):
-    """A plain streaming copy of known size: reads and writes 512 MiB."""
+    """A plain streaming copy of known size: reads and writes 512 MiB (a
+    negation, whose kernel no workload's input generation launches, so its
+    dispatches are told apart by name)."""
     import torch
     src = torch.empty(COPY_ELEMS, dtype=torch.bfloat16, device=dev).normal_()
     dst = torch.empty_like(src)
     for _ in range(3):
-        torch.mul(src, 1.0, out=dst)
+        torch.neg(src, out=dst)
     torch.cuda.synchronize()
     del src, dst
 
@@ -617,27 +655,35 @@ def _per_dispatch(rows, counter, match):
     return total, sum(len(d) for d in per.values()), sorted(per)
 
 
+def leg_of(args) -> str:
+    from sparse_long_context_piattn_amd import workloads as wl
+    if wl.WORKLOADS[args.workload].kind == "decode":
+        return "decode"
+    return "backward" if args.backward else "layer" if args.layer else "fwd"
+
+
 def pmc_summary(args):
-    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the forward kernels, each
+    """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of the leg's kernels, each
     scaled by the reading of the same counter on the plain copy, summed over
     the kernels of one step into the HBM bytes per step that bench.py
     reports as roofline.traffic."""
+    leg = leg_of(args)
     fetch_rows, write_rows = _counter_rows(args.pmc_summary[0]), _counter_rows(args.pmc_summary[1])
-    is_fwd = lambda name: "fwd_" in name and "kernel" in name
-    is_copy = lambda name: "elementwise" in name and "MulFunctor" in name   # calibrate_copy
-    f_fwd, nf, knames = _per_dispatch(fetch_rows, "FETCH_SIZE", is_fwd)
-    w_fwd, nw, _ = _per_dispatch(write_rows, "WRITE_SIZE", is_fwd)
+    is_leg = LEG_KERNELS[leg]
+    is_copy = lambda name: "elementwise" in name and "neg_kernel" in name   # calibrate_copy
+    f_fwd, nf, knames = _per_dispatch(fetch_rows, "FETCH_SIZE", is_leg)
+    w_fwd, nw, _ = _per_dispatch(write_rows, "WRITE_SIZE", is_leg)
     f_cp, _, _ = _per_dispatch(fetch_rows, "FETCH_SIZE", is_copy)
     w_cp, _, _ = _per_dispatch(write_rows, "WRITE_SIZE", is_copy)
     copy_kib = COPY_ELEMS * 2 / 1024.0
     fs, ws = copy_kib / f_cp, copy_kib / w_cp
-    rec = {"workload": args.workload, "kernels": knames, "kernel_digest": kernel_digest(),
+    rec = {"workload": args.workload, "leg": leg, "kernels": knames, "kernel_digest": kernel_digest(leg),
            "fetch_kib_per_step": f_fwd, "write_kib_per_step": w_fwd,
            "dispatches": [nf, nw],
            "copy_kib_each_way": copy_kib, "copy_fetch_kib": f_cp, "copy_write_kib": w_cp,
            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
            "hbm_bytes_per_step": int(round((f_fwd * fs + w_fwd * ws) * 1024))}
-    out = os.path.join(ROOT, "profiles", "traffic_%s.json" % args.workload)
+    out = os.path.join(ROOT, "profiles", "traffic_%s.json" % traffic_name(args.workload, leg))
     json.dump(rec, open(out, "w"), indent=1)
     print(json.dumps(rec))
 
