@@ -17,8 +17,8 @@
 // from L2.  The output projection is a GEMM over M = tokens, N = Dout,
 // K = H d with the head concatenation folded into the A operand's addresses
 // (o stays in the attention's [B, H, n, d] layout, any strides): 256 x 256
-// tiles, K in chunks of 32 (always inside one head), a ring of three LDS
-// slots filled two stages ahead by LDS-direct loads, XOR-swizzled rows so
+// tiles, K in chunks of 32 (always inside one head), a ring of five LDS
+// slots filled four stages ahead by LDS-direct loads, XOR-swizzled rows so
 // that the MFMA operand reads are free of bank conflicts, and an epilogue
 // that turns the accumulators into whole bf16 rows through LDS.  fp32 inputs
 // take plain per-element kernels.
@@ -127,6 +127,7 @@ constexpr int PM = 256, PN = 256, PK = 32;   // tile rows (tokens), columns (out
 constexpr int PSLOT = (PM + PN) * PK;        // elements of one ring slot (A rows, then W rows)
 constexpr int PW = 8;                        // waves per workgroup (two per SIMD)
 constexpr int PLPW = 4;                      // 1 KB loads per wave per stage
+constexpr int PSLOTS = 5;                    // LDS ring slots (160 KB): loads run four stages ahead
 
 // Element offset of 16-byte chunk c (of 4) of row r in a [rows][32] bf16
 // tile, XOR-swizzled by (r / 2) % 4: the 16 rows x 4 chunks of an MFMA
@@ -143,7 +144,7 @@ constexpr int32_t GM = 8;
 
 __global__ __launch_bounds__(PW * 64, 1) void out_proj_mfma_kernel(ProjArgs a, int32_t mtiles, int32_t ntiles,
                                                                  int32_t total) {
-    __shared__ __attribute__((aligned(16))) uint16_t ring[3 * PSLOT];
+    __shared__ __attribute__((aligned(16))) uint16_t ring[PSLOTS * PSLOT];
     const int32_t logical = xcd_logical(blockIdx.x, total);
     const int32_t gsize = GM * ntiles, grp = logical / gsize, first = grp * GM;
     const int32_t gm = imin32(mtiles - first, GM), w_in = logical - grp * gsize;
@@ -209,17 +210,16 @@ __global__ __launch_bounds__(PW * 64, 1) void out_proj_mfma_kernel(ProjArgs a, i
             for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
     };
 
-    issue(0, ring);
-    issue(1, ring + PSLOT);
-    // step s: this wave's stage-s loads landed (stage s+1 may be in flight),
-    // barrier (everyone's landed, stage s-1 fully read), issue stage s+2
-    // into the slot of stage s-1, compute stage s
+#pragma unroll
+    for (int j = 0; j < PSLOTS - 1; ++j) issue(j, ring + j * PSLOT);
+    // step s: this wave's stage-s loads landed (the next PSLOTS - 2 stages
+    // may be in flight), barrier (everyone's landed, stage s-1 fully read),
+    // issue stage s + PSLOTS - 1 into the slot of stage s-1, compute stage s
     for (int32_t s = 0; s < nk; ++s) {
-        const int cur = s % 3;
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(PLPW));
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(PLPW * (PSLOTS - 2)));
         lds_barrier();
-        issue(s + 2, ring + ((s + 2) % 3) * PSLOT);
-        compute(ring + cur * PSLOT);
+        issue(s + PSLOTS - 1, ring + ((s + PSLOTS - 1) % PSLOTS) * PSLOT);
+        compute(ring + (s % PSLOTS) * PSLOT);
     }
     __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));                   // the trailing reloads land
     lds_barrier();                                                 // every wave done with the ring
