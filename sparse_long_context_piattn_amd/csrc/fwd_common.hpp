@@ -67,9 +67,13 @@ __device__ __forceinline__ float f16hi(uint32_t w) { return (float)__builtin_bit
 // layout (lane (x, g) holds d = 16 bb + 4 g + 0..3 of row x), then read back
 // 16 bytes each, a row's 2D bytes from 2D/16 neighbouring lanes.  Rows past
 // the residue or without skip keys are not stored; hs says whether row x has
-// skip keys (its record (lse2, e) is written then).
+// skip keys (its record (lse2, e) is written then).  sl is the sum of the
+// bf16 P the accumulators were built from (the partial is normalised by it,
+// so it is an exact convex combination of the value rows); sl32 the sum of
+// the same exponentials in fp32, the row's skip mass (its record).
 template <int D, bool BIDIR>
-__device__ __forceinline__ void store_skip_chunk(uint16_t* tt, const f32x4_t (&sacc)[D / 16], float sl, float sm,
+__device__ __forceinline__ void store_skip_chunk(uint16_t* tt, const f32x4_t (&sacc)[D / 16], float sl, float sl32,
+                                                 float sm,
                                                  bool hs, int32_t c, int32_t res, int32_t pr, int32_t pi,
                                                  int32_t mlo, int32_t M, uint16_t* Ob, int64_t sot, float* Ls,
                                                  int lane) {
@@ -93,7 +97,7 @@ __device__ __forceinline__ void store_skip_chunk(uint16_t* tt, const f32x4_t (&s
         *reinterpret_cast<uint2*>(tt + swr<D>(x, 2 * bb + (g >> 1)) + 4 * (g & 1)) = w;
     }
     if (hs && g == 0)
-        *reinterpret_cast<f32x2_t*>(Ls + 2 * (res + (16 * c + x) * pi)) = f32x2_t{sm + __log2f(sl), (float)e};
+        *reinterpret_cast<f32x2_t*>(Ls + 2 * (res + (16 * c + x) * pi)) = f32x2_t{sm + __log2f(sl32), (float)e};
 #pragma unroll
     for (int j = 0; j < 32 * D / 1024; ++j) {
         const int o = 1024 * j + 16 * lane;               // byte offset in the [16][D] fp16 tile
@@ -270,7 +274,10 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
     f32x4_t acc[DB];
 #pragma unroll
     for (int bb = 0; bb < DB; ++bb) acc[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float mrun = -INFINITY, lrun = 0.0f, mL = -INFINITY, cst = pl;
+    // lrun: this lane's quarter of the row's sum of the bf16 P that acc is
+    // built from (the normaliser); l32: this lane's 4 keys of every block in
+    // fp32 (the row's window mass: its log-sum-exp)
+    float mrun = -INFINITY, lrun = 0.0f, l32 = 0.0f, mL = -INFINITY, cst = pl;
 
     auto compute = [&](int32_t t, const uint16_t* Ks, const uint16_t* Vs) __attribute__((always_inline)) {
         const int32_t kt0 = klo + t * KT;
@@ -305,16 +312,21 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
 #pragma unroll
             for (int bb = 0; bb < DB; ++bb) acc[bb] *= fac;
             lrun *= fac;
+            l32 *= fac;
             mrun = mnew;
             mL = mnew + LAZY;
             cst = pl - mu;
         }
+        // P in bf16 for the PV products and the normaliser; the mass from the
+        // fp32 values
         s16x4_t pb[NB];
 #pragma unroll
         for (int u = 0; u < NB; ++u) {
-            const uint32_t w0 = cvt_pk_bf16(exp2_fast(fmaf(sc[u][0], sl2, cst)), exp2_fast(fmaf(sc[u][1], sl2, cst)));
-            const uint32_t w1 = cvt_pk_bf16(exp2_fast(fmaf(sc[u][2], sl2, cst)), exp2_fast(fmaf(sc[u][3], sl2, cst)));
-            pb[u] = __builtin_bit_cast(s16x4_t, make_uint2(w0, w1));
+            float p[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = exp2_fast(fmaf(sc[u][r], sl2, cst));
+            pb[u] = __builtin_bit_cast(s16x4_t, make_uint2(cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3])));
+            l32 += (p[0] + p[1]) + (p[2] + p[3]);
         }
         f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -346,8 +358,8 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
         lds_barrier();
         uint16_t* prow = (16 * wave < KT ? Kp : Vp);
         const int qr = 16 * wave + x, rr = qr & (KT - 1), rr0 = (16 * wave) & (KT - 1);
-        const float ltot = sum4(lrun);
-        const float lw = mrun + __log2f(ltot);          // log2-sum-exp of the window part
+        const float ltot = sum4(lrun);                  // normaliser of acc
+        const float lw = mrun + __log2f(sum4(l32));     // log2-sum-exp of the window part
         float fw = 1.0f / ltot, fs = 0.0f, lfin = lw;
         uint2 os[DB];
 #pragma unroll

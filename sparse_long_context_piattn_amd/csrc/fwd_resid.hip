@@ -198,6 +198,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     __shared__ __attribute__((aligned(16))) uint16_t qst[NW * IW * QSLOT];   // items' query rows
     __shared__ __attribute__((aligned(16))) float gst[NW * IW * 64];          // items' gate logits
     __shared__ __attribute__((aligned(16))) float mrec[16 * T * 2];             // items' (m, l)
+    __shared__ __attribute__((aligned(16))) float mrec32[16 * T];               // items' fp32 mass
 
     // XCD-aware order: each XCD gets a contiguous run of logical tiles.
     const int32_t hw = blockIdx.x;
@@ -299,7 +300,10 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     // ---- row groups of this wave: period t_j = t0 + wp + 2j
     bf16x8_t qf[TW][DC];
     f32x4_t acc[TW][DB];
-    float mrun[TW], lrun[TW], pl[TW];
+    // lrun: this lane's quarter of the row's sum of the bf16 P that acc is
+    // built from (the normaliser); l32: this lane's keys' exponentials in
+    // fp32 (the row's mass: its log-sum-exp)
+    float mrun[TW], lrun[TW], l32[TW], pl[TW];
     int32_t ij[TW];
     bool qv[TW];
     {
@@ -324,6 +328,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
             for (int bb = 0; bb < DB; ++bb) acc[j][bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
             mrun[j] = -INFINITY;
             lrun[j] = 0.0f;
+            l32[j] = 0.0f;
         }
     }
 
@@ -372,6 +377,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
 #pragma unroll
                 for (int bb = 0; bb < DB; ++bb) acc[j][bb] *= fac;
                 lrun[j] *= fac;
+                l32[j] *= fac;
                 mrun[j] = mnew;
                 mL = mnew + LAZY;
                 cst = pl[j] - mu;
@@ -380,9 +386,13 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
 #pragma unroll
             for (int u = 0; u < KBC; ++u) {
                 if (kb0 + u < NB) {
-                    const uint32_t w0 = cvt_pk_bf16(exp2_fast(fmaf(sc[u][0], sl2, cst)), exp2_fast(fmaf(sc[u][1], sl2, cst)));
-                    const uint32_t w1 = cvt_pk_bf16(exp2_fast(fmaf(sc[u][2], sl2, cst)), exp2_fast(fmaf(sc[u][3], sl2, cst)));
-                    pb[u] = __builtin_bit_cast(s16x4_t, make_uint2(w0, w1));
+                    // P in bf16 for the PV products and the normaliser,
+                    // the mass from the fp32 values
+                    float p[4];
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) p[r] = exp2_fast(fmaf(sc[u][r], sl2, cst));
+                    pb[u] = __builtin_bit_cast(s16x4_t, make_uint2(cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3])));
+                    l32[j] += (p[0] + p[1]) + (p[2] + p[3]);
                 } else {
                     pb[u] = s16x4_t{0, 0, 0, 0};
                 }
@@ -426,7 +436,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
     // col = lane % 16 is period t0 + col (a query for col < T).
     bf16x8_t sq[IW][DC];
     f32x4_t sacc[IW][DB];
-    float sm[IW], sl[IW], sps[IW], smL[IW], scst[IW];
+    float sm[IW], sl[IW], sl32[IW], sps[IW], smL[IW], scst[IW];
     int32_t slo[IW], stq[IW];
     uint32_t sspan[IW];
     const int col = x;
@@ -487,6 +497,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
             sm[it] = -INFINITY;
             smL[it] = -INFINITY;
             sl[it] = 0.0f;
+            sl32[it] = 0.0f;
             scst[it] = sps[it];
         }
     };
@@ -522,13 +533,16 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
 #pragma unroll
             for (int bb = 0; bb < DB; ++bb) sacc[it][bb] *= fac;
             sl[it] *= fac;
+            sl32[it] *= fac;
             sm[it] = mnew;
             smL[it] = mnew + LAZY;
             scst[it] = sps[it] - mu;
         }
-        const uint32_t w0 = cvt_pk_bf16(exp2_fast(fmaf(sc[0], sl2, scst[it])), exp2_fast(fmaf(sc[1], sl2, scst[it])));
-        const uint32_t w1 = cvt_pk_bf16(exp2_fast(fmaf(sc[2], sl2, scst[it])), exp2_fast(fmaf(sc[3], sl2, scst[it])));
-        const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(w0, w1));
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = exp2_fast(fmaf(sc[r], sl2, scst[it]));
+        const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3])));
+        sl32[it] += (p[0] + p[1]) + (p[2] + p[3]);  // this lane's keys, fp32; sum4 when merged
         const f32x4_t ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, pb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
         sl[it] += ls[0];                         // full column sum in every lane
 #pragma unroll
@@ -548,11 +562,15 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
 #pragma unroll
         for (int it = 0; it < IW; ++it) {
             const int xx = 2 * wave + it;
+            const float slf = sum4(sl32[it]);               // the column's fp32 mass (every lane)
             if (col < T) {
                 const uint32_t rec = sbase + (uint32_t)(wave * UNIT * 2) +
                                      4u * (uint32_t)(((it * DB) * 4 + g) * 32 + ((col ^ (xx & 7)) << 2));
                 lds_write_o(rec, sacc[it][0], sacc[it][1], sacc[it][2], sacc[it][3]);
-                if (g == 0) lds_write_ml(lds_addr(mrec) + 8u * (uint32_t)(xx * T + col), sm[it], sl[it]);
+                if (g == 0) {
+                    lds_write_ml(lds_addr(mrec) + 8u * (uint32_t)(xx * T + col), sm[it], sl[it]);
+                    mrec32[xx * T + col] = slf;
+                }
             }
         }
         lds_barrier();
@@ -570,6 +588,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
                 const float fl = exp2_fast(mrun[j] - mu);
                 const float fs = exp2_fast(msk - mu);
                 lrun[j] = lrun[j] * fl + 0.25f * lsk * fs;
+                l32[j] = l32[j] * fl + 0.25f * mrec32[x * T + cj] * fs;
                 mrun[j] = mnew;
 #pragma unroll
                 for (int bb = 0; bb < DB; ++bb) acc[j][bb] = acc[j][bb] * fl + sv[bb] * fs;
@@ -645,6 +664,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
 #pragma unroll
     for (int j = 0; j < TW; ++j) {
         const float ltot = sum4(lrun[j]);
+        const float lmass = sum4(l32[j]);                // cross-lane: before the lane exits
         if (!qv[j]) continue;
         const float inv = 1.0f / ltot;
         uint16_t* orow = Ob + (int64_t)ij[j] * a.so.t;
@@ -655,7 +675,7 @@ __global__ __launch_bounds__(NT) void fwd_resid_kernel(FwdArgs a, int32_t a_tile
             w.y = cvt_pk_bf16(acc[j][bb][2] * inv, acc[j][bb][3] * inv);
             *reinterpret_cast<uint2*>(orow + 16 * bb + 4 * g) = w;
         }
-        if (a.lse && g == 0) a.lse[gbase + (int64_t)ij[j] * a.sg.t] = (mrun[j] + __log2f(ltot)) * PIATTN_LN2;
+        if (a.lse && g == 0) a.lse[gbase + (int64_t)ij[j] * a.sg.t] = (mrun[j] + __log2f(lmass)) * PIATTN_LN2;
     }
 }
 

@@ -132,10 +132,12 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_kernel(FwdArgs a, float* lse
     const int tr_col = 4 * (x & 3);
     const s16x4_t ones4 = __builtin_bit_cast(s16x4_t, make_uint2(0x3f803f80u, 0x3f803f80u));
 
-    // ---- state of the current chunk (query periods 16c + col, col = x)
+    // ---- state of the current chunk (query periods 16c + col, col = x);
+    // sl: the column's sum of the bf16 P the accumulators are built from;
+    // sl32: this lane's 4 keys of every block in fp32 (the column's mass)
     bf16x8_t sq[DC];
     f32x4_t sacc[DB];
-    float sm = -INFINITY, sl = 0.0f, smL = -INFINITY, scst = 0.0f;
+    float sm = -INFINITY, sl = 0.0f, sl32 = 0.0f, smL = -INFINITY, scst = 0.0f;
     int32_t slo = EMPTY, stq = 0;
     uint32_t sspan = 0;
     bool shs = false;
@@ -157,13 +159,14 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_kernel(FwdArgs a, float* lse
         sm = -INFINITY;
         smL = -INFINITY;
         sl = 0.0f;
+        sl32 = 0.0f;
         scst = 0.0f;
     };
     // (through the slot of the chunk's last unit: the next unit issues into
     // it only after these stores, which wait for their LDS reads)
     auto chunk_store = [&](int32_t c, uint16_t* slot) __attribute__((always_inline)) {
-        store_skip_chunk<D, BIDIR>(slot + wave * UNIT, sacc, sl, sm, shs, c, res, pr, pi, mlo, M, Ob, a.so.t, Ls,
-                                   lane);
+        store_skip_chunk<D, BIDIR>(slot + wave * UNIT, sacc, sl, sum4(sl32), sm, shs, c, res, pr, pi, mlo, M, Ob,
+                                   a.so.t, Ls, lane);
     };
     auto unit_compute = [&](int32_t kb, const uint16_t* slot) __attribute__((always_inline)) {
         const uint16_t* Ks = slot + wave * UNIT;
@@ -193,18 +196,21 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_kernel(FwdArgs a, float* lse
 #pragma unroll
             for (int bb = 0; bb < DB; ++bb) sacc[bb] *= fac;
             sl *= fac;
+            sl32 *= fac;
             sm = mnew;
             smL = mnew + LAZY;
             scst = -mu;
         }
-        const uint32_t w0 = cvt_pk_bf16(exp2_fast(fmaf(sc[0], sl2, scst)), exp2_fast(fmaf(sc[1], sl2, scst)));
-        const uint32_t w1 = cvt_pk_bf16(exp2_fast(fmaf(sc[2], sl2, scst)), exp2_fast(fmaf(sc[3], sl2, scst)));
-        const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(w0, w1));
+        float p[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) p[r] = exp2_fast(fmaf(sc[r], sl2, scst));
+        const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3])));
         s16x4_t vv[DB];
 #pragma unroll
         for (int bb = 0; bb < DB; ++bb) vv[bb] = ld_tr16(Vs + swu<D>(tr_row, 2 * bb + (tr_col >> 3)) + (tr_col & 7));
+        sl32 += (p[0] + p[1]) + (p[2] + p[3]);
         const f32x4_t ls = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, pb, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        sl += ls[0];
+        sl += ls[0];                                  // full column sum in every lane
 #pragma unroll
         for (int bb = 0; bb < DB; ++bb)
             sacc[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vv[bb], pb, sacc[bb], 0, 0, 0);
@@ -330,7 +336,6 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
     const float sl2 = a.scale_log2;
     const int tr_row = 4 * g + (x >> 2);
     const int tr_col = 4 * (x & 3);
-    const s16x4_t ones4 = __builtin_bit_cast(s16x4_t, make_uint2(0x3f803f80u, 0x3f803f80u));
 
     bf16x8_t kr[NK][DC];                                  // ring of entry operands
     s16x4_t vr[NK][DB];
@@ -403,22 +408,28 @@ __global__ __launch_bounds__(SW * 64) void fwd_skip_ring_kernel(FwdArgs a, float
         f32x4_t sacc[DB];
 #pragma unroll
         for (int bb = 0; bb < DB; ++bb) sacc[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        // the accumulators and the normaliser from the bf16 P, the mass
+        // from the fp32 values (this lane's keys)
+        const s16x4_t ones4 = __builtin_bit_cast(s16x4_t, make_uint2(0x3f803f80u, 0x3f803f80u));
         f32x4_t lsum = {0.f, 0.f, 0.f, 0.f};
+        float lpart = 0.0f;
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
             const int slot = (RS + 1 + i) % NK;
-            const uint32_t w0 = cvt_pk_bf16(exp2_fast(fmaf(sc[i][0], sl2, scst)), exp2_fast(fmaf(sc[i][1], sl2, scst)));
-            const uint32_t w1 = cvt_pk_bf16(exp2_fast(fmaf(sc[i][2], sl2, scst)), exp2_fast(fmaf(sc[i][3], sl2, scst)));
-            const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(w0, w1));
+            float p[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p[r] = exp2_fast(fmaf(sc[i][r], sl2, scst));
+            const s16x4_t pb = __builtin_bit_cast(s16x4_t, make_uint2(cvt_pk_bf16(p[0], p[1]), cvt_pk_bf16(p[2], p[3])));
+            lpart += (p[0] + p[1]) + (p[2] + p[3]);
             lsum = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(ones4, pb, lsum, 0, 0, 0);
 #pragma unroll
             for (int bb = 0; bb < DB; ++bb)
                 sacc[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vr[slot][bb], pb, sacc[bb], 0, 0, 0);
         }
-        const float sl = lsum[0];
+        const float sl = lsum[0], sl32 = sum4(lpart);
         // the chunk's skip partial, through the slot of entry e: free until
         // entry e+3 is issued after the next chunk's LDS reads
-        store_skip_chunk<D, BIDIR>(ws + ((e % 3 + 3) % 3) * BLK, sacc, sl, sm, hs, c, res, pr, pi, mlo, M, Ob,
+        store_skip_chunk<D, BIDIR>(ws + ((e % 3 + 3) % 3) * BLK, sacc, sl, sl32, sm, hs, c, res, pr, pi, mlo, M, Ob,
                                    a.so.t, Ls, lane);
     };
 

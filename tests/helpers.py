@@ -14,10 +14,13 @@ from sparse_long_context_piattn_amd import workloads as wl
 
 BF16_TOL = 2e-2
 F32_TOL = 1e-5
-# Row log-normaliser: the bf16 MFMA path normalises with the bf16-rounded
-# softmax weights it multiplies V by, so its sum carries their unit roundoff
-# 2^-8 (relative), i.e. up to ~0.0039 in natural-log units.
-LSE_TOL_BF16 = 5e-3
+# Row log-normaliser.  On every path it is log(sum exp(logit)) computed in
+# fp32 from exact inputs (bf16 values are exact in fp32): scores accumulated
+# in fp32 (MFMA or VALU) over d <= 128 exact products, the exponentials
+# summed in fp32 before any bf16 rounding of the weights, one log.  For the
+# magnitudes of these workloads that stays well under 1e-5 in natural-log
+# units, the same bound on both dtypes.
+LSE_TOL_BF16 = 1e-5
 LSE_TOL_F32 = 1e-5
 
 
