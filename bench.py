@@ -34,7 +34,8 @@ MALL_BYTES = 256 << 20
 _SHARED_SOURCES = ["pattern.hpp", "common.hpp", "gather.hpp", "mfma_util.hpp", "kernels.hpp", "api.cpp",
                    "api_internal.hpp"]
 LEG_SOURCES = {
-    "fwd": _SHARED_SOURCES + ["fwd_common.hpp", "fwd_gather.hip", "fwd_resid.hip", "fwd_split.hip", "noalloc.hip"],
+    "fwd": _SHARED_SOURCES + ["fwd_common.hpp", "fwd_gather.hip", "fwd_resid.hip", "fwd_split.hip", "fwd_f32mfma.hip",
+                              "noalloc.hip"],
     "decode": _SHARED_SOURCES + ["decode.hip"],
     "backward": _SHARED_SOURCES + ["bwd.hip", "bwd_band.hip"],
     "layer": _SHARED_SOURCES + ["proj.hip"],
@@ -750,7 +751,7 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward (piattn_bwd) instead of the forward (prefill workloads)")
     ap.add_argument("--kernel", default="auto",
-                    help="prefill kernel to force (auto, split, resid, gather) for comparisons")
+                    help="prefill kernel to force (auto, split, resid, gather, f32mfma) for comparisons")
     ap.add_argument("--rolling", action="store_true",
                     help="decode over a rolling cache of max(k, M pi) + 1 rows")
     ap.add_argument("--calibrate-copy", action="store_true",

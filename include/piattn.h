@@ -382,7 +382,8 @@ enum {
     PIATTN_FWD_SPLIT = 1,   /* skip pass + window pass (bf16, d 64 / 128) */
     PIATTN_FWD_RESID = 2,   /* residue-tiled single kernel (bf16, d 64) */
     PIATTN_FWD_GATHER = 3,  /* one wave per row (any dtype and d) */
-    PIATTN_FWD_LAST = PIATTN_FWD_GATHER,
+    PIATTN_FWD_F32MFMA = 4, /* fp32 on fp32 MFMA, 16 query rows per wave (fp32, d 32 / 64 / 128) */
+    PIATTN_FWD_LAST = PIATTN_FWD_F32MFMA,
     PIATTN_BWD_BAND = 1,    /* MFMA band kernels (bf16, d 64 / 128, lse given) */
     PIATTN_BWD_GATHER = 2   /* gather kernels (any dtype and d) */
 };

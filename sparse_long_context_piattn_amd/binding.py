@@ -474,7 +474,7 @@ def neighbors(n: int, *, window_k: int, period_pi: int, num_skips: int, bidirect
     return idx, kind, count
 
 
-FWD_KERNELS = {"auto": 0, "split": 1, "resid": 2, "gather": 3}
+FWD_KERNELS = {"auto": 0, "split": 1, "resid": 2, "gather": 3, "f32mfma": 4}
 BWD_KERNELS = {"auto": 0, "band": 1, "gather": 2}
 
 

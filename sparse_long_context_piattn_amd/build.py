@@ -20,7 +20,7 @@ LIB = os.path.join(PKG, "libpiattn.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.cpp", "neighbors.hip", "fwd_gather.hip", "fwd_resid.hip",
-           "fwd_split.hip", "decode.hip", "bwd.hip", "bwd_band.hip",
+           "fwd_split.hip", "fwd_f32mfma.hip", "decode.hip", "bwd.hip", "bwd_band.hip",
            "proj.hip", "noalloc.hip"]
 
 # Packed-fp32 VALU forms are kept out of the device code (plain fp32 only).

@@ -333,10 +333,13 @@ int piattn_fwd(piattn_dtype dtype, int32_t B, int32_t H, int32_t n, int32_t d, c
         if (force == PIATTN_FWD_RESID && fwd_resid_supported(dt, a)) return launch_status(launch_fwd_resid(a, st));
         if (force == PIATTN_FWD_SPLIT && fwd_split_supported(dt, a)) return split();
         if (force == PIATTN_FWD_GATHER) return launch_status(launch_fwd_gather(dt, a, st));
+        if (force == PIATTN_FWD_F32MFMA && fwd_f32mfma_supported(dt, a))
+            return launch_status(launch_fwd_f32mfma(a, st));
         return fail(PIATTN_EUNSUPPORTED, "the forced prefill kernel (%d) cannot take this call", force);
     }
     if (fwd_split_supported(dt, a)) return split();
     if (fwd_resid_supported(dt, a)) return launch_status(launch_fwd_resid(a, st));
+    if (fwd_f32mfma_supported(dt, a) && fwd_f32mfma_preferred(a)) return launch_status(launch_fwd_f32mfma(a, st));
     return launch_status(launch_fwd_gather(dt, a, st));
 }
 

@@ -15,6 +15,11 @@ hipError_t launch_fwd_resid(const FwdArgs& a, hipStream_t stream);
 // Split prefill (bf16, d 64/128, any pi): skip pass in residue layout, then a
 // window pass that merges the two partial softmaxes.
 bool fwd_split_supported(int dtype, const FwdArgs& a);
+// fp32 prefill on fp32 MFMA (d 32/64/128): 16 query rows per wave, the
+// union's 16-key blocks in key order.
+bool fwd_f32mfma_supported(int dtype, const FwdArgs& a);
+bool fwd_f32mfma_preferred(const FwdArgs& a);   // cost model against the gather kernel
+hipError_t launch_fwd_f32mfma(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_fwd_split(const FwdArgs& a, float* ws, hipStream_t stream);
 hipError_t launch_decode(int dtype, const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_cache_append(int dtype, const AppendArgs& a, hipStream_t stream);

@@ -83,6 +83,49 @@ def test_forced_kernel_matches_oracle(case, kernel):
     assert max_err(lse, rlse, "lse " + tag) <= lse_tol_for(w)
 
 
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_f32mfma_matches_oracle(case):
+    """The fp32 MFMA kernel on the same shapes in fp32 (its own dtype)."""
+    name, B, H, n, d, k, pi, M, bidir = case
+    w = wl.Workload(name + "_f32", "fwd", "f32", B=B, H=H, n=n, d=d, k=k, pi=pi, M=M, bidir=bidir,
+                    seed=zlib.crc32(name.encode()) % 1000)
+    x = wl.make_fwd_inputs(w, device=DEV)
+    lse = torch.empty_like(x["g"])
+    out = run_fwd(x, w, "f32mfma", lse=lse)
+    torch.cuda.synchronize()
+    ref, rlse = oracle_dense_fwd(x, w, want_lse=True)
+    tag = "f32mfma %s" % name
+    assert max_err(out, ref, "fwd " + tag) <= tol_for(w)
+    assert max_err(lse, rlse, "lse " + tag) <= lse_tol_for(w)
+
+
+def test_f32mfma_tiny_fp32_every_row():
+    """The fp32 workload (B1 H2 n256 d32, k8 pi16 M4) on the fp32 MFMA kernel, every row."""
+    w = wl.WORKLOADS["tiny_fp32"]
+    x = wl.make_fwd_inputs(w, device=DEV)
+    lse = torch.empty_like(x["g"])
+    out = run_fwd(x, w, "f32mfma", lse=lse)
+    torch.cuda.synchronize()
+    ref, rlse = oracle_dense_fwd(x, w, want_lse=True)
+    assert max_err(out, ref, "fwd f32mfma tiny_fp32") <= tol_for(w)
+    assert max_err(lse, rlse, "lse f32mfma tiny_fp32") <= lse_tol_for(w)
+
+
+def test_f32mfma_varlen_every_row():
+    for bidir in (True, False):
+        w = wl.Workload("vl32", "fwd", "f32", H=3, d=32, k=12, pi=20, M=5, bidir=bidir, nseq=6,
+                        len_lo=1, len_hi=900, seed=29)
+        x = wl.make_fwd_inputs(w, device=DEV, lengths=[0, 1, 700, 33, 899, 64])
+        lse = torch.empty_like(x["g"])
+        out = run_fwd(x, w, "f32mfma", lse=lse)
+        torch.cuda.synchronize()
+        ref, rlse = oracle_varlen_fwd(x, w, want_lse=True)
+        T = x["q"].shape[0]
+        tag = "f32mfma varlen bidir=%d" % bidir
+        assert max_err(out.reshape(T * w.H, w.d), ref, "fwd " + tag) <= tol_for(w)
+        assert max_err(lse.reshape(-1), rlse, "lse " + tag) <= lse_tol_for(w)
+
+
 @pytest.mark.parametrize("kernel", ["resid", "split"])
 def test_forced_kernel_varlen_every_row(kernel):
     for bidir in (True, False):

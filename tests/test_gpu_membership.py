@@ -128,14 +128,17 @@ def test_forward_membership_bit_exact(case, kernel):
     assert np.array_equal(got_skip, exp_skip), (name, kernel, np.argwhere(got_skip != exp_skip)[:8])
 
 
-def test_forward_membership_fp32_gather():
-    n, d, k, pi, M = 200, 32, 6, 16, 5
+@pytest.mark.parametrize("kernel", ["gather", "f32mfma"])
+@pytest.mark.parametrize("n,d,k,pi,M,levels", [(200, 32, 6, 16, 5, ()), (150, 64, 20, 7, 9, ()),
+                                                (130, 32, 0, 3, 30, ()), (90, 128, 40, 16, 0, ()),
+                                                (240, 32, 4, 8, 3, ((16, 4), (32, 2)))])
+def test_forward_membership_fp32(kernel, n, d, k, pi, M, levels):
     for bidir in (False, True):
-        K = kind_matrix(n, k, pi, M, bidir, ())
+        K = kind_matrix(n, k, pi, M, bidir, levels)
         exp_local, exp_skip = expected_shows(K)
-        got_local, got_skip = fwd_probe(n, d, k, pi, M, bidir, (), "gather", dtype=torch.float32)
-        assert np.array_equal(got_local, exp_local), bidir
-        assert np.array_equal(got_skip, exp_skip), bidir
+        got_local, got_skip = fwd_probe(n, d, k, pi, M, bidir, levels, kernel, dtype=torch.float32)
+        assert np.array_equal(got_local, exp_local), (kernel, bidir)
+        assert np.array_equal(got_skip, exp_skip), (kernel, bidir)
 
 
 @pytest.mark.parametrize("kernel", ["split", "resid", "gather"])

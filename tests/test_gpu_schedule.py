@@ -68,7 +68,8 @@ def test_schedule_neighbors_bit_exact(case):
 
 
 FWD = [(c, dt, d, kern) for c in SCHEDS for dt, d, kern in
-       (("bf16", 64, "split"), ("bf16", 128, "split"), ("f32", 32, "gather"), ("bf16", 64, "gather"))]
+       (("bf16", 64, "split"), ("bf16", 128, "split"), ("f32", 32, "gather"), ("bf16", 64, "gather"),
+        ("f32", 32, "f32mfma"), ("f32", 64, "f32mfma"))]
 
 
 @pytest.mark.parametrize("case,dt,d,kernel", FWD,

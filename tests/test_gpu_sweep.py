@@ -3,7 +3,7 @@
 Each of 48 forward and 32 backward cases draws a window k, period pi, skip count M, direction, head dim,
 ragged length and (sometimes) a skip schedule of up to three levels, within
 the bounds the library accepts; the prefill runs on every kernel that takes
-the pattern (split, resid, gather; pa.forced_kernels), and the backward on
+the pattern (split, resid, gather, f32mfma; pa.forced_kernels), and the backward on
 both paths.  Tolerances as in the other parity tests: 1e-5 (fp32) / 2e-2
 (bf16) for the forward, 1e-5 / 3e-2 relative to the gradient's scale for
 the backward.
@@ -56,7 +56,7 @@ def test_sweep_fwd_every_kernel(seed):
     x = wl.make_fwd_inputs(w, device=DEV)
     ref = oracle_dense_fwd(x, w)
     ran = 0
-    for kern in ("split", "resid", "gather"):
+    for kern in ("split", "resid", "gather", "f32mfma"):
         print("sweep fwd seed %d %s: %s" % (seed, kern, w), flush=True)
         try:
             out = _forced("fwd", kern, lambda: pa.fwd(
