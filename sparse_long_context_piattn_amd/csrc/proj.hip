@@ -19,9 +19,10 @@
 // (o stays in the attention's [B, H, n, d] layout, any strides): 256 x 256
 // tiles, K in chunks of 32 (always inside one head), a ring of five LDS
 // slots filled four stages ahead by LDS-direct loads, XOR-swizzled rows so
-// that the MFMA operand reads are free of bank conflicts, and an epilogue
-// that turns the accumulators into whole bf16 rows through LDS.  fp32 inputs
-// take plain per-element kernels.
+// that the MFMA operand reads are free of bank conflicts, two groups of four
+// waves that alternate between reading a chunk's operands and running its
+// MFMAs, and an epilogue that turns the accumulators into whole bf16 rows
+// through LDS.  fp32 inputs take plain per-element kernels.
 #include "kernels.hpp"
 #include "mfma_util.hpp"
 
@@ -135,8 +136,14 @@ constexpr int PSLOTS = 5;                    // LDS ring slots (160 KB): loads r
 __device__ __forceinline__ int psw(int r, int c) { return r * PK + ((c ^ ((r >> 1) & 3)) << 3); }
 
 // 256 x 256 tile, eight waves of 64 x 128 (4 x 8 MFMA blocks), two per
-// SIMD so that one wave's MFMAs cover the other's barrier and LDS waits: per
-// k-chunk a wave reads 12 operand rows of 16 bytes for 32 MFMAs.
+// SIMD: per k-chunk a wave reads 12 operand rows of 16 bytes for 32 MFMAs.
+// The LDS then carries 96 KB of operand reads and 32 KB of staging writes
+// per chunk of the tile, as long at about 128 bytes a clock as the chunk's
+// 64 MFMAs per SIMD.  The two waves of a SIMD work in opposite phases: waves
+// 0-3 run the MFMAs of chunk s while waves 4-7 read the operands of chunk s
+// into registers, then they swap at a barrier, so each SIMD's matrix unit is
+// fed by one wave while the LDS serves the other (a wave's own reads in
+// flight slow its MFMA issue, the other wave's do not).
 // Tile order: groups of GM row tiles, rows fastest inside a group, so that
 // each XCD's run of 32 consecutive tiles is about 8 row tiles x 4 column
 // tiles sharing their A and W slabs in that XCD's L2.
@@ -179,16 +186,26 @@ __global__ __launch_bounds__(PW * 64, 1) void out_proj_mfma_kernel(ProjArgs a, i
             voff[j] = (uint32_t)(((int64_t)nn * a.ldw + 8 * lc) * 2);
         }
     }
-    const uint16_t* obase = static_cast<const uint16_t*>(a.o);
-    const uint16_t* wbase = static_cast<const uint16_t*>(a.w);
-    auto issue = [&](int32_t s, uint16_t* slot) __attribute__((always_inline)) {
-        s = imin32(s, nk - 1);                                     // past the end: a harmless reload
-        const int32_t k0 = s * PK;
-        const int32_t h = k0 / a.d, c0 = k0 - h * a.d;
-        const uint16_t* src = isw ? wbase + k0 : obase + (int64_t)h * a.so_h + c0;
+    // stages are issued in order: the source of the next one advances by a
+    // k-chunk, for A to the next head's column 0 after a head's last chunk;
+    // past the last stage the last one is reloaded (harmless, keeps the
+    // per-stage load count and so the waits uniform)
+    const uint16_t* src = isw ? static_cast<const uint16_t*>(a.w) : static_cast<const uint16_t*>(a.o);
+    int32_t next = 0, kcol = 0;
+    auto issue = [&](uint16_t* slot) __attribute__((always_inline)) {
         uint16_t* dst = slot + (isw ? PM * PK : 0) + rbase * PK;
 #pragma unroll
         for (int j = 0; j < PLPW; ++j) dma16(src, voff[j], lds_addr(dst + 16 * j * PK));
+        if (next < nk - 1) {
+            ++next;
+            kcol += PK;
+            if (!isw && kcol == a.d) {
+                kcol = 0;
+                src += a.so_h - (a.d - PK);
+            } else {
+                src += PK;
+            }
+        }
     };
 
     f32x4_t acc[4][8];
@@ -198,32 +215,43 @@ __global__ __launch_bounds__(PW * 64, 1) void out_proj_mfma_kernel(ProjArgs a, i
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;       // the wave's 64 x 128 sub-tile
 
-    auto compute = [&](const uint16_t* slot) __attribute__((always_inline)) {
-        bf16x8_t av[4], bv[8];
+    // Phases, one barrier after each: waves 0-3 (group 0) take the read
+    // phase of chunk s in phase 2s and its MFMAs in phase 2s+1; waves 4-7
+    // (group 1) one phase later.  The read phase of chunk s also issues the
+    // wave's loads of stage s+4 into the slot of chunk s-1, which both groups
+    // finished reading by phase 2s-1.  Stage c must have landed for every
+    // wave before phase 2c: each wave waits for its own share at the end of
+    // phase 2c-1 (group 0 after the MFMAs of c-1, group 1 after reading c-1),
+    // when the stages after c that it has issued are c+1..c+3.
+    const int group = wave >> 2;
+    auto bar = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    bf16x8_t av[4], bv[8];
+#pragma unroll
+    for (int j = 0; j < PSLOTS - 1; ++j) issue(ring + j * PSLOT);
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(PLPW * (PSLOTS - 2)));  // own stage 0
+    bar();
+    if (group == 1) bar();
+    for (int32_t s = 0; s < nk; ++s) {
+        const uint16_t* slot = ring + (s % PSLOTS) * PSLOT;
 #pragma unroll
         for (int j = 0; j < 8; ++j) bv[j] = *reinterpret_cast<const bf16x8_t*>(slot + PM * PK + psw(wn + 16 * j + x, g));
 #pragma unroll
         for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const bf16x8_t*>(slot + psw(wm + 16 * i + x, g));
+        issue(ring + ((s + PSLOTS - 1) % PSLOTS) * PSLOT);
+        if (group == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(PLPW * (PSLOTS - 2)));
+        bar();
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-    };
-
-#pragma unroll
-    for (int j = 0; j < PSLOTS - 1; ++j) issue(j, ring + j * PSLOT);
-    // step s: this wave's stage-s loads landed (the next PSLOTS - 2 stages
-    // may be in flight), barrier (everyone's landed, stage s-1 fully read),
-    // compute stage s, then issue stage s + PSLOTS - 1 into the slot of
-    // stage s-1 (issued after the MFMAs, the loads leave the MFMA start
-    // after the barrier undelayed: 3.72 against 3.85 ms at M = 131072,
-    // N = K = 4096; unchanged at the 8K shape)
-    for (int32_t s = 0; s < nk; ++s) {
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(PLPW * (PSLOTS - 2)));
-        lds_barrier();
-        compute(ring + (s % PSLOTS) * PSLOT);
-        issue(s + PSLOTS - 1, ring + ((s + PSLOTS - 1) % PSLOTS) * PSLOT);
+        if (group == 0) __builtin_amdgcn_s_waitcnt(vm_wait_imm(PLPW * (PSLOTS - 2)));
+        bar();
     }
+    if (group == 0) bar();                                         // as many barriers as group 1
     __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));                   // the trailing reloads land
     lds_barrier();                                                 // every wave done with the ring
 
