@@ -417,6 +417,76 @@ def test_schedule_redundant_levels_change_nothing(oracle_lib, bidir):
     assert all(np.array_equal(x, y) for x, y in zip(a, b))
 
 
+# ------------------------------------------------------ receptive field of layers
+# The English gist.science summary (section 3 "Key Contributions", item
+# "Theoretical Receptive Field Improvement") credits the periodic skips with a
+# "binary lifting" growth of the receptive field over stacked layers.  The
+# computable reading: key i - delta reaches query i through L layers of the
+# pattern exactly when some path of at most L neighbour hops joins them (the
+# repeated boolean products of the SWA worked example above; a token's own
+# position is in its window, so shorter paths count too).  In a causal pattern
+# every hop goes back by one of the pattern's offsets: 0..k in the window, or
+# a skip distance.  For k < pi a skip hop replaces at least two window hops,
+# so a shortest path covers q = delta // pi periods with skip hops and the
+# rest r = delta % pi with ceil(r / k) window hops, and:
+#   one period (pi, M):                  ceil(q / M) + ceil(r / k)
+#   doubling schedule (pi 2^l, 1),
+#   l = 0 .. R-1:                        q // 2^(R-1) + popcount(q % 2^(R-1)) + ceil(r / k)
+# -- the second is the binary expansion of q: the layers needed grow with the
+# logarithm of the distance, while a single period needs q / M of them.  Both
+# are checked against breadth-first search over the oracle's neighbour lists.
+
+def _min_layers(n, kw, pi, M, levels, i):
+    idx, _, cnt = oracle.neighbor_table(n, kw, pi, M, False, q_begin=0, q_count=n, levels=levels)
+    mask = np.zeros((n, n), bool)
+    for r in range(n):
+        mask[r, idx[r, :cnt[r]]] = True
+    depth = np.full(n, -1)
+    depth[i] = 0
+    front = np.zeros(n, bool)
+    front[i] = True
+    layer = 0
+    while front.any():
+        layer += 1
+        nxt = mask[front].any(axis=0) & (depth < 0)
+        depth[nxt] = layer
+        front = nxt
+    return depth
+
+
+def _ceil(a, b):
+    return -(-a // b)
+
+
+@pytest.mark.parametrize("n,kw,pi,M", [(700, 3, 8, 4), (500, 5, 16, 1), (400, 1, 4, 7), (300, 6, 7, 0)])
+def test_receptive_field_single_period(oracle_lib, n, kw, pi, M):
+    for i in (n - 1, n // 2 + 3):
+        depth = _min_layers(n, kw, pi, M, None, i)
+        for delta in range(0, i + 1):
+            q, r = divmod(delta, pi)
+            if M == 0:
+                want = _ceil(delta, kw)
+            else:
+                want = _ceil(q, M) + _ceil(r, kw)
+            assert depth[i - delta] == want, (i, delta)
+        assert np.all(depth[i + 1:] == -1)                 # causal: nothing after i
+
+
+@pytest.mark.parametrize("n,kw,pi,R", [(1200, 3, 8, 5), (900, 2, 5, 6), (640, 4, 9, 3)])
+def test_receptive_field_doubling_schedule_is_binary_lifting(oracle_lib, n, kw, pi, R):
+    levels = [(pi << l, 1) for l in range(1, R)]
+    top = 1 << (R - 1)
+    i = n - 1
+    depth = _min_layers(n, kw, pi, 1, levels, i)
+    for delta in range(0, i + 1):
+        q, r = divmod(delta, pi)
+        want = q // top + bin(q % top).count("1") + _ceil(r, kw)
+        assert depth[i - delta] == want, delta
+    # within R layers the periods alone reach back (2^R - 1) pi: every
+    # multiple of pi up to there, each in popcount(q) <= R layers
+    assert all(depth[i - m * pi] <= R for m in range(1, min(i // pi, (1 << R) - 1) + 1))
+
+
 def test_schedule_decode_equals_last_prefill_row(oracle_lib):
     n, d, kw = 90, 8, 4
     levels = [(6, 3), (12, 3), (24, 3)]
