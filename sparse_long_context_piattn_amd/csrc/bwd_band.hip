@@ -74,7 +74,10 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w 
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 // One record per row: D_i = <dout_i, out_i> over D/8 lanes (16 bytes each),
-// and c_i = prior - lse_i log2(e) for both key kinds.
+// and c_i = prior - lse_i log2(e) for both key kinds.  A wave takes RG
+// groups of 64 / (D/8) rows and issues all their out and dout loads before
+// the first product, so that each lane has RG x 32 bytes in flight.
+constexpr int RG = 4;
 template <int D>
 __global__ __launch_bounds__(256) void bwd_record_kernel(BwdArgs ba) {
     constexpr int LPK = D / 8, NS = 64 / LPK;
@@ -83,36 +86,45 @@ __global__ __launch_bounds__(256) void bwd_record_kernel(BwdArgs ba) {
     const int slot = lane / LPK, c = (lane % LPK) * 8;
     const int32_t h = blockIdx.y, b = blockIdx.z;
     const SeqLoc sl = seq_loc(a, b);
-    const int32_t i0 = (blockIdx.x * 4 + wave) * NS + slot;
-    const bool valid = i0 < sl.n;
-    const int32_t i = valid ? i0 : sl.n - 1;
     if (sl.n < 1) return;
-    const int64_t tok = sl.tok0 + i;
-    const int64_t orow = sl.bq * a.so.s + h * a.so.h + tok * a.so.t + c;
-    const uint4 o = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.o) + orow);
-    const uint4 g = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(ba.dout) + orow);
-    float dp = 0.0f;
-    dp = fmaf(bf16_lo(o.x), bf16_lo(g.x), dp);
-    dp = fmaf(bf16_hi(o.x), bf16_hi(g.x), dp);
-    dp = fmaf(bf16_lo(o.y), bf16_lo(g.y), dp);
-    dp = fmaf(bf16_hi(o.y), bf16_hi(g.y), dp);
-    dp = fmaf(bf16_lo(o.z), bf16_lo(g.z), dp);
-    dp = fmaf(bf16_hi(o.z), bf16_hi(g.z), dp);
-    dp = fmaf(bf16_lo(o.w), bf16_lo(g.w), dp);
-    dp = fmaf(bf16_hi(o.w), bf16_hi(g.w), dp);
+    uint4 o[RG], g[RG];
+    int32_t row[RG];
 #pragma unroll
-    for (int off = 1; off < LPK; off <<= 1) dp += __shfl_xor(dp, off, 64);
-    if (valid && (lane % LPK) == 0) {
-        const int64_t goff = sl.bq * a.sg.s + h * a.sg.h + tok * a.sg.t;
-        float pl, ps;
-        gate_priors(a.g[goff], row_span(i, sl.n, a.pat).has_skip(), &pl, &ps);
-        const float lse2 = ba.lse_in[goff] * PIATTN_LOG2E;
-        RowRec r;
-        r.D = dp;
-        r.cw = pl - lse2;
-        r.cs = ps - lse2;
-        r.ss = 0.0f;
-        reinterpret_cast<RowRec*>(ba.rowstat)[((int64_t)b * a.H + h) * a.n + i] = r;
+    for (int r = 0; r < RG; ++r) {
+        const int32_t i0 = ((blockIdx.x * 4 + wave) * RG + r) * NS + slot;
+        row[r] = i0;
+        const int32_t i = i0 < sl.n ? i0 : sl.n - 1;
+        const int64_t orow = sl.bq * a.so.s + h * a.so.h + (sl.tok0 + i) * a.so.t + c;
+        o[r] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.o) + orow);
+        g[r] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(ba.dout) + orow);
+    }
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+        float dp = 0.0f;
+        dp = fmaf(bf16_lo(o[r].x), bf16_lo(g[r].x), dp);
+        dp = fmaf(bf16_hi(o[r].x), bf16_hi(g[r].x), dp);
+        dp = fmaf(bf16_lo(o[r].y), bf16_lo(g[r].y), dp);
+        dp = fmaf(bf16_hi(o[r].y), bf16_hi(g[r].y), dp);
+        dp = fmaf(bf16_lo(o[r].z), bf16_lo(g[r].z), dp);
+        dp = fmaf(bf16_hi(o[r].z), bf16_hi(g[r].z), dp);
+        dp = fmaf(bf16_lo(o[r].w), bf16_lo(g[r].w), dp);
+        dp = fmaf(bf16_hi(o[r].w), bf16_hi(g[r].w), dp);
+#pragma unroll
+        for (int off = 1; off < LPK; off <<= 1) dp += __shfl_xor(dp, off, 64);
+        const int32_t i = row[r];
+        if (i < sl.n && (lane % LPK) == 0) {
+            const int64_t tok = sl.tok0 + i;
+            const int64_t goff = sl.bq * a.sg.s + h * a.sg.h + tok * a.sg.t;
+            float pl, ps;
+            gate_priors(a.g[goff], row_span(i, sl.n, a.pat).has_skip(), &pl, &ps);
+            const float lse2 = ba.lse_in[goff] * PIATTN_LOG2E;
+            RowRec rec;
+            rec.D = dp;
+            rec.cw = pl - lse2;
+            rec.cs = ps - lse2;
+            rec.ss = 0.0f;
+            reinterpret_cast<RowRec*>(ba.rowstat)[((int64_t)b * a.H + h) * a.n + i] = rec;
+        }
     }
 }
 
@@ -527,7 +539,7 @@ template <int D, bool BIDIR>
 hipError_t launch_t(const BwdArgs& ba, hipStream_t stream) {
     const FwdArgs& a = ba.f;
     constexpr int NS = 64 / (D / 8);
-    const dim3 rgrid((a.n + 4 * NS - 1) / (4 * NS), a.H, a.B);
+    const dim3 rgrid((a.n + 4 * RG * NS - 1) / (4 * RG * NS), a.H, a.B);
     hipLaunchKernelGGL((bwd_record_kernel<D>), rgrid, dim3(256), 0, stream, ba);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
