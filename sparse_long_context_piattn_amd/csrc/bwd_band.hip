@@ -75,8 +75,8 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 
 // One record per row: D_i = <dout_i, out_i> over D/8 lanes (16 bytes each),
 // and c_i = prior - lse_i log2(e) for both key kinds.  A wave takes RG
-// groups of 64 / (D/8) rows and issues all their out and dout loads before
-// the first product, so that each lane has RG x 32 bytes in flight.
+// groups of 64 / (D/8) rows and issues all their loads (out, dout, gate,
+// lse) before the first product: one memory round trip per wave.
 constexpr int RG = 4;
 template <int D>
 __global__ __launch_bounds__(256) void bwd_record_kernel(BwdArgs ba) {
@@ -88,15 +88,20 @@ __global__ __launch_bounds__(256) void bwd_record_kernel(BwdArgs ba) {
     const SeqLoc sl = seq_loc(a, b);
     if (sl.n < 1) return;
     uint4 o[RG], g[RG];
+    float gl[RG], ls[RG];
     int32_t row[RG];
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
         const int32_t i0 = ((blockIdx.x * 4 + wave) * RG + r) * NS + slot;
         row[r] = i0;
         const int32_t i = i0 < sl.n ? i0 : sl.n - 1;
-        const int64_t orow = sl.bq * a.so.s + h * a.so.h + (sl.tok0 + i) * a.so.t + c;
+        const int64_t tok = sl.tok0 + i;
+        const int64_t orow = sl.bq * a.so.s + h * a.so.h + tok * a.so.t + c;
+        const int64_t goff = sl.bq * a.sg.s + h * a.sg.h + tok * a.sg.t;
         o[r] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(a.o) + orow);
         g[r] = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(ba.dout) + orow);
+        gl[r] = a.g[goff];                                     // every lane of the row: one address
+        ls[r] = ba.lse_in[goff];
     }
 #pragma unroll
     for (int r = 0; r < RG; ++r) {
@@ -113,11 +118,9 @@ __global__ __launch_bounds__(256) void bwd_record_kernel(BwdArgs ba) {
         for (int off = 1; off < LPK; off <<= 1) dp += __shfl_xor(dp, off, 64);
         const int32_t i = row[r];
         if (i < sl.n && (lane % LPK) == 0) {
-            const int64_t tok = sl.tok0 + i;
-            const int64_t goff = sl.bq * a.sg.s + h * a.sg.h + tok * a.sg.t;
             float pl, ps;
-            gate_priors(a.g[goff], row_span(i, sl.n, a.pat).has_skip(), &pl, &ps);
-            const float lse2 = ba.lse_in[goff] * PIATTN_LOG2E;
+            gate_priors(gl[r], row_span(i, sl.n, a.pat).has_skip(), &pl, &ps);
+            const float lse2 = ls[r] * PIATTN_LOG2E;
             RowRec rec;
             rec.D = dp;
             rec.cw = pl - lse2;
