@@ -1,6 +1,7 @@
 """Seeded random sweep of patterns through the GPU paths, against the oracle.
 
-Each of 48 forward and 32 backward cases draws a window k, period pi, skip count M, direction, head dim,
+Each of 48 forward and 32 backward cases (PIATTN_SWEEP_FWD / PIATTN_SWEEP_BWD
+widen the seed ranges) draws a window k, period pi, skip count M, direction, head dim,
 ragged length and (sometimes) a skip schedule of up to three levels, within
 the bounds the library accepts; the prefill runs on every kernel that takes
 the pattern (split, resid, gather, f32mfma; pa.forced_kernels), and the backward on
@@ -8,6 +9,8 @@ both paths.  Tolerances as in the other parity tests: 1e-5 (fp32) / 2e-2
 (bf16) for the forward, 1e-5 / 3e-2 relative to the gradient's scale for
 the backward.
 """
+
+import os
 
 import numpy as np
 import pytest
@@ -50,7 +53,7 @@ def _forced(which, kernel, fn):
         return fn()
 
 
-@pytest.mark.parametrize("seed", range(48))
+@pytest.mark.parametrize("seed", range(int(os.environ.get("PIATTN_SWEEP_FWD", "48"))))
 def test_sweep_fwd_every_kernel(seed):
     w = _case(seed)
     x = wl.make_fwd_inputs(w, device=DEV)
@@ -72,7 +75,7 @@ def test_sweep_fwd_every_kernel(seed):
     assert ran >= 1 or w.levels
 
 
-@pytest.mark.parametrize("seed", range(32))
+@pytest.mark.parametrize("seed", range(int(os.environ.get("PIATTN_SWEEP_BWD", "32"))))
 def test_sweep_bwd_both_paths(seed):
     w = _case(100 + seed)
     if w.n > 900:
