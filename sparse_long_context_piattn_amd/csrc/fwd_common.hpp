@@ -115,8 +115,8 @@ constexpr int SW = 4;
 // Window-pass shape: WW waves of 16 query rows (a 64-row tile), KT key rows
 // per LDS slot.  Small workgroups with small slots keep several tiles in
 // flight per CU, each at a different point of its load / compute cycle:
-// 24 KB of LDS at d = 64 (four workgroups per CU, the register budget set
-// for four waves per SIMD), 48 KB at d = 128 (three per CU).  A 128-row
+// 24 KB of LDS at d = 64 (the register budget set for four waves per
+// SIMD), 33 KB at d = 128 (four per CU).  A 128-row
 // tile with 64-key slots, which halves the halo re-reads, measured slower
 // at both head dims: 97 KB of LDS at d = 128 allow one workgroup per CU,
 // whose loads then stall at every tile start.
@@ -125,8 +125,13 @@ struct WinShape {
     static constexpr int WW = 4;
     static constexpr int KT = 32;
     static constexpr int QTW = 16 * WW;
-    static constexpr int EU = D == 64 ? 4 : 3;           // waves per SIMD the register budget must allow
-    static constexpr int LDS = 6 * KT * D * 2 + QTW * 4;  // bytes: three K and three V slots, the gates
+    // K/V slot pairs in the ring: three (loads two tiles ahead) at d = 64;
+    // two (one ahead) at d = 128, where 33 KB instead of 49 KB of LDS lets
+    // four workgroups share a CU instead of three (prefill_128k 1.883-1.888
+    // -> 1.832-1.835 ms; at d = 64 two pairs measured no faster)
+    static constexpr int NSL = D == 64 ? 3 : 2;
+    static constexpr int EU = 4;                             // waves per SIMD the register budget must allow
+    static constexpr int LDS = 2 * NSL * KT * D * 2 + QTW * 4;   // bytes: NSL K and NSL V slots, the gates
 };
 
 // Window tile qt of (sequence b, head h): 64 query rows, their window keys,
@@ -142,13 +147,18 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
     static_assert(KT % (RPI * (WW / 2)) == 0, "slot split");
     static_assert(2 * KT == QT, "query rows are staged through one slot pair");
     static_assert(NB % 2 == 0, "PV runs on pairs of 16-key blocks");
+    constexpr int NSL = WinShape<D>::NSL;
+    static_assert(NSL == 2 || NSL == 3, "two or three slot pairs");
     uint16_t* const k0s = lds;
     uint16_t* const k1s = lds + KT * D;
-    uint16_t* const k2s = lds + 2 * KT * D;
-    uint16_t* const v0s = lds + 3 * KT * D;
-    uint16_t* const v1s = lds + 4 * KT * D;
-    uint16_t* const v2s = lds + 5 * KT * D;
-    float* const gls = reinterpret_cast<float*>(lds + 6 * KT * D);
+    uint16_t* const k2s = lds + 2 * KT * D;                  // NSL = 3 only
+    uint16_t* const v0s = lds + NSL * KT * D;
+    uint16_t* const v1s = lds + (NSL + 1) * KT * D;
+    uint16_t* const v2s = lds + (NSL + 2) * KT * D;          // NSL = 3 only
+    float* const gls = reinterpret_cast<float*>(lds + 2 * NSL * KT * D);
+    // the query rows are staged through the last slot pair
+    uint16_t* const kqs = NSL == 3 ? k2s : k1s;
+    uint16_t* const vqs = NSL == 3 ? v2s : v1s;
 
     int32_t n = a.n;
     int64_t tok0 = 0;
@@ -227,14 +237,15 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
         }
     };
 
-    // ---- prologue: key tiles 0 and 1, the 128 query rows through slot 2
-    // (rows 0-63 in k2s, 64-127 in v2s) and the gate logits
+    // ---- prologue: key tile 0 (and tile 1 with three pairs), the 64 query
+    // rows through the last pair (rows 0..KT-1 in its K slot, the rest in
+    // its V slot) and the gate logits
     issue(k0s, v0s, 0);
     {
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const int r0 = ((wave % (WW / 2)) * LPW + j) * RPI;
-            stage_rows(Qb, (int32_t)a.sq.t, q0 + (isv ? KT : 0) + r0, r0, isv ? v2s : k2s);
+            stage_rows(Qb, (int32_t)a.sq.t, q0 + (isv ? KT : 0) + r0, r0, isv ? vqs : kqs);
         }
         if (wave == 0) {
 #pragma unroll
@@ -244,7 +255,7 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
             }
         }
     }
-    issue(k1s, v1s, 1);
+    if (NSL == 3) issue(k1s, v1s, 1);
 
     const float sl2 = a.scale_log2;
     const int tr_row = 4 * g + (x >> 2);
@@ -253,19 +264,19 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
 
 
     // wait for tile 0, the query rows and the gates (tile 1 may be in flight)
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPW));
+    __builtin_amdgcn_s_waitcnt(vm_wait_imm(NSL == 3 ? LPW : 0));
     lds_barrier();
     bf16x8_t qf[DC];
     float pl, ps;
     {
-        const int qr = 16 * wave + x;                   // slot 2 holds rows 0..KT-1 in K, the rest in V
-        const uint16_t* qsrc = qr < KT ? k2s : v2s;
+        const int qr = 16 * wave + x;                   // the query pair holds rows 0..KT-1 in K, the rest in V
+        const uint16_t* qsrc = qr < KT ? kqs : vqs;
         const int rr = qr & (KT - 1);
 #pragma unroll
         for (int c = 0; c < DC; ++c) qf[c] = *reinterpret_cast<const bf16x8_t*>(qsrc + swr<D>(rr, 4 * c + g));
         gate_priors(gls[qr], hs, &pl, &ps);
     }
-    lds_barrier();                                       // slot 2 is free for tile 2
+    lds_barrier();                                       // the query pair is free for the next tile
 
     // the record of the lane's row, loaded now so that its latency hides
     // behind the window loop
@@ -351,10 +362,10 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
     // bf16 rows then go back through the wave's own rows of P so that each
     // store instruction writes whole rows.
     auto epilogue = [&](uint16_t* Kp, uint16_t* Vp) __attribute__((always_inline)) {
-        // stage ntiles landed (stage ntiles+1 may be in flight); the
-        // barrier also lets every wave's reload into P land when P holds no
-        // partials
-        __builtin_amdgcn_s_waitcnt(vm_wait_imm(LPW));
+        // stage ntiles landed (with three pairs stage ntiles+1 may be in
+        // flight); the barrier also lets every wave's reload into P land
+        // when P holds no partials
+        __builtin_amdgcn_s_waitcnt(vm_wait_imm(NSL == 3 ? LPW : 0));
         lds_barrier();
         uint16_t* prow = (16 * wave < KT ? Kp : Vp);
         const int qr = 16 * wave + x, rr = qr & (KT - 1), rr0 = (16 * wave) & (KT - 1);
@@ -405,16 +416,39 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
         issue(Kn, Vn, t + 2);
         compute(t, Kc, Vc);
     };
-    for (int32_t t = 0; t < ntiles; t += 3) {
-        step(t, k0s, v0s, k2s, v2s);
-        if (t + 1 >= ntiles) break;
-        step(t + 1, k1s, v1s, k0s, v0s);
-        if (t + 2 >= ntiles) break;
-        step(t + 2, k2s, v2s, k1s, v1s);
+    // two pairs: step t waits for all of its loads (tile t, issued one step
+    // before), barrier (tile t-1 fully read), issues stage t+1 into the pair
+    // of tile t-1, computes tile t
+    auto step2 = [&](int32_t t, const uint16_t* Kc, const uint16_t* Vc, uint16_t* Kn, uint16_t* Vn)
+        __attribute__((always_inline)) {
+        if (t > 0) {
+            __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
+            lds_barrier();
+        }
+        issue(Kn, Vn, t + 1);
+        compute(t, Kc, Vc);
+    };
+    if constexpr (NSL == 3) {
+        for (int32_t t = 0; t < ntiles; t += 3) {
+            step(t, k0s, v0s, k2s, v2s);
+            if (t + 1 >= ntiles) break;
+            step(t + 1, k1s, v1s, k0s, v0s);
+            if (t + 2 >= ntiles) break;
+            step(t + 2, k2s, v2s, k1s, v1s);
+        }
+        // stage ntiles went to slot ntiles % 3
+        const int pslot = ntiles % 3;
+        epilogue(pslot == 0 ? k0s : pslot == 1 ? k1s : k2s, pslot == 0 ? v0s : pslot == 1 ? v1s : v2s);
+    } else {
+        for (int32_t t = 0; t < ntiles; t += 2) {
+            step2(t, k0s, v0s, k1s, v1s);
+            if (t + 1 >= ntiles) break;
+            step2(t + 1, k1s, v1s, k0s, v0s);
+        }
+        // stage ntiles went to pair ntiles % 2
+        const int pslot = ntiles % 2;
+        epilogue(pslot == 0 ? k0s : k1s, pslot == 0 ? v0s : v1s);
     }
-    // stage ntiles went to slot ntiles % 3
-    const int pslot = ntiles % 3;
-    epilogue(pslot == 0 ? k0s : pslot == 1 ? k1s : k2s, pslot == 0 ? v0s : pslot == 1 ? v1s : v2s);
     __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));         // loads past the end land before the LDS retires
 }
 
