@@ -17,8 +17,8 @@
 // from L2.  The output projection is a GEMM over M = tokens, N = Dout,
 // K = H d with the head concatenation folded into the A operand's addresses
 // (o stays in the attention's [B, H, n, d] layout, any strides): 256 x 256
-// tiles, K in chunks of 32 (always inside one head), a ring of five LDS
-// slots filled four stages ahead by LDS-direct loads, XOR-swizzled rows so
+// or 320 x 256 tiles, K in chunks of 32 (always inside one head), a ring of
+// five or four LDS slots filled ahead by LDS-direct loads, XOR-swizzled rows so
 // that the MFMA operand reads are free of bank conflicts, two groups of four
 // waves that alternate between reading a chunk's operands and running its
 // MFMAs, and an epilogue that turns the accumulators into whole bf16 rows
@@ -124,40 +124,48 @@ __global__ __launch_bounds__(256) void gate_f32_kernel(GateArgs a) {
 }
 
 // ------------------------------------------------------------ output projection
-constexpr int PM = 256, PN = 256, PK = 32;   // tile rows (tokens), columns (outputs), k-chunk
-constexpr int PSLOT = (PM + PN) * PK;        // elements of one ring slot (A rows, then W rows)
+constexpr int PN = 256, PK = 32;             // tile columns (outputs), k-chunk
 constexpr int PW = 8;                        // waves per workgroup (two per SIMD)
-constexpr int PLPW = 4;                      // 1 KB loads per wave per stage
-constexpr int PSLOTS = 5;                    // LDS ring slots (160 KB): loads run four stages ahead
+// WB 16-row blocks per wave: TM = 64 WB tile rows (tokens); the ring slot
+// holds TM A rows and PN W rows; as many slots as fit 160 KB
+template <int WB>
+struct ProjTile {
+    static constexpr int TM = 64 * WB;
+    static constexpr int SLOT = (TM + PN) * PK;
+    static constexpr int SLOTS = (160 * 1024) / (SLOT * 2);
+};
 
 // Element offset of 16-byte chunk c (of 4) of row r in a [rows][32] bf16
 // tile, XOR-swizzled by (r / 2) % 4: the 16 rows x 4 chunks of an MFMA
 // operand read then fall on distinct banks.
 __device__ __forceinline__ int psw(int r, int c) { return r * PK + ((c ^ ((r >> 1) & 3)) << 3); }
 
-// 256 x 256 tile, eight waves of 64 x 128 (4 x 8 MFMA blocks), two per
-// SIMD: per k-chunk a wave reads 12 operand rows of 16 bytes for 32 MFMAs.
-// The LDS then carries 96 KB of operand reads and 32 KB of staging writes
-// per chunk of the tile, as long at about 128 bytes a clock as the chunk's
-// 64 MFMAs per SIMD.  The two waves of a SIMD work in opposite phases: waves
-// 0-3 run the MFMAs of chunk s while waves 4-7 read the operands of chunk s
-// into registers, then they swap at a barrier, so each SIMD's matrix unit is
-// fed by one wave while the LDS serves the other (a wave's own reads in
-// flight slow its MFMA issue, the other wave's do not).
+// TM x 256 tile (TM = 256 or 320), eight waves of 16 WB x 128 (WB x 8 MFMA
+// blocks, WB = 4 or 5), two per SIMD: per k-chunk a wave reads WB + 8
+// operand rows of 16 bytes for 8 WB MFMAs.  A wave's LDS reads arrive at
+// about 20 bytes a clock, so its 12 KB (WB = 4) take a little longer than
+// its 32 MFMAs; WB = 5 brings the two closer.  The two waves of a SIMD work
+// in opposite phases: waves 0-3 run the MFMAs of chunk s while waves 4-7
+// read the operands of chunk s into registers, then they swap at a barrier,
+// so each SIMD's matrix unit is fed by one wave while the LDS serves the
+// other (a wave's own reads in flight slow its MFMA issue, the other
+// wave's do not).
 // Tile order: groups of GM row tiles, rows fastest inside a group, so that
 // each XCD's run of 32 consecutive tiles is about 8 row tiles x 4 column
 // tiles sharing their A and W slabs in that XCD's L2.
 constexpr int32_t GM = 8;
 
+template <int WB>
 __global__ __launch_bounds__(PW * 64, 1) void out_proj_mfma_kernel(ProjArgs a, int32_t mtiles, int32_t ntiles,
                                                                  int32_t total) {
-    __shared__ __attribute__((aligned(16))) uint16_t ring[PSLOTS * PSLOT];
+    constexpr int TM = ProjTile<WB>::TM, PS = ProjTile<WB>::SLOTS, SLOT = ProjTile<WB>::SLOT;
+    __shared__ __attribute__((aligned(16))) uint16_t ring[PS * SLOT];
     const int32_t logical = xcd_logical(blockIdx.x, total);
     const int32_t gsize = GM * ntiles, grp = logical / gsize, first = grp * GM;
     const int32_t gm = imin32(mtiles - first, GM), w_in = logical - grp * gsize;
     const int32_t mt = first + w_in % gm, nt = w_in / gm;
     const int64_t M = (int64_t)a.B * a.n;
-    const int64_t m0 = (int64_t)mt * PM;
+    const int64_t m0 = (int64_t)mt * TM;
     const int32_t n0 = nt * PN;
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -167,13 +175,13 @@ __global__ __launch_bounds__(PW * 64, 1) void out_proj_mfma_kernel(ProjArgs a, i
 
     // ---- staging.  One 1 KB load covers 16 rows x 64 bytes; lane l fills
     // row l / 4, physical chunk l % 4 = logical chunk (l % 4) ^ ((row / 2) % 4).
-    // Waves 0-3 load the A rows (tokens), waves 4-7 the W rows (outputs),
-    // 64 rows each.
+    // Waves 0-3 load the A rows (tokens), TM / 4 each, waves 4-7 the W rows
+    // (outputs), 64 each.
     const bool isw = wave >= PW / 2;
-    const int rbase = (wave & 3) * 64;
-    uint32_t voff[PLPW];
+    const int rbase = (wave & 3) * (isw ? 64 : TM / 4);
+    uint32_t voff[WB];
 #pragma unroll
-    for (int j = 0; j < PLPW; ++j) {
+    for (int j = 0; j < WB; ++j) {
         const int rr = rbase + 16 * j + lane / 4;                 // tile row of this lane's 16 bytes
         const int lc = (lane % 4) ^ ((rr >> 1) & 3);
         if (!isw) {
@@ -193,9 +201,10 @@ __global__ __launch_bounds__(PW * 64, 1) void out_proj_mfma_kernel(ProjArgs a, i
     const uint16_t* src = isw ? static_cast<const uint16_t*>(a.w) : static_cast<const uint16_t*>(a.o);
     int32_t next = 0, kcol = 0;
     auto issue = [&](uint16_t* slot) __attribute__((always_inline)) {
-        uint16_t* dst = slot + (isw ? PM * PK : 0) + rbase * PK;
+        uint16_t* dst = slot + (isw ? TM * PK : 0) + rbase * PK;
 #pragma unroll
-        for (int j = 0; j < PLPW; ++j) dma16(src, voff[j], lds_addr(dst + 16 * j * PK));
+        for (int j = 0; j < WB; ++j)
+            if (!isw || j < 4) dma16(src, voff[j], lds_addr(dst + 16 * j * PK));
         if (next < nk - 1) {
             ++next;
             kcol += PK;
@@ -208,47 +217,54 @@ __global__ __launch_bounds__(PW * 64, 1) void out_proj_mfma_kernel(ProjArgs a, i
         }
     };
 
-    f32x4_t acc[4][8];
+    f32x4_t acc[WB][8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < WB; ++i)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    const int wm = (wave >> 1) * 64, wn = (wave & 1) * 128;       // the wave's 64 x 128 sub-tile
+    const int wm = (wave >> 1) * 16 * WB, wn = (wave & 1) * 128;  // the wave's 16 WB x 128 sub-tile
 
     // Phases, one barrier after each: waves 0-3 (group 0) take the read
     // phase of chunk s in phase 2s and its MFMAs in phase 2s+1; waves 4-7
     // (group 1) one phase later.  The read phase of chunk s also issues the
-    // wave's loads of stage s+4 into the slot of chunk s-1, which both groups
-    // finished reading by phase 2s-1.  Stage c must have landed for every
-    // wave before phase 2c: each wave waits for its own share at the end of
-    // phase 2c-1 (group 0 after the MFMAs of c-1, group 1 after reading c-1),
-    // when the stages after c that it has issued are c+1..c+3.
+    // wave's loads of stage s+PS-1 into the slot of chunk s-1, which both
+    // groups finished reading by phase 2s-1.  Stage c must have landed for
+    // every wave before phase 2c: each wave waits for its own share at the
+    // end of phase 2c-1 (group 0 after the MFMAs of c-1, group 1 after
+    // reading c-1), when the stages after c that it has issued are
+    // c+1..c+PS-2.
     const int group = wave >> 2;
     auto bar = [&]() __attribute__((always_inline)) {
         __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
     };
-    bf16x8_t av[4], bv[8];
+    bf16x8_t av[WB], bv[8];
+    // a wave's loads per stage: WB (A rows) or 4 (W rows); the waits below
+    // leave the wave's PS - 2 newest stages in flight
+    auto wait_own = [&]() __attribute__((always_inline)) {
+        if (isw) __builtin_amdgcn_s_waitcnt(vm_wait_imm(4 * (PS - 2)));
+        else __builtin_amdgcn_s_waitcnt(vm_wait_imm(WB * (PS - 2)));
+    };
 #pragma unroll
-    for (int j = 0; j < PSLOTS - 1; ++j) issue(ring + j * PSLOT);
-    __builtin_amdgcn_s_waitcnt(vm_wait_imm(PLPW * (PSLOTS - 2)));  // own stage 0
+    for (int j = 0; j < PS - 1; ++j) issue(ring + j * SLOT);
+    wait_own();                                                    // own stage 0
     bar();
     if (group == 1) bar();
     for (int32_t s = 0; s < nk; ++s) {
-        const uint16_t* slot = ring + (s % PSLOTS) * PSLOT;
+        const uint16_t* slot = ring + (s % PS) * SLOT;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bv[j] = *reinterpret_cast<const bf16x8_t*>(slot + PM * PK + psw(wn + 16 * j + x, g));
+        for (int j = 0; j < 8; ++j) bv[j] = *reinterpret_cast<const bf16x8_t*>(slot + TM * PK + psw(wn + 16 * j + x, g));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) av[i] = *reinterpret_cast<const bf16x8_t*>(slot + psw(wm + 16 * i + x, g));
-        issue(ring + ((s + PSLOTS - 1) % PSLOTS) * PSLOT);
-        if (group == 1) __builtin_amdgcn_s_waitcnt(vm_wait_imm(PLPW * (PSLOTS - 2)));
+        for (int i = 0; i < WB; ++i) av[i] = *reinterpret_cast<const bf16x8_t*>(slot + psw(wm + 16 * i + x, g));
+        issue(ring + ((s + PS - 1) % PS) * SLOT);
+        if (group == 1) wait_own();
         bar();
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < WB; ++i)
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av[i], bv[j], acc[i][j], 0, 0, 0);
-        if (group == 0) __builtin_amdgcn_s_waitcnt(vm_wait_imm(PLPW * (PSLOTS - 2)));
+        if (group == 0) wait_own();
         bar();
     }
     if (group == 0) bar();                                         // as many barriers as group 1
@@ -267,9 +283,11 @@ __global__ __launch_bounds__(PW * 64, 1) void out_proj_mfma_kernel(ProjArgs a, i
         bias[j] = (a.bias && col < a.Dout) ? a.bias[col] : 0.0f;
     }
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
+    for (int half = 0; half < (WB + 1) / 2; ++half) {
+        const int nb = 2 * half + 1 < WB ? 2 : 1;                 // 16-row blocks in this pass
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i) {
+            if (2 * half + i >= WB) break;
 #pragma unroll
             for (int j = 0; j < 8; ++j)
 #pragma unroll
@@ -278,9 +296,11 @@ __global__ __launch_bounds__(PW * 64, 1) void out_proj_mfma_kernel(ProjArgs a, i
                     tile[rr * 128 + ((((cc >> 3) ^ (rr & 15)) << 3) | (cc & 7))] =
                         (uint16_t)(cvt_pk_bf16(acc[2 * half + i][j][r] + bias[j], 0.0f) & 0xffffu);
                 }
+        }
         lds_barrier();
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
+            if (q >= 4 * nb) break;
             const int rr = 4 * q + lane / 16, ch = lane % 16;      // 4 rows x 16 chunks per instruction
             const int64_t t = m0 + wm + 32 * half + rr;
             const int32_t col = n0 + wn + 8 * ch;
@@ -352,11 +372,24 @@ bool out_proj_mfma_ok(int dtype, const ProjArgs& a) {
 hipError_t launch_out_proj(int dtype, const ProjArgs& a, hipStream_t stream) {
     const int64_t M = (int64_t)a.B * a.n;
     if (out_proj_mfma_ok(dtype, a)) {
-        const int64_t mtiles = (M + PM - 1) / PM, ntiles = ((int64_t)a.Dout + PN - 1) / PN;
+        // 80-row waves (320-row tiles) when there are enough tiles for the
+        // grid's last round not to matter: at M = 131072, N = K = 4096 3.54
+        // against 3.68 ms; at M = 32768, N = K = 1024 (412 tiles against
+        // 512) 0.096 against 0.087 ms
+        const int64_t ntiles = ((int64_t)a.Dout + PN - 1) / PN;
+        const int64_t mt5 = (M + ProjTile<5>::TM - 1) / ProjTile<5>::TM;
+        if (mt5 * ntiles >= 2048) {
+            const int64_t total = mt5 * ntiles;
+            if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
+            hipLaunchKernelGGL(out_proj_mfma_kernel<5>, dim3((uint32_t)total), dim3(PW * 64), 0, stream, a,
+                               (int32_t)mt5, (int32_t)ntiles, (int32_t)total);
+            return hipGetLastError();
+        }
+        const int64_t mtiles = (M + ProjTile<4>::TM - 1) / ProjTile<4>::TM;
         const int64_t total = mtiles * ntiles;
         if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(out_proj_mfma_kernel, dim3((uint32_t)total), dim3(PW * 64), 0, stream, a, (int32_t)mtiles,
-                           (int32_t)ntiles, (int32_t)total);
+        hipLaunchKernelGGL(out_proj_mfma_kernel<4>, dim3((uint32_t)total), dim3(PW * 64), 0, stream, a,
+                           (int32_t)mtiles, (int32_t)ntiles, (int32_t)total);
         return hipGetLastError();
     }
     const int64_t blocks = (M * a.Dout + 255) / 256;

@@ -123,6 +123,26 @@ def test_out_proj_matches_oracle(case):
     _check(y, ref, absref, dt == torch.bfloat16, "out_proj " + name)
 
 
+def test_out_proj_320_row_tiles():
+    """At least 2048 tiles of 320 rows (here 129 x 16): the dispatch takes the
+    80-row waves; a ragged last row tile, checked on sampled rows (the first
+    two tiles, the last 700 rows, 2000 more at random)."""
+    B, H, n, d, Dout = 1, 2, 40_960 + 77, 32, 4096
+    o = _rand((B, n, H, d), 30, torch.bfloat16).permute(0, 2, 1, 3)
+    w = _rand((Dout, H * d), 31, torch.bfloat16, (H * d) ** -0.5)
+    bias = _rand((Dout,), 32, torch.float32)
+    print("out_proj 320-row tiles", flush=True)
+    y = pa.out_proj(o, w, bias)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(33)
+    rows = np.unique(np.concatenate([np.arange(640), np.arange(n - 700, n), rng.integers(0, n, 2000)]))
+    oh = host_array(o.contiguous())[:, :, rows, :]
+    ref = oproj.out_proj(oh, host_array(w), bias.cpu().numpy())
+    absref = oproj.out_proj(np.abs(oproj._f64(oh)), np.abs(oproj._f64(host_array(w))))
+    got = y[:, torch.from_numpy(rows).to(DEV), :]
+    _check(got, ref, absref, True, "out_proj 320-row tiles")
+
+
 def test_out_proj_packed_and_padded_weights():
     """Packed [T, H, d] attention output (varlen) gives [T, Dout]; a weight
     matrix with a row stride above H*d is read through ldw."""
