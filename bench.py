@@ -813,7 +813,7 @@ def main():
         return pmc_summary(args)
 
     if args.gpus != 1:
-        log("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        log("bench.py runs on exactly one GPU: the library has no multi-GPU path "
             "(a (sequence, head) shard per GPU would need no exchange; see the design notes).")
         sys.exit(2)
 

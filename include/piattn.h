@@ -60,7 +60,7 @@ typedef enum {
 enum {
     PIATTN_OK = 0,
     PIATTN_EINVAL = 1,       /* bad pointer, size, stride, alignment or pattern */
-    PIATTN_EUNSUPPORTED = 2, /* valid request this build does not implement */
+    PIATTN_EUNSUPPORTED = 2, /* valid request the library does not implement */
     PIATTN_EWORKSPACE = 3,   /* workspace missing or too small */
     PIATTN_EHIP = 4          /* the HIP runtime reported a launch error */
 };
