@@ -15,6 +15,8 @@
 // part that share only lse_i and D_i, so the two parts run separately.
 //
 // bwd_record_kernel: each row's record {D_i, c_i (window), c_i (skip)}.
+// When every residue view is one tile long the skip pass forms these
+// records itself (REC below) and this kernel does not run.
 //
 // bwd_band_kernel: a view is the rows of one sequence at positions
 // base + p step, p = 0 .. L-1: the whole sequence (step 1) for the window,
@@ -134,8 +136,13 @@ __global__ __launch_bounds__(256) void bwd_record_kernel(BwdArgs ba) {
 // MASKED: the skip multiples are a schedule's mask (skip pass only); a
 // separate instantiation keeps the mask test out of the other kernels'
 // register budget.
+// REC (skip pass only, every view one tile long): the pass forms the row
+// records itself, in place of bwd_record_kernel.  Its phase B then reads
+// only its own tile's records; a prologue computes them into LDS from out,
+// dout, the gate and lse, and finishA stores each own row's whole record
+// (the window pass reads them there).
 // TB: rows per tile, 16 per wave.
-template <int D, bool SKIP, bool BIDIR, bool MASKED, int TB>
+template <int D, bool SKIP, bool BIDIR, bool MASKED, bool REC, int TB>
 __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdArgs ba, int32_t step, int32_t nres,
                                                                             int32_t tiles, int32_t total,
                                                                             int32_t merge) {
@@ -146,10 +153,15 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
     __shared__ __attribute__((aligned(16))) uint16_t x1s[BT * D];
     __shared__ __attribute__((aligned(16))) uint16_t y0s[BT * D];
     __shared__ __attribute__((aligned(16))) uint16_t y1s[BT * D];
-    __shared__ __attribute__((aligned(16))) float c0s[BT];
-    __shared__ __attribute__((aligned(16))) float c1s[BT];
-    __shared__ __attribute__((aligned(16))) float d0s[BT];
-    __shared__ __attribute__((aligned(16))) float d1s[BT];
+    // the stages' records (c and D of the query rows: two slots each), or
+    // with REC those of the tile's own rows (c, then D)
+    __shared__ __attribute__((aligned(16))) float recs[(REC ? 2 : 4) * BT];
+    // (REC: the stages load no records, and both stage slots name the own
+    // tile's c and D)
+    float* const c0s = recs;
+    float* const c1s = recs + (REC ? 0 : 1) * BT;
+    float* const d0s = recs + (REC ? 1 : 2) * BT;
+    float* const d1s = recs + (REC ? 1 : 3) * BT;
 
     const FwdArgs& a = ba.f;
     // Each pass walks its tiles in the reverse of the order of the kernel
@@ -232,7 +244,7 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
             const int r0 = (wave % (NW / 2)) * 32 + j * RPI;
             stage_rows(src, rst, tb + r0, r0, dst, lane);
         }
-        if (!pa && wave % (NW / 2) == 0) {
+        if (!REC && !pa && wave % (NW / 2) == 0) {
             const uint32_t field = wave == 0 ? (SKIP ? 8u : 4u) : 0u;
 #pragma unroll
             for (int q = 0; q < BT / 64; ++q) {
@@ -255,7 +267,42 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
         qf[c] = *reinterpret_cast<const bf16x8_t*>(Qb + pc * qst + 32 * c + 8 * g);
         of[c] = *reinterpret_cast<const bf16x8_t*>(Ob + pc * ost + 32 * c + 8 * g);
     }
-    const RowRec own = Rb[(int64_t)pc * step];
+    RowRec own;
+    if constexpr (REC) {
+        // The own rows' records: D_i = <dout_i, out_i> (the lane's 8 DC
+        // values of row pc, then the four lanes of the row) and
+        // c_i = prior - lse_i log2(e).
+        const uint16_t* Xb = static_cast<const uint16_t*>(a.o) + sq.bq * a.so.s + h * a.so.h + r0tok * a.so.t;
+        float dp = 0.0f;
+#pragma unroll
+        for (int c = 0; c < DC; ++c) {
+            const uint4 ov = *reinterpret_cast<const uint4*>(Xb + pc * ost + 32 * c + 8 * g);
+            const uint4 dv = __builtin_bit_cast(uint4, of[c]);
+            dp = fmaf(bf16_lo(ov.x), bf16_lo(dv.x), dp);
+            dp = fmaf(bf16_hi(ov.x), bf16_hi(dv.x), dp);
+            dp = fmaf(bf16_lo(ov.y), bf16_lo(dv.y), dp);
+            dp = fmaf(bf16_hi(ov.y), bf16_hi(dv.y), dp);
+            dp = fmaf(bf16_lo(ov.z), bf16_lo(dv.z), dp);
+            dp = fmaf(bf16_hi(ov.z), bf16_hi(dv.z), dp);
+            dp = fmaf(bf16_lo(ov.w), bf16_lo(dv.w), dp);
+            dp = fmaf(bf16_hi(ov.w), bf16_hi(dv.w), dp);
+        }
+        own.D = sum4(dp);
+        const int32_t iseq = res + pc * step;
+        const int64_t goff = sq.bq * a.sg.s + h * a.sg.h + (sq.tok0 + iseq) * a.sg.t;
+        float pl, ps;
+        gate_priors(a.g[goff], row_span(iseq, sq.n, a.pat).has_skip(), &pl, &ps);
+        const float lse2 = ba.lse_in[goff] * PIATTN_LOG2E;
+        own.cw = pl - lse2;
+        own.cs = ps - lse2;
+        own.ss = 0.0f;
+        if (g == 0) {                                   // read by phase B after its first barrier
+            recs[16 * wave + x] = own.cs;
+            recs[BT + 16 * wave + x] = own.D;
+        }
+    } else {
+        own = Rb[(int64_t)pc * step];
+    }
     const float cq = SKIP ? own.cs : own.cw;
 
     const float sl2 = a.scale_log2;
@@ -399,7 +446,11 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
         }
         if (!mine) return;
         if (g == 0) {
-            if (SKIP) {
+            if (REC) {
+                RowRec rr = own;
+                rr.ss = srow;
+                Rb[(int64_t)pme * step] = rr;
+            } else if (SKIP) {
                 Rb[(int64_t)pme * step].ss = srow;
             } else {
                 const int64_t goff = sq.bq * a.sg.s + h * a.sg.h + (sq.tok0 + pme) * a.sg.t;
@@ -526,12 +577,13 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
 #pragma unroll
     for (int bb = 0; bb < DB; ++bb) dka[bb] = dva[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     for (int32_t s = NA; s < N; ++s) {
+        const int32_t qt = ilo + s - NA;                // the stage's query tile
         if (s & 1) {
             waitissue(s, x0s, y0s, c0s, d0s);
-            computeB((ilo + s - NA) * BT, x1s, y1s, c1s, d1s);
+            computeB(qt * BT, x1s, y1s, c1s, d1s);
         } else {
             waitissue(s, x1s, y1s, c1s, d1s);
-            computeB((ilo + s - NA) * BT, x0s, y0s, c0s, d0s);
+            computeB(qt * BT, x0s, y0s, c0s, d0s);
         }
     }
     lds_barrier();
@@ -542,19 +594,30 @@ template <int D, bool BIDIR>
 hipError_t launch_t(const BwdArgs& ba, hipStream_t stream) {
     const FwdArgs& a = ba.f;
     constexpr int NS = 64 / (D / 8);
-    const dim3 rgrid((a.n + 4 * RG * NS - 1) / (4 * RG * NS), a.H, a.B);
-    hipLaunchKernelGGL((bwd_record_kernel<D>), rgrid, dim3(256), 0, stream, ba);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const bool skips = a.pat.M >= a.pat.mlo;
+    // The skip pass forms the records itself when every residue view is one
+    // tile long (phase B then needs only the tile's own rows).  With longer
+    // views it would recompute its neighbour tiles' records: measured slower
+    // at prefill_128k (d = 128, 8 tiles per view: 6.37 against 6.29 ms), so
+    // there, and without skips, the record kernel runs.
+    const bool rec = skips && (a.n - 1) / a.pat.pi + 1 <= BT;
+    hipError_t e = hipSuccess;
+    if (!rec) {
+        const dim3 rgrid((a.n + 4 * RG * NS - 1) / (4 * RG * NS), a.H, a.B);
+        hipLaunchKernelGGL((bwd_record_kernel<D>), rgrid, dim3(256), 0, stream, ba);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (skips) {
         const int32_t nres = imin32(a.pat.pi, a.n);
         const int32_t lmax = (a.n - 1) / a.pat.pi + 1;
         const int32_t tiles = (lmax + BT - 1) / BT;
         const int64_t total = (int64_t)tiles * nres * a.H * a.B;
         if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-        auto kern = a.pat.masked ? bwd_band_kernel<D, true, BIDIR, true, BT>
-                                 : bwd_band_kernel<D, true, BIDIR, false, BT>;
+        auto kern = a.pat.masked ? (rec ? bwd_band_kernel<D, true, BIDIR, true, true, BT>
+                                        : bwd_band_kernel<D, true, BIDIR, true, false, BT>)
+                                 : (rec ? bwd_band_kernel<D, true, BIDIR, false, true, BT>
+                                        : bwd_band_kernel<D, true, BIDIR, false, false, BT>);
         hipLaunchKernelGGL(kern, dim3((uint32_t)total), dim3(BT * 4), 0, stream, ba, a.pat.pi, nres, tiles,
                            (int32_t)total, 0);
         e = hipGetLastError();
@@ -563,7 +626,7 @@ hipError_t launch_t(const BwdArgs& ba, hipStream_t stream) {
     const int32_t tiles = (a.n + BTW - 1) / BTW;
     const int64_t total = (int64_t)tiles * a.H * a.B;
     if (total > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((bwd_band_kernel<D, false, BIDIR, false, BTW>), dim3((uint32_t)total), dim3(BTW * 4), 0, stream,
+    hipLaunchKernelGGL((bwd_band_kernel<D, false, BIDIR, false, false, BTW>), dim3((uint32_t)total), dim3(BTW * 4), 0, stream,
                        ba, 1, 1, tiles, (int32_t)total, skips ? 1 : 0);
     return hipGetLastError();
 }

@@ -84,6 +84,17 @@ CASES = [
     ("bf16_d128_M1", "bf16", 2, 1, 300, 128, 10, 64, 1, False),
     ("bf16_d64_n63", "bf16", 1, 2, 63, 64, 7, 9, 6, True),
     ("bf16_d64_k200_pi3", "bf16", 1, 1, 400, 64, 200, 3, 100, False),
+    # either side of the length at which the band skip pass forms the row
+    # records itself (every residue view one 64-row tile: n <= 64 pi) instead
+    # of reading them from the record kernel
+    ("bf16_d64_views_one_tile", "bf16", 1, 2, 448, 64, 5, 7, 9, False),
+    ("bf16_d64_views_one_row_more", "bf16", 1, 2, 449, 64, 5, 7, 9, False),
+    ("bf16_d64_bidir_views_one_tile", "bf16", 1, 2, 448, 64, 5, 7, 9, True),
+    ("bf16_d64_bidir_views_one_row_more", "bf16", 1, 2, 449, 64, 5, 7, 9, True),
+    ("bf16_d128_views_one_tile", "bf16", 1, 2, 320, 128, 4, 5, 7, False),
+    ("bf16_d128_views_one_row_more", "bf16", 1, 2, 321, 128, 4, 5, 7, False),
+    ("bf16_d128_bidir_views_one_tile", "bf16", 1, 2, 320, 128, 4, 5, 7, True),
+    ("bf16_d128_bidir_views_one_row_more", "bf16", 1, 2, 321, 128, 4, 5, 7, True),
 ]
 
 # bf16_d64_k200_pi3 (causal, first skip multiple 67) gives the skip pass a
