@@ -77,10 +77,11 @@ __device__ __forceinline__ int swz(int r, int c) {
     return r * D + ((c ^ (r & 7)) << 3);
 }
 
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
+// LDS byte address of a pointer into a __shared__ array: the low 32 bits of
+// its flat address (the shared aperture sits in the high half).  A cast to
+// the LDS address space would add a null check (a compare and a select per
+// address; -O1 builds even lower it to a compare the gfx950 backend rejects).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)p; }
 
 // Workgroup barrier for LDS traffic only: waits for this wave's LDS
 // operations, not for its loads in flight.
