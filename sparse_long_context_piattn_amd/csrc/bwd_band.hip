@@ -515,11 +515,14 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
             }
         }
     };
-    auto finishB = [&](uint16_t* regk, uint16_t* regv) __attribute__((always_inline)) {
+    // loaded: the partial rows were issued into the regions already
+    auto finishB = [&](uint16_t* regk, uint16_t* regv, bool loaded) __attribute__((always_inline)) {
         if (!wave_live) return;
         if (!SKIP && merge) {
-            partial_in(dKb, kst, regk);
-            partial_in(dVb, vst, regv);
+            if (!loaded) {
+                partial_in(dKb, kst, regk);
+                partial_in(dVb, vst, regv);
+            }
             __builtin_amdgcn_s_waitcnt(vm_wait_imm(0));
         }
         acc_to_lds(dka, ba.scale, regk);
@@ -576,18 +579,33 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
     }
 #pragma unroll
     for (int bb = 0; bb < DB; ++bb) dka[bb] = dva[bb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    // The window pass adds the skip pass's dk and dv partials.  During the
+    // last phase-B step the slot that does not hold its stage is free, so
+    // each wave loads its partial rows into its region there one step early,
+    // under that step's MFMAs, instead of after the last barrier.
+    const bool pre = !SKIP && merge && N > NA;           // workgroup-uniform
+    uint16_t* const fk = ((N - 1) & 1) ? x0s : x1s;      // the free slot at step N-1
+    uint16_t* const fv = ((N - 1) & 1) ? y0s : y1s;
     for (int32_t s = NA; s < N; ++s) {
         const int32_t qt = ilo + s - NA;                // the stage's query tile
-        if (s & 1) {
+        if (s & 1)
             waitissue(s, x0s, y0s, c0s, d0s);
-            computeB(qt * BT, x1s, y1s, c1s, d1s);
-        } else {
+        else
             waitissue(s, x1s, y1s, c1s, d1s);
-            computeB(qt * BT, x0s, y0s, c0s, d0s);
+        if (pre && s == N - 1 && wave_live) {
+            partial_in(dKb, kst, fk + 16 * wave * D);
+            partial_in(dVb, vst, fv + 16 * wave * D);
         }
+        if (s & 1)
+            computeB(qt * BT, x1s, y1s, c1s, d1s);
+        else
+            computeB(qt * BT, x0s, y0s, c0s, d0s);
     }
     lds_barrier();
-    finishB(x0s + 16 * wave * D, y0s + 16 * wave * D);
+    if (pre)
+        finishB(fk + 16 * wave * D, fv + 16 * wave * D, true);
+    else
+        finishB(x0s + 16 * wave * D, y0s + 16 * wave * D, false);
 }
 
 template <int D, bool BIDIR>
