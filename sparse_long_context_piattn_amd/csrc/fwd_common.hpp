@@ -104,8 +104,8 @@ __device__ __forceinline__ void store_skip_chunk(uint16_t* tt, const f32x4_t (&s
         const int r = o / (2 * D), cc = (o % (2 * D)) / 16;
         const uint4 val = *reinterpret_cast<const uint4*>(tt + swr<D>(r, cc));
         const int32_t tr = 16 * c + r;
-        if (tr < pr && row_has_skip<BIDIR>(tr, pr, mlo, M))
-            *reinterpret_cast<uint4*>(Ob + (int64_t)(res + tr * pi) * sot + 8 * cc) = val;
+        if (tr < pr && row_has_skip<BIDIR>(tr, pr, mlo, M))   // read again only by the window pass
+            store_nt16(Ob + (int64_t)(res + tr * pi) * sot + 8 * cc, val);
     }
 }
 
@@ -205,7 +205,10 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
     const bool isv = wave >= WW / 2;
     const uint16_t* src0 = isv ? Vb : Kb;
     const int32_t st = isv ? (int32_t)a.sv.t : (int32_t)a.sk.t;
-    auto stage_rows = [&](const uint16_t* src, int32_t stt, int32_t s0, int r0, uint16_t* dst)
+    // stream: rows this tile alone reads (its query and skip-partial rows),
+    // loaded with the non-temporal hint; the key rows, which the next tile
+    // reads again from L2 as its halo, without it
+    auto stage_rows = [&](const uint16_t* src, int32_t stt, int32_t s0, int r0, uint16_t* dst, bool stream)
         __attribute__((always_inline)) {
         const int rl = r0 + lane / CH;
         const int lc = ((lane % CH) ^ (rl & 7)) << 3;
@@ -213,7 +216,10 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
         const uint16_t* ub = inside ? src + (int64_t)s0 * stt : src;
         const uint32_t off = inside ? (uint32_t)((lane / CH) * stt + lc)
                                     : (uint32_t)(imin32(imax32(s0 + lane / CH, 0), n - 1) * stt + lc);
-        dma16(ub, off * 2u, lds_addr(dst + r0 * D));
+        if (stream)
+            dma16<true>(ub, off * 2u, lds_addr(dst + r0 * D));
+        else
+            dma16(ub, off * 2u, lds_addr(dst + r0 * D));
     };
     // Stage t < ntiles: key tile t.  Stage ntiles, when skip partials are
     // merged: the tile's fp16 skip partial rows, each wave its own 16 rows
@@ -225,7 +231,7 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
 #pragma unroll
             for (int j = 0; j < LPW; ++j) {
                 const int r0 = ((wave % (WW / 2)) * LPW + j) * RPI;
-                stage_rows(Ob, (int32_t)a.so.t, q0 + (isv ? KT : 0) + r0, r0, isv ? Vs : Ks);
+                stage_rows(Ob, (int32_t)a.so.t, q0 + (isv ? KT : 0) + r0, r0, isv ? Vs : Ks, true);
             }
             return;
         }
@@ -233,7 +239,7 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const int r0 = ((wave % (WW / 2)) * LPW + j) * RPI;
-            stage_rows(src0, st, klo + t * KT + r0, r0, isv ? Vs : Ks);
+            stage_rows(src0, st, klo + t * KT + r0, r0, isv ? Vs : Ks, false);
         }
     };
 
@@ -245,7 +251,7 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
 #pragma unroll
         for (int j = 0; j < LPW; ++j) {
             const int r0 = ((wave % (WW / 2)) * LPW + j) * RPI;
-            stage_rows(Qb, (int32_t)a.sq.t, q0 + (isv ? KT : 0) + r0, r0, isv ? vqs : kqs);
+            stage_rows(Qb, (int32_t)a.sq.t, q0 + (isv ? KT : 0) + r0, r0, isv ? vqs : kqs, true);
         }
         if (wave == 0) {
 #pragma unroll
@@ -401,7 +407,7 @@ __device__ __forceinline__ void window_tile(const FwdArgs& a, const float* lse_s
             const int r = o / (2 * D), cc = (o % (2 * D)) / 16;
             const uint4 val = *reinterpret_cast<const uint4*>(prow + swr<D>(rr0 + r, cc));
             const int32_t row = q0 + 16 * wave + r;
-            if (row < n) *reinterpret_cast<uint4*>(Ob + (int64_t)row * a.so.t + 8 * cc) = val;
+            if (row < n) store_nt16(Ob + (int64_t)row * a.so.t + 8 * cc, val);   // the result
         }
     };
     // step t: wait for this wave's loads of tile t (tile t+1 may be in

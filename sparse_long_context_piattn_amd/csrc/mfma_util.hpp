@@ -10,6 +10,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4_t lds_s16x4_t;
 
 
@@ -110,9 +111,21 @@ __device__ __forceinline__ const void* uniform_ptr(const void* p) {
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
     return reinterpret_cast<const void*>(((uint64_t)hi << 32) | lo);
 }
+// NT: with the non-temporal hint, for rows nothing in the kernel reads again.
+template <bool NT = false>
 __device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-    asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(uniform_ptr(sbase)),
-                 "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+    if constexpr (NT)
+        asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1 nt" : : "v"(voff), "s"(uniform_ptr(sbase)),
+                     "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+    else
+        asm volatile("s_nop 4\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(uniform_ptr(sbase)),
+                     "{m0}"(__builtin_amdgcn_readfirstlane(lds)) : "memory");
+}
+
+// 16-byte store with the non-temporal hint (global_store_dwordx4 ... nt),
+// for rows nothing in the kernel reads again.
+__device__ __forceinline__ void store_nt16(void* p, uint4 v) {
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4_t, v), static_cast<u32x4_t*>(p));
 }
 
 // 4-byte LDS-direct load of each active lane (lane l writes lds + 4 l);
