@@ -211,14 +211,20 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
     // ---- staging: rows s0 .. s0+RPI-1 of the view into slot rows r0 ..;
     // lane row r0 + lane/CH, physical chunk lane%CH = logical chunk
     // (lane%CH) ^ (row%8); rows past the view load its last row
-    auto stage_rows = [&](const uint16_t* src, int64_t rst, int32_t s0, int r0, uint16_t* dst, int ln)
-        __attribute__((always_inline)) {
+    // stream: rows only this workgroup reads (the skip partials the window
+    // pass adds), loaded with the non-temporal hint; the staged tiles,
+    // which neighbouring tiles read again, without it
+    auto stage_rows = [&](const uint16_t* src, int64_t rst, int32_t s0, int r0, uint16_t* dst, int ln,
+                          bool stream = false) __attribute__((always_inline)) {
         const int rl = r0 + ln / CH;
         const int lc = ((ln % CH) ^ (rl & 7)) << 3;
         const bool inside = s0 + RPI - 1 < L;
         const uint16_t* ub = inside ? src + (int64_t)s0 * rst : src;
         const int64_t row = inside ? (int64_t)(ln / CH) : (int64_t)imin32(s0 + ln / CH, L - 1);
-        dma16(ub, (uint32_t)(row * rst + lc) * 2u, lds_addr(dst + r0 * D));
+        if (stream)
+            dma16<true>(ub, (uint32_t)(row * rst + lc) * 2u, lds_addr(dst + r0 * D));
+        else
+            dma16(ub, (uint32_t)(row * rst + lc) * 2u, lds_addr(dst + r0 * D));
     };
     // stage s < NA: key tile jlo+s (K to x, V to y); then query tile
     // ilo+s-NA (Q to x, dO to y, the rows' c and D to cs, ds).  The first
@@ -397,7 +403,7 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
     auto partial_in = [&](const uint16_t* gb, int64_t rst, uint16_t* reg) __attribute__((always_inline)) {
         const int ln = fresh_lane();
 #pragma unroll
-        for (int j = 0; j < 16 / RPI; ++j) stage_rows(gb, rst, pw + j * RPI, j * RPI, reg, ln);
+        for (int j = 0; j < 16 / RPI; ++j) stage_rows(gb, rst, pw + j * RPI, j * RPI, reg, ln, true);
     };
     // the wave's accumulators (MFMA layout, times mul, plus the partial in
     // the region when merging) into its region as bf16
@@ -419,7 +425,8 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
         }
     };
     // the region's rows out, 16 bytes per lane (a 32-bit byte offset from
-    // the view's first row: within the bound the launcher checks)
+    // the view's first row: within the bound the launcher checks), with the
+    // non-temporal hint: this kernel does not read them again
     auto lds_to_rows = [&](uint16_t* gb, int64_t rst, const uint16_t* reg) __attribute__((always_inline)) {
         const int ln = fresh_lane();
 #pragma unroll
@@ -427,7 +434,7 @@ __global__ __launch_bounds__(TB * 4, D == 64 ? 4 : 2) void bwd_band_kernel(BwdAr
             const int r = j * RPI + ln / CH, c = ln % CH;
             const uint4 val = *reinterpret_cast<const uint4*>(reg + swr<D>(r, c));
             const uint32_t off = (uint32_t)((pw + r) * (int32_t)rst + 8 * c) * 2u;
-            if (pw + r < L) *reinterpret_cast<uint4*>(reinterpret_cast<char*>(gb) + off) = val;
+            if (pw + r < L) store_nt16(reinterpret_cast<char*>(gb) + off, val);
         }
     };
     // dq rows out (the skip pass stores partials, the window pass adds them)

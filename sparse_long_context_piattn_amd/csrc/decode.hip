@@ -48,7 +48,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeArgs a) {
         const T* vb = static_cast<const T*>(a.vc) + (int64_t)s * a.sv.s + (int64_t)h * a.sv.h;
         float pl, ps;
         gate_priors(a.g[(int64_t)s * a.sg.s + (int64_t)h * a.sg.h], sp.has_skip(), &pl, &ps);
-        gather_row<T, D, MASKED>(qrow, kb, vb, a.sk.t, a.sv.t, sp, i, a.pat, w0, w1, pl, ps,
+        gather_row<T, D, MASKED, true>(qrow, kb, vb, a.sk.t, a.sv.t, sp, i, a.pat, w0, w1, pl, ps,
                          a.scale_log2, st, a.ring);
         reduce_slots<D>(st);
     }

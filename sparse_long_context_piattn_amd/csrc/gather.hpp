@@ -20,13 +20,25 @@
 template <typename T>
 struct Elem;
 
+typedef unsigned int gather_u32x4 __attribute__((ext_vector_type(4)));
+
+// 16 bytes at p, with the non-temporal hint when NT (rows read once).
+template <bool NT>
+__device__ __forceinline__ uint4 load16(const void* p) {
+    if constexpr (NT)
+        return __builtin_bit_cast(uint4, __builtin_nontemporal_load(static_cast<const gather_u32x4*>(p)));
+    else
+        return *static_cast<const uint4*>(p);
+}
+
 template <>
 struct Elem<float> {
+    template <bool NT = false>
     static __device__ __forceinline__ void load8(const float* p, float x[8]) {
-        const float4 a = *reinterpret_cast<const float4*>(p);
-        const float4 b = *reinterpret_cast<const float4*>(p + 4);
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+        const uint4 a = load16<NT>(p);
+        const uint4 b = load16<NT>(p + 4);
+        x[0] = __uint_as_float(a.x); x[1] = __uint_as_float(a.y); x[2] = __uint_as_float(a.z); x[3] = __uint_as_float(a.w);
+        x[4] = __uint_as_float(b.x); x[5] = __uint_as_float(b.y); x[6] = __uint_as_float(b.z); x[7] = __uint_as_float(b.w);
     }
     static __device__ __forceinline__ void store8(float* p, const float x[8]) {
         *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
@@ -37,8 +49,9 @@ struct Elem<float> {
 // bf16 is carried as its raw 16-bit pattern.
 template <>
 struct Elem<uint16_t> {
+    template <bool NT = false>
     static __device__ __forceinline__ void load8(const uint16_t* p, float x[8]) {
-        const uint4 w = *reinterpret_cast<const uint4*>(p);
+        const uint4 w = load16<NT>(p);
         x[0] = bf16lo(w.x); x[1] = bf16hi(w.x); x[2] = bf16lo(w.y); x[3] = bf16hi(w.y);
         x[4] = bf16lo(w.z); x[5] = bf16hi(w.z); x[6] = bf16lo(w.w); x[7] = bf16hi(w.w);
     }
@@ -69,8 +82,9 @@ struct RowPartial {
 // Process union positions [u0, u1) of row i.  kbase/vbase point at token 0
 // of the row's (sequence, head); k_tok_stride / v_tok_stride are the token
 // strides of the key and value tensors.  ring > 0: key position j lives in
-// row j mod ring (a rolling cache); 0: in row j.
-template <typename T, int D, bool MASKED>
+// row j mod ring (a rolling cache); 0: in row j.  NT: the key and value
+// rows are loaded with the non-temporal hint (decode reads each once).
+template <typename T, int D, bool MASKED, bool NT = false>
 __device__ __forceinline__ void gather_row(const T* __restrict__ qrow, const T* __restrict__ kbase,
                                            const T* __restrict__ vbase, int64_t k_tok_stride,
                                            int64_t v_tok_stride,
@@ -103,8 +117,8 @@ __device__ __forceinline__ void gather_row(const T* __restrict__ qrow, const T* 
                 const int32_t r = ri - (i - key);
                 key = r < 0 ? r + ring : r;
             }
-            Elem<T>::load8(kbase + (int64_t)key * k_tok_stride + c, kv);
-            Elem<T>::load8(vbase + (int64_t)key * v_tok_stride + c, vv);
+            Elem<T>::template load8<NT>(kbase + (int64_t)key * k_tok_stride + c, kv);
+            Elem<T>::template load8<NT>(vbase + (int64_t)key * v_tok_stride + c, vv);
             prior = loc ? pl : ps;
         } else {
 #pragma unroll
