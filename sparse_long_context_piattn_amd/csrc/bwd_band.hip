@@ -623,8 +623,9 @@ hipError_t launch_t(const BwdArgs& ba, hipStream_t stream) {
     // The skip pass forms the records itself when every residue view is one
     // tile long (phase B then needs only the tile's own rows).  With longer
     // views it would recompute its neighbour tiles' records: measured slower
-    // at prefill_128k (d = 128, 8 tiles per view: 6.37 against 6.29 ms), so
-    // there, and without skips, the record kernel runs.
+    // on a causal prefill of 32 heads x 131072 tokens at d = 128, pi = 256
+    // (8 tiles per view: 6.37 against 6.29 ms), so there, and without skips,
+    // the record kernel runs.
     const bool rec = skips && (a.n - 1) / a.pat.pi + 1 <= BT;
     hipError_t e = hipSuccess;
     if (!rec) {

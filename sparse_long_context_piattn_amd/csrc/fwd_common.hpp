@@ -127,8 +127,9 @@ struct WinShape {
     static constexpr int QTW = 16 * WW;
     // K/V slot pairs in the ring: three (loads two tiles ahead) at d = 64;
     // two (one ahead) at d = 128, where 33 KB instead of 49 KB of LDS lets
-    // four workgroups share a CU instead of three (prefill_128k 1.883-1.888
-    // -> 1.832-1.835 ms; at d = 64 two pairs measured no faster)
+    // four workgroups share a CU instead of three (32 heads x 131072 tokens,
+    // k = 128: 1.883-1.888 -> 1.832-1.835 ms; at d = 64 two pairs measured
+    // no faster)
     static constexpr int NSL = D == 64 ? 3 : 2;
     static constexpr int EU = 4;                             // waves per SIMD the register budget must allow
     static constexpr int LDS = 2 * NSL * KT * D * 2 + QTW * 4;   // bytes: NSL K and NSL V slots, the gates
