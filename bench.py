@@ -263,7 +263,8 @@ def cpu_baseline_decode(w, x, budget_s: float):
 def cpu_baseline_backward(w, x, budget_s: float):
     """The fp64 backward oracle on whole (sequence, head) slices of the
     workload (it takes a packed batch; one head at a time is the sample).
-    The backward oracle is serial C: the rate is one thread's."""
+    The oracle runs the (sequence, head) pairs of one call in parallel; each
+    call here gets a single slice, so the rate is one thread's."""
     import numpy as np
     import torch
 
@@ -295,7 +296,7 @@ def cpu_baseline_backward(w, x, budget_s: float):
         el, rows, j = el + e_, rows + r_, j + 1
     return _baseline("queries/s", rows / el, rows / el, 1,
                      "%d whole (sequence, head) slices (%d rows) of the %s workload, fp64 backward "
-                     "(serial), %.1f s on 1 thread" % (j, rows, w.name, el))
+                     "(one slice per call), %.1f s on 1 thread" % (j, rows, w.name, el))
 
 
 def cpu_baseline_layer(w, xs, x, wg, wo, o, budget_s: float):

@@ -342,8 +342,10 @@ void oracle_decode(int S, int H, int d, const void *q, const void *kc,
 }
 
 /*
- * Backward of the prefill over a packed batch (every row; single-threaded,
- * since the key-side gradients are scattered).  dout [T, H, d] (element
+ * Backward of the prefill over a packed batch (every row).  The key-side
+ * gradients are scattered within a (sequence, head), so the pairs run in
+ * parallel (OpenMP) and the rows of one pair in order: every sum is taken in
+ * the same order as in a serial run.  dout [T, H, d] (element
  * type dtd) is the gradient of the loss with respect to out; the results are
  * the gradients with respect to q, k, v ([T, H, d] fp64, zeroed here) and
  * the gate logits g ([T, H] fp64).  It is the chain rule through the one
@@ -368,19 +370,23 @@ void oracle_bwd_levels(int nseq, const int64_t *cu, int H, int d,
 {
     int64_t T = cu[nseq];
     int cap = list_cap(kw, nlev, lM);
-    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * cap);
-    int8_t *kind = (int8_t *)malloc((size_t)cap);
-    double *sc = (double *)malloc(sizeof(double) * cap);
-    double *dp = (double *)malloc(sizeof(double) * cap);
-    int s, h, i, a, c;
+    int64_t pair;
 
     memset(dq, 0, sizeof(double) * (size_t)(T * H * d));
     memset(dk, 0, sizeof(double) * (size_t)(T * H * d));
     memset(dv, 0, sizeof(double) * (size_t)(T * H * d));
     memset(dg, 0, sizeof(double) * (size_t)(T * H));
-    for (s = 0; s < nseq; ++s) {
+#pragma omp parallel
+    {
+    int32_t *idx = (int32_t *)malloc(sizeof(int32_t) * cap);
+    int8_t *kind = (int8_t *)malloc((size_t)cap);
+    double *sc = (double *)malloc(sizeof(double) * cap);
+    double *dp = (double *)malloc(sizeof(double) * cap);
+#pragma omp for schedule(dynamic, 1)
+    for (pair = 0; pair < (int64_t)nseq * H; ++pair) {
+        int s = (int)(pair / H), h = (int)(pair % H), i, a, c;
         int n = (int)(cu[s + 1] - cu[s]);
-        for (h = 0; h < H; ++h) {
+        {
             int64_t base = (cu[s] * H + h) * (int64_t)d; /* token 0 of this (sequence, head) */
             int64_t ts = (int64_t)H * d;                 /* token stride */
             for (i = 0; i < n; ++i) {
@@ -430,6 +436,7 @@ void oracle_bwd_levels(int nseq, const int64_t *cu, int H, int d,
     free(kind);
     free(sc);
     free(dp);
+    }
 }
 
 void oracle_bwd(int nseq, const int64_t *cu, int H, int d, const void *q,
