@@ -18,7 +18,7 @@ import sparse_long_context_piattn_amd as pa
 from sparse_long_context_piattn_amd import workloads as wl
 
 import oracle
-from helpers import LSE_TOL_BF16, LSE_TOL_F32, host_array, max_err, oracle_dense_fwd, packed, tol_for
+from helpers import LSE_TOL_BF16, LSE_TOL_F32, host_array, lse_tol_for, max_err, oracle_dense_fwd, packed, tol_for
 
 pytestmark = [pytest.mark.gpu,
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
@@ -90,19 +90,33 @@ def test_schedule_fwd_matches_oracle(case, dt, d, kernel):
     assert max_err(lse, rlse) <= (LSE_TOL_F32 if dt == "f32" else LSE_TOL_BF16)
 
 
-def test_schedule_workload_one_head_every_row():
+def test_schedule_workload_every_row():
     """prefill_8k_sched (B4 H16 n8192 d64, k64, levels (128,16) (256,16)
-    (512,16)): every row of sequence 2, head 9 of the full-size call."""
+    (512,16)): every row of the full-size call, with its lse, and every
+    gradient row of its backward on the band kernels."""
     w = wl.WORKLOADS["prefill_8k_sched"]
     x = wl.make_fwd_inputs(w, device=DEV)
     print("schedule workload prefill_8k_sched", flush=True)
-    out = pa.fwd(x["q"], x["k"], x["v"], x["g"], window_k=w.k, period_pi=w.pi, num_skips=w.M,
-                 levels=w.levels)
+    kw = dict(window_k=w.k, period_pi=w.pi, num_skips=w.M, levels=w.levels)
+    lse = torch.empty_like(x["g"])
+    out = pa.fwd(x["q"], x["k"], x["v"], x["g"], lse=lse, **kw)
     torch.cuda.synchronize()
-    b, h = 2, 9
-    xs = {k_: v_[b:b + 1, h:h + 1] for k_, v_ in x.items()}
-    ref = oracle_dense_fwd(xs, w)
-    assert max_err(out[b:b + 1, h:h + 1], ref, "sched prefill_8k_sched") <= tol_for(w)
+    ref, rlse = oracle_dense_fwd(x, w, want_lse=True)
+    assert max_err(out, ref, "sched prefill_8k_sched all rows") <= tol_for(w)
+    assert max_err(lse, rlse, "sched lse prefill_8k_sched all rows") <= lse_tol_for(w)
+    gen = torch.Generator(device=DEV).manual_seed(w.seed + 3)
+    dout = torch.randn(x["q"].shape, generator=gen, device=DEV).to(torch.bfloat16)
+    grads = _forced("bwd", "band", lambda: pa.bwd(x["q"], x["k"], x["v"], x["g"], out, dout, lse=lse, **kw))
+    torch.cuda.synchronize()
+    B, H, n, d = x["q"].shape
+    gg = x["g"].detach().cpu().permute(0, 2, 1).reshape(B * n, H).double().numpy()
+    rg = oracle.bwd(packed(x["q"]), packed(x["k"]), packed(x["v"]), gg, packed(dout), np.arange(B + 1) * n,
+                    w.k, w.pi, w.M, w.bidir, w.scale, levels=w.levels)
+    back = lambda t: t.reshape(B, n, H, d).transpose(0, 2, 1, 3)
+    refs = (back(rg[0]), back(rg[1]), back(rg[2]), rg[3].reshape(B, n, H).transpose(0, 2, 1))
+    for got, r, nm in zip(grads, refs, ("dq", "dk", "dv", "dg")):
+        scale = max(1.0, float(np.abs(r).max()))
+        assert max_err(got, r, "sched bwd prefill_8k_sched %s" % nm) / scale <= 3e-2, nm
 
 
 @pytest.mark.parametrize("rolling", [False, True])
